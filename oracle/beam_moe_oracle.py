@@ -1,0 +1,277 @@
+"""Plain, slow FP64 CPU oracle for the forward pass of one Beam MoE block.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this module; only the tests, the smoke check and the benchmark's CPU
+baseline leg do.  It shares no code with the HIP path.
+
+Source of every step: the Beam launch blog ("Beam 501B", Hugging Face blog,
+in the Chinese translation on hot.xinyuan-ai.com, section "专家混合模型" /
+mixture of experts, and section "残差流" for the FP32 policy), the rewrite on
+tech.fxxz.com (section "混合专家系统"), the bilingual excerpt of the English
+original (MoE paragraph), and the config.json fields quoted on oferry.com
+(section "config.json 里还有六处能直接抄的细节": n_group 8, topk_group 4,
+norm_topk_prob true, routed_scaling_factor 2.5).  What those passages fix:
+
+* router: a sigmoid score for every expert (blog, MoE section);
+* experts are split into n_group groups; a group is ranked by the sum of the
+  two highest scores inside it; the topk_group best groups are kept; the top-k
+  experts are taken from inside the kept groups; there is no shared expert;
+* the k expert outputs are combined with the normalised router weights and
+  multiplied by 2.5 (norm_topk_prob, routed_scaling_factor);
+* every expert is a SwiGLU MLP (hidden 5120, intermediate 2560);
+* the router and the SwiGLU product are computed in FP32.
+
+Readings where the pages are silent (each one is repeated where it is used):
+
+* groups are contiguous blocks of E / n_group expert indices;
+* ties are broken towards the lower index (groups and experts), and the k
+  selected ids are listed by score descending, then id ascending;
+* a group of a single expert scores that expert alone (top-2 of one value);
+* SwiGLU is silu(x W_gate^T) * (x W_up^T), followed by W_down, with no
+  biases, weights in the [out, in] layout;
+* no normalisation epsilon, no capacity limit, no token dropping.
+
+All arithmetic is float64 on float64 copies of the given (bf16-rounded or
+fp32) inputs, except :func:`select_fp32`, which follows a fixed FP32
+evaluation order on purpose (see there).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# router
+# --------------------------------------------------------------------------
+def router_logits(x, w_router, logit_bias=None):
+    """L[t, e] = sum_h x[t, h] * W_r[e, h] (+ b[e]), in FP64.
+
+    Blog, MoE section: every expert gets a router score; residual-stream
+    section: the router runs in FP32 (here FP64, which contains it).
+    """
+    X = np.asarray(x, dtype=np.float64)
+    W = np.asarray(w_router, dtype=np.float64)
+    L = X @ W.T
+    if logit_bias is not None:
+        L = L + np.asarray(logit_bias, dtype=np.float64)[None, :]
+    return L
+
+
+def sigmoid(L):
+    """1 / (1 + exp(-L)), evaluated without overflow for either sign."""
+    L = np.asarray(L, dtype=np.float64)
+    out = np.empty_like(L)
+    pos = L >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-L[pos]))
+    ex = np.exp(L[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def _ranked(values):
+    """Indices of a 1-D array ordered by value descending, index ascending."""
+    v = np.asarray(values)
+    return np.lexsort((np.arange(v.shape[0]), -v))
+
+
+def group_scores(S, num_groups):
+    """GS[t, g] = largest + second-largest score of group g (contiguous blocks).
+
+    Blog, MoE section: groups are ranked by the sum of their two best experts.
+    A group of one expert scores that expert alone.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    T, E = S.shape
+    gs = E // num_groups
+    blocks = S.reshape(T, num_groups, gs)
+    top = -np.sort(-blocks, axis=2)
+    return top[:, :, 0] + (top[:, :, 1] if gs >= 2 else 0.0)
+
+
+def kept_groups(GS, topk_groups):
+    """Boolean mask [T, G] of the topk_group groups with the largest group score."""
+    GS = np.asarray(GS)
+    T, G = GS.shape
+    mask = np.zeros((T, G), dtype=bool)
+    for t in range(T):
+        mask[t, _ranked(GS[t])[:topk_groups]] = True
+    return mask
+
+
+def select_experts(S, group_mask, topk):
+    """ids[t, :] = the topk experts with the highest score among the kept groups."""
+    S = np.asarray(S)
+    T, E = S.shape
+    G = group_mask.shape[1]
+    cand = np.repeat(group_mask, E // G, axis=1)
+    ids = np.empty((T, topk), dtype=np.int32)
+    for t in range(T):
+        c = np.nonzero(cand[t])[0]
+        order = np.lexsort((c, -S[t, c]))
+        ids[t] = c[order[:topk]]
+    return ids
+
+
+def normalised_weights(S, ids, routed_scaling):
+    """w[t, k] = S[t, id_k] / sum_j S[t, id_j] * routed_scaling (norm_topk_prob, x2.5)."""
+    sel = np.take_along_axis(np.asarray(S, dtype=np.float64), ids.astype(np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True) * routed_scaling
+
+
+def route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling):
+    """Router + group-limited selection + weights, all FP64.
+
+    Returns (ids [T,K] int32, w [T,K] f64, S [T,E] f64, GS [T,G] f64).
+    """
+    S = sigmoid(router_logits(x, w_router, logit_bias))
+    GS = group_scores(S, num_groups)
+    ids = select_experts(S, kept_groups(GS, topk_groups), topk)
+    w = normalised_weights(S, ids, routed_scaling)
+    return ids, w, S, GS
+
+
+def route_margins(S, num_groups, topk_groups, topk):
+    """Per-token distance from a routing decision flip, in FP64.
+
+    m_t = min(GS_(TG) - GS_(TG+1), S_(K) - S_(K+1) over the kept groups'
+    candidates), with (j) the j-th largest.  A missing (TG+1)-th group or
+    (K+1)-th candidate contributes +inf.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    T, E = S.shape
+    GS = group_scores(S, num_groups)
+    mask = kept_groups(GS, topk_groups)
+    cand = np.repeat(mask, E // num_groups, axis=1)
+    m = np.full(T, np.inf)
+    for t in range(T):
+        g = -np.sort(-GS[t])
+        if num_groups > topk_groups:
+            m[t] = min(m[t], g[topk_groups - 1] - g[topk_groups])
+        c = -np.sort(-S[t, cand[t]])
+        if c.shape[0] > topk:
+            m[t] = min(m[t], c[topk - 1] - c[topk])
+    return m
+
+
+def select_fp32(scores, num_groups, topk_groups, topk, routed_scaling):
+    """Selection on caller-supplied FP32 scores with a fixed FP32 evaluation order.
+
+    Same rule as :func:`route` after the sigmoid, but every floating-point
+    value that decides or forms an output is an IEEE FP32 result:
+
+    * GS = fl32(first + second) of the group's two largest scores;
+    * sum = fl32 running sum of the selected scores in output order
+      (((S_0 + S_1) + S_2) + ...);
+    * w_k = fl32(fl32(S_k / sum) * fl32(routed_scaling)).
+
+    This is the supplied-scores mode: ids and weights are meant to agree bit
+    for bit with any implementation that states the same FP32 order.
+    """
+    S = np.asarray(scores, dtype=np.float32)
+    T, E = S.shape
+    gs = E // num_groups
+    scale = np.float32(routed_scaling)
+    ids = np.empty((T, topk), dtype=np.int32)
+    w = np.empty((T, topk), dtype=np.float32)
+    for t in range(T):
+        GS = np.empty(num_groups, dtype=np.float32)
+        for g in range(num_groups):
+            blk = S[t, g * gs:(g + 1) * gs]
+            order = _ranked(blk)
+            GS[g] = blk[order[0]] + (blk[order[1]] if gs >= 2 else np.float32(0.0))
+        keep = _ranked(GS)[:topk_groups]
+        cand = np.concatenate([np.arange(g * gs, (g + 1) * gs) for g in sorted(keep)])
+        order = np.lexsort((cand, -S[t, cand]))
+        sel = cand[order[:topk]]
+        ids[t] = sel
+        total = np.float32(0.0)
+        for e in sel:
+            total = np.float32(total + S[t, e])
+        for k, e in enumerate(sel):
+            w[t, k] = np.float32(np.float32(S[t, e] / total) * scale)
+    return ids, w
+
+
+# --------------------------------------------------------------------------
+# dispatch
+# --------------------------------------------------------------------------
+def dispatch(ids, num_experts):
+    """Counting sort of the T*K (token, slot) pairs by expert.
+
+    counts[e] = #{i : ids.flat[i] == e}; offsets = exclusive prefix sum with
+    offsets[E] = T*K; sorted_slots = the indices i = t*K + k in ascending
+    expert order, ascending i inside an expert (a stable sort, hence unique).
+    Every token runs exactly K experts (blog, MoE section); no capacity limit.
+    """
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    counts = np.bincount(flat, minlength=num_experts).astype(np.int32)
+    offsets = np.zeros(num_experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    slots = np.argsort(flat, kind="stable").astype(np.int32)
+    return counts, offsets, slots
+
+
+# --------------------------------------------------------------------------
+# experts and combine
+# --------------------------------------------------------------------------
+def silu(v):
+    return v * sigmoid(v)
+
+
+def swiglu_expert(x_rows, w_gate, w_up, w_down):
+    """y = (silu(x W_gate^T) * (x W_up^T)) W_down^T for each row, FP64.
+
+    Blog, MoE section: each expert is a SwiGLU MLP with intermediate size
+    2560; the SwiGLU product is FP32 on the pages (FP64 here).
+    """
+    X = np.asarray(x_rows, dtype=np.float64)
+    g = X @ np.asarray(w_gate, dtype=np.float64).T
+    u = X @ np.asarray(w_up, dtype=np.float64).T
+    h = silu(g) * u
+    return h @ np.asarray(w_down, dtype=np.float64).T
+
+
+def combine(y, w):
+    """out[t] = sum_k w[t, k] * y[t, k, :] (blog, MoE section: weighted combine)."""
+    y = np.asarray(y, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    return np.einsum("tk,tkh->th", w, y)
+
+
+def expert_outputs(x, ids, expert_weights):
+    """y[t, k, :] = expert ids[t, k] applied to x[t] (FP64).
+
+    expert_weights(e) -> (W_gate [I,H], W_up [I,H], W_down [H,I]); it is called
+    once for every expert some row uses, in ascending expert order.
+    """
+    ids = np.asarray(ids)
+    X = np.asarray(x, dtype=np.float64)
+    T, K = ids.shape
+    y = np.zeros((T, K, X.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        rows, ks = np.nonzero(ids == e)
+        wg, wu, wd = expert_weights(int(e))
+        y[rows, ks] = swiglu_expert(X[rows], wg, wu, wd)
+    return y
+
+
+def moe_forward(x, w_router, logit_bias, expert_weights, num_groups, topk_groups, topk,
+                routed_scaling):
+    """Whole block for the given token rows: route, dispatch, experts, combine.
+
+    Routing is per token, so any subset of a batch's rows may be passed; the
+    dispatch by-products then describe that subset.  Returns a dict with ids,
+    w, S, GS, counts, offsets, slots and out [T, H] (FP64).
+    """
+    ids, w, S, GS = route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling)
+    counts, offsets, slots = dispatch(ids, np.asarray(w_router).shape[0])
+    y = expert_outputs(x, ids, expert_weights)
+    out = combine(y, w)
+    return dict(ids=ids, w=w, S=S, GS=GS, counts=counts, offsets=offsets, slots=slots, out=out)
+
+
+def route_only(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling):
+    """Router, selection and dispatch, without the experts."""
+    ids, w, S, GS = route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling)
+    counts, offsets, slots = dispatch(ids, w_router.shape[0])
+    return dict(ids=ids, w=w, S=S, GS=GS, counts=counts, offsets=offsets, slots=slots)
