@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the Beam MoE block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,prefill]
+                    [--no-cpu-baseline]
+
+A step is one beam_moe_forward call over one batch of synthetic input (router,
+selection, dispatch, gate/up + SwiGLU, down, combine), inputs resident in HBM.
+W untimed steps, then K timed steps between a synchronize and HIP events on
+the launch stream.  The library's own stage events (beam_moe_timing_*) give
+each kernel's average duration inside the same timed region, which feeds the
+roofline figure of the dominant kernel.
+
+Prints one JSON line.  Its headline is the decode batch (T=64, HBM-bound);
+the prefill batch (T=16384, MFMA-bound) is reported in the same line under
+"prefill" with its own roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
+METRIC = "MoE-layer tokens/s (decode T=64, prefill T=16K); % HBM BW / bf16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="decode,prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
+    return ap.parse_args()
+
+
+def time_workload(name, experts, steps, warmup):
+    import torch
+    from grouped_top_routing_fp32_amd import binding, synth
+
+    wl = synth.WORKLOADS[name]
+    d = wl.dims
+    x = synth.make_x(wl, "cuda")
+    wr = synth.make_router(wl, "cuda")
+    bias = synth.make_bias(wl, "cuda")
+    wg, wu, wd = experts
+    bufs = binding.ForwardBuffers(d, wl.tokens, "cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        binding.beam_moe_forward(d, x, wr, bias, wg, wu, wd, bufs=bufs, stream=stream)
+    torch.cuda.synchronize()
+    binding.beam_moe_timing_read()                 # drop anything recorded before
+    binding.beam_moe_timing_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        binding.beam_moe_forward(d, x, wr, bias, wg, wu, wd, bufs=bufs, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    binding.beam_moe_timing_enable(False)
+    stage_ms, calls = binding.beam_moe_timing_read()
+    total_ms = start.elapsed_time(end)
+    assert calls == steps, (calls, steps)
+    counts = bufs.counts.cpu()
+    return dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps,
+                stage_ms={k: v / steps for k, v in stage_ms.items()},
+                n_touched=int((counts > 0).sum()), max_count=int(counts.max()), x=x, wr=wr, bias=bias, bufs=bufs)
+
+
+def accounting(r):
+    """Algorithmic bytes and FLOPs of each kernel of one step (no cache effects, no re-reads)."""
+    wl = r["wl"]
+    d = wl.dims
+    T, H, I, E, K = wl.tokens, d.hidden, d.intermediate, d.num_experts, d.topk
+    n = T * K
+    nt = r["n_touched"]
+    b = {
+        "router_logits": T * H * 2 + E * H * 4,
+        "gate_up": nt * 2 * I * H * 2 + T * H * 2 + n * I * 2,
+        "down": nt * H * I * 2 + n * I * 2 + n * H * 4,
+        "combine": n * H * 4 + n * 4 + T * H * 4,
+    }
+    f = {
+        "router_logits": 2 * T * H * E,
+        "gate_up": 2 * n * 2 * I * H,
+        "down": 2 * n * H * I,
+    }
+    layer_bytes = nt * 3 * I * H * 2 + E * H * 4 + T * H * 2 + T * H * 4
+    expert_flops = 2 * n * 3 * I * H
+    return b, f, layer_bytes, expert_flops
+
+
+def roofline(r, bound):
+    b, f, layer_bytes, expert_flops = accounting(r)
+    kernel = "gate_up"
+    dur_s = r["stage_ms"][kernel] / 1e3
+    if bound == "hbm":
+        achieved = b[kernel] / dur_s / 1e9
+        return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": b[kernel], "avg_launch_ms": round(r["stage_ms"][kernel], 4)}
+    achieved = f[kernel] / dur_s / 1e12
+    return {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": f[kernel], "avg_launch_ms": round(r["stage_ms"][kernel], 4)}
+
+
+def layer_summary(r):
+    b, f, layer_bytes, expert_flops = accounting(r)
+    s = r["ms_per_step"] / 1e3
+    return {"layer_hbm_gbs": round(layer_bytes / s / 1e9, 1), "layer_hbm_frac": round(layer_bytes / s / 1e9 / HBM_PEAK_GBS, 4),
+            "layer_expert_tflops": round(expert_flops / s / 1e12, 1),
+            "layer_mfma_frac": round(expert_flops / s / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+            "experts_touched": r["n_touched"], "max_rows_per_expert": r["max_count"]}
+
+
+def cpu_baseline(r, target_s):
+    """The FP64 oracle on the host cores, on the first tokens of the same batch."""
+    import numpy as np
+    from oracle import beam_moe_oracle as orc
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas_threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in info if i.get("user_api") == "blas"}))
+    except Exception:
+        blas_threads, blas = os.cpu_count(), "?"
+    wl = r["wl"]
+    d = wl.dims
+    X_all = r["x"].float().cpu().numpy()
+    W_r = r["wr"].cpu().numpy()
+    bias = None if r["bias"] is None else r["bias"].cpu().numpy()
+    wg, wu, wd = r["experts"]
+    host = {}
+
+    def fetch(ids):
+        for e in np.unique(ids):
+            e = int(e)
+            if e not in host:
+                host[e] = (wg[e].float().cpu().numpy(), wu[e].float().cpu().numpy(), wd[e].float().cpu().numpy())
+
+    # untimed calibration on one token: how many tokens fit the target time
+    ids1, *_ = orc.route(X_all[:1], W_r, bias, d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
+    fetch(ids1)
+    t0 = time.perf_counter()
+    orc.moe_forward(X_all[:1], W_r, bias, lambda e: host[e], d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
+    per_token = time.perf_counter() - t0
+    n = int(max(1, min(wl.tokens, target_s / max(per_token, 1e-3))))
+    ids_n, *_ = orc.route(X_all[:n], W_r, bias, d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
+    fetch(ids_n)
+    t0 = time.perf_counter()
+    orc.moe_forward(X_all[:n], W_r, bias, lambda e: host[e], d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
+    el = time.perf_counter() - t0
+    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {n} of the {wl.tokens} tokens of the {wl.name} batch, whole block in FP64 "
+                      f"(numpy, BLAS={blas}); {el:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Beam MoE block here runs on a single MI355X "
+              "(no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from grouped_top_routing_fp32_amd import binding, synth
+    binding.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    names = [w for w in args.workloads.split(",") if w]
+    print(f"[bench] generating Beam expert weights (20.1 GB bf16) on the device", file=sys.stderr, flush=True)
+    experts = synth.make_experts(synth.WORKLOADS["decode"], "cuda")
+    torch.cuda.synchronize()
+    results = {}
+    for name in names:
+        print(f"[bench] timing {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+        r = time_workload(name, experts, args.steps, args.warmup)
+        r["experts"] = experts
+        results[name] = r
+        print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step; stages {r['stage_ms']}", file=sys.stderr, flush=True)
+
+    def record(name):
+        r = results[name]
+        wl = r["wl"]
+        d = wl.dims
+        bound = "hbm" if wl.tokens * d.topk / d.num_experts < 32 else "mfma"
+        cfg = {"workload": f"{name}: Beam MoE block forward, T={wl.tokens}", "tokens": wl.tokens,
+               "hidden": d.hidden, "intermediate": d.intermediate, "experts": d.num_experts,
+               "groups": d.num_groups, "topk_groups": d.topk_groups, "topk": d.topk,
+               "routed_scaling": d.routed_scaling, "router_bias": "zipf(1.2)" if wl.zipf_s else None}
+        out = {"value": round(wl.tokens / (r["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
+               "ms_per_step": round(r["ms_per_step"], 4), "config": cfg, "roofline": roofline(r, bound)}
+        out.update(layer_summary(r))
+        return out
+
+    head = names[0]
+    line = {"metric": METRIC}
+    main_rec = record(head)
+    line.update({"value": main_rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                 "warmup": args.warmup, "ms_per_step": main_rec["ms_per_step"], "higher_is_better": True,
+                 "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                 "config": main_rec["config"], "roofline": main_rec["roofline"]})
+    for k in ("layer_hbm_gbs", "layer_hbm_frac", "layer_expert_tflops", "layer_mfma_frac", "stage_ms",
+              "experts_touched", "max_rows_per_expert"):
+        line[k] = main_rec[k]
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (oracle) on {head}", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(results[head], args.cpu_seconds)
+    for name in names[1:]:
+        line[name] = record(name)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

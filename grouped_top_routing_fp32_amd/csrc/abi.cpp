@@ -1,0 +1,345 @@
+// C ABI of the Beam MoE block: argument validation, workspace carving and
+// kernel launches on the caller's stream.  The operations and conventions are
+// stated in include/beam_moe.h.
+#include "../../include/beam_moe.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <array>
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+#include <mutex>
+#include <vector>
+
+namespace beam {
+struct Tile;
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part, int T, int H, int E, int splits,
+                                int k_per_split, hipStream_t st);
+hipError_t launch_select(const float* src, int splits, bool from_partials, const float* bias, float* scores_out,
+                         int T, int E, int G, int TG, int K, float scale, int32_t* ids, float* w, hipStream_t st);
+int dispatch_units(int n);
+hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_slots, Tile* tiles_a, int mt_a, Tile* tiles_b, int mt_b, int32_t* ntiles,
+                           hipStream_t st);
+int tiled_gateup_rows();
+int tiled_down_rows();
+int tiled_gateup_cols();
+int tiled_down_cols();
+hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, int H, int I,
+                                int K, hipStream_t st);
+hipError_t launch_down_stream(const uint16_t* h, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                              int max_tiles, const uint16_t* wd, float* y, int H, int I, hipStream_t st);
+hipError_t launch_gateup_tiled(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                               int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, int H, int I,
+                               int K, hipStream_t st);
+hipError_t launch_down_tiled(const uint16_t* h, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                             int max_tiles, const uint16_t* wd, float* y, int H, int I, hipStream_t st);
+hipError_t launch_combine(const float* y, const float* w, float* out, int T, int H, int K, hipStream_t st);
+}  // namespace beam
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTileBytes = 16;          // sizeof(beam::Tile)
+constexpr int kWholeExpert = 1 << 30;   // tile height meaning "all rows of the expert"
+constexpr int64_t kMaxPairs = 1 << 28;  // T * K limit
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool dims_ok(const beam_moe_dims* d) {
+  if (!d) return false;
+  const int E = d->num_experts, G = d->num_groups, TG = d->topk_groups, K = d->topk;
+  if (E < 1 || E > 256 || G < 1 || G > 64 || E % G != 0) return false;
+  if (TG < 1 || TG > G) return false;
+  const int cand = TG * (E / G);
+  if (K < 1 || K > 16 || K > cand) return false;
+  if (d->hidden < 256 || d->hidden % 256 != 0) return false;
+  if (d->intermediate < 128 || d->intermediate % 128 != 0) return false;
+  if (!std::isfinite(d->routed_scaling)) return false;
+  return true;
+}
+
+// Expert-path choice: the stream kernels serve batches with few rows per
+// expert (weights streamed once per 16 rows), the tiled kernels the rest.
+bool use_stream_path(const beam_moe_dims* d, int T) {
+  const double avg_rows = (double)T * d->topk / d->num_experts;
+  return avg_rows < 32.0;
+}
+
+struct Plan {
+  int T, H, I, E, K, n;
+  // router
+  int splits, k_per_split;
+  size_t off_part;
+  // dispatch
+  int units;
+  size_t off_hist;
+  // expert tiles
+  bool stream;
+  int mt_a, mt_b, max_tiles_a, max_tiles_b;
+  size_t off_tiles_a, off_tiles_b, off_ntiles;
+  // activations
+  size_t off_h, off_y;
+  size_t total;
+};
+
+void make_plan(const beam_moe_dims* d, int T, Plan* p) {
+  p->T = T;
+  p->H = d->hidden;
+  p->I = d->intermediate;
+  p->E = d->num_experts;
+  p->K = d->topk;
+  p->n = T * d->topk;
+  const int ksteps = p->H / 32;
+  int rtiles = ((T + 63) / 64) * ((p->E + 63) / 64);
+  if (rtiles < 1) rtiles = 1;
+  int splits = (256 + rtiles - 1) / rtiles;
+  if (splits > ksteps) splits = ksteps;
+  if (splits > 64) splits = 64;
+  if (splits < 1) splits = 1;
+  const int steps_per = (ksteps + splits - 1) / splits;
+  p->k_per_split = steps_per * 32;
+  p->splits = (ksteps + steps_per - 1) / steps_per;
+  p->units = beam::dispatch_units(p->n);
+  p->stream = use_stream_path(d, T);
+  if (p->stream) {
+    p->mt_a = p->mt_b = kWholeExpert;
+    p->max_tiles_a = p->max_tiles_b = p->E < p->n ? p->E : p->n;
+  } else {
+    p->mt_a = beam::tiled_gateup_rows();
+    p->mt_b = beam::tiled_down_rows();
+    const int m = p->E < p->n ? p->E : p->n;
+    p->max_tiles_a = p->n / p->mt_a + m;
+    p->max_tiles_b = p->n / p->mt_b + m;
+  }
+  size_t off = 0;
+  p->off_part = off;
+  off = align_up(off + (size_t)p->splits * T * p->E * sizeof(float));
+  p->off_hist = off;
+  off = align_up(off + (size_t)p->units * p->E * sizeof(int32_t));
+  p->off_tiles_a = off;
+  off = align_up(off + (size_t)(p->max_tiles_a + 1) * kTileBytes);
+  p->off_tiles_b = off;
+  off = align_up(off + (size_t)(p->max_tiles_b + 1) * kTileBytes);
+  p->off_ntiles = off;
+  off = align_up(off + 2 * sizeof(int32_t));
+  p->off_h = off;
+  off = align_up(off + (size_t)p->n * p->I * 2);
+  p->off_y = off;
+  off = align_up(off + (size_t)p->n * p->H * sizeof(float));
+  p->total = off;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename Tp>
+Tp* at(void* ws, size_t off) {
+  return reinterpret_cast<Tp*>(static_cast<char*>(ws) + off);
+}
+
+int check_common(const beam_moe_dims* d, int32_t T) {
+  if (!d) return BEAM_MOE_ERR_INVALID_ARG;
+  if (!dims_ok(d)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (T < 0) return BEAM_MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * d->topk > kMaxPairs) return BEAM_MOE_ERR_UNSUPPORTED;
+  return BEAM_MOE_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return BEAM_MOE_ERR_INVALID_ARG;
+  return BEAM_MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BEAM_MOE_OK : BEAM_MOE_ERR_HIP; }
+
+// ---------------------------------------------------------------------------
+// stage timing (diagnostics)
+// ---------------------------------------------------------------------------
+enum Stage { kStRouter = 0, kStSelect, kStDispatch, kStGateUp, kStDown, kStCombine, kNumStages };
+const char* const kStageNames[kNumStages] = {"router_logits", "select", "dispatch", "gate_up", "down", "combine"};
+
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<std::array<hipEvent_t, kNumStages + 1>> slots;
+  size_t used = 0;
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+// Events of the current forward call, or nullptr when timing is off.
+hipEvent_t* timing_slot() {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (!t.enabled) return nullptr;
+  if (t.used == t.slots.size()) {
+    std::array<hipEvent_t, kNumStages + 1> ev{};
+    for (auto& e : ev)
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    t.slots.push_back(ev);
+  }
+  return t.slots[t.used++].data();
+}
+
+hipError_t mark(hipEvent_t* ev, int i, hipStream_t st) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; }
+
+
+}  // namespace
+
+extern "C" {
+
+size_t beam_moe_workspace_bytes(const beam_moe_dims* dims, int32_t T) {
+  if (check_common(dims, T) != BEAM_MOE_OK) return SIZE_MAX;
+  Plan p;
+  make_plan(dims, T, &p);
+  return p.total;
+}
+
+const char* beam_moe_status_str(int status) {
+  switch (status) {
+    case BEAM_MOE_OK: return "ok";
+    case BEAM_MOE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, negative T)";
+    case BEAM_MOE_ERR_UNSUPPORTED: return "unsupported dims";
+    case BEAM_MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case BEAM_MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int beam_moe_route(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                   const float* logit_bias, int32_t* topk_ids, float* topk_w, float* scores_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK || T == 0) return rc;
+  if ((rc = check_ptrs({x_bf16, w_router, topk_ids, topk_w})) != BEAM_MOE_OK) return rc;
+  if ((logit_bias && !aligned16(logit_bias)) || (scores_out && !aligned16(scores_out)))
+    return BEAM_MOE_ERR_INVALID_ARG;
+  Plan p;
+  make_plan(d, T, &p);
+  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* part = at<float>(ws, p.off_part);
+  rc = hip_status(beam::launch_router_logits(static_cast<const uint16_t*>(x_bf16), w_router, part, T, p.H, p.E,
+                                             p.splits, p.k_per_split, st));
+  if (rc != BEAM_MOE_OK) return rc;
+  return hip_status(beam::launch_select(part, p.splits, true, logit_bias, scores_out, T, p.E, d->num_groups,
+                                        d->topk_groups, d->topk, d->routed_scaling, topk_ids, topk_w, st));
+}
+
+int beam_moe_select(const beam_moe_dims* d, int32_t T, const float* scores, int32_t* topk_ids, float* topk_w,
+                    void* stream) {
+  int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK || T == 0) return rc;
+  if ((rc = check_ptrs({scores, topk_ids, topk_w})) != BEAM_MOE_OK) return rc;
+  return hip_status(beam::launch_select(scores, 1, false, nullptr, nullptr, T, d->num_experts, d->num_groups,
+                                        d->topk_groups, d->topk, d->routed_scaling, topk_ids, topk_w,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int beam_moe_dispatch(const beam_moe_dims* d, int32_t T, const int32_t* topk_ids, int32_t* expert_counts,
+                      int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK || T == 0) return rc;
+  if ((rc = check_ptrs({topk_ids, expert_counts, expert_offsets, sorted_slots})) != BEAM_MOE_OK) return rc;
+  Plan p;
+  make_plan(d, T, &p);
+  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  return hip_status(beam::launch_dispatch(topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), expert_counts,
+                                          expert_offsets, sorted_slots, nullptr, 0, nullptr, 0, nullptr,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                     const float* logit_bias, const void* w_gate, const void* w_up, const void* w_down, float* out,
+                     int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                     int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK || T == 0) return rc;
+  if ((rc = check_ptrs({x_bf16, w_router, w_gate, w_up, w_down, out, topk_ids, topk_w, expert_counts,
+                        expert_offsets, sorted_slots})) != BEAM_MOE_OK)
+    return rc;
+  if (logit_bias && !aligned16(logit_bias)) return BEAM_MOE_ERR_INVALID_ARG;
+  Plan p;
+  make_plan(d, T, &p);
+  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
+  const uint16_t* wu = static_cast<const uint16_t*>(w_up);
+  const uint16_t* wd = static_cast<const uint16_t*>(w_down);
+  float* part = at<float>(ws, p.off_part);
+  beam::Tile* tiles_a = at<beam::Tile>(ws, p.off_tiles_a);
+  beam::Tile* tiles_b = at<beam::Tile>(ws, p.off_tiles_b);
+  int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
+  uint16_t* h = at<uint16_t>(ws, p.off_h);
+  float* y = at<float>(ws, p.off_y);
+  hipEvent_t* ev = timing_slot();
+
+#define BEAM_TRY(expr)                                  \
+  do {                                                  \
+    if ((rc = hip_status(expr)) != BEAM_MOE_OK) return rc; \
+  } while (0)
+  BEAM_TRY(mark(ev, kStRouter, st));
+  BEAM_TRY(beam::launch_router_logits(x, w_router, part, T, p.H, p.E, p.splits, p.k_per_split, st));
+  BEAM_TRY(mark(ev, kStSelect, st));
+  BEAM_TRY(beam::launch_select(part, p.splits, true, logit_bias, nullptr, T, p.E, d->num_groups, d->topk_groups,
+                               d->topk, d->routed_scaling, topk_ids, topk_w, st));
+  BEAM_TRY(mark(ev, kStDispatch, st));
+  BEAM_TRY(beam::launch_dispatch(topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), expert_counts, expert_offsets,
+                                 sorted_slots, tiles_a, p.mt_a, tiles_b, p.mt_b, ntiles, st));
+  BEAM_TRY(mark(ev, kStGateUp, st));
+  if (p.stream)
+    BEAM_TRY(beam::launch_gateup_stream(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, p.H, p.I, p.K,
+                                        st));
+  else
+    BEAM_TRY(beam::launch_gateup_tiled(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, p.H, p.I, p.K,
+                                       st));
+  BEAM_TRY(mark(ev, kStDown, st));
+  if (p.stream)
+    BEAM_TRY(beam::launch_down_stream(h, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I, st));
+  else
+    BEAM_TRY(beam::launch_down_tiled(h, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I, st));
+  BEAM_TRY(mark(ev, kStCombine, st));
+  BEAM_TRY(beam::launch_combine(y, topk_w, out, T, p.H, p.K, st));
+  BEAM_TRY(mark(ev, kNumStages, st));
+#undef BEAM_TRY
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_timing_enable(int enable) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.enabled = enable != 0;
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_timing_read(float* stage_ms, int32_t max_stages, int32_t* n_stages, int32_t* calls) {
+  if (!stage_ms || !n_stages || !calls || max_stages < 0) return BEAM_MOE_ERR_INVALID_ARG;
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  const int ns = max_stages < kNumStages ? max_stages : kNumStages;
+  for (int s = 0; s < ns; ++s) stage_ms[s] = 0.f;
+  *n_stages = ns;
+  *calls = (int32_t)t.used;
+  if (t.used > 0 && hipEventSynchronize(t.slots[t.used - 1][kNumStages]) != hipSuccess) return BEAM_MOE_ERR_HIP;
+  for (size_t c = 0; c < t.used; ++c) {
+    for (int s = 0; s < ns; ++s) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, t.slots[c][s], t.slots[c][s + 1]) != hipSuccess) return BEAM_MOE_ERR_HIP;
+      stage_ms[s] += ms;
+    }
+  }
+  t.used = 0;
+  return BEAM_MOE_OK;
+}
+
+const char* beam_moe_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < kNumStages) ? kStageNames[stage] : nullptr;
+}
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+// Router and group-limited top-k selection of the Beam MoE block (gfx950).
+//
+// Beam launch blog, section "mixture of experts": every expert gets a sigmoid
+// score; experts form n_group groups; a group is ranked by the sum of its two
+// best scores; the topk_group best groups are kept; the top-k experts inside
+// them are chosen; their weights are normalised and multiplied by 2.5.  The
+// "residual stream" section puts the router in FP32.
+//
+// Two kernels:
+//   router_logits_kernel  FP32-exact logits on bf16 MFMA.  x is bf16, W_r is
+//       fp32; each W_r element is split exactly into three bf16 pieces
+//       (w = hi + mid + lo), so every product x*piece is exact in FP32 and
+//       the MFMA accumulates in FP32: an FP32 contraction at bf16-MFMA rate.
+//       The K dimension may be split across workgroups; partial sums land in
+//       workspace and are added in a fixed order by the select kernel.
+//   select_kernel  one wave per token: partial sums + bias + sigmoid, then the
+//       group top-2 sums, the kept groups and K rounds of a wave-wide argmax.
+#include "common.h"
+
+namespace beam {
+
+constexpr int kRtM = 64;       // tokens per router tile
+constexpr int kRtN = 64;       // experts per router tile
+constexpr int kRtK = 32;       // K step
+constexpr int kRtLd = kRtK + 8;  // LDS row stride in bf16 elements (80 bytes: conflict-free 16-byte reads)
+
+// Exact three-way split of an fp32 value into bf16 pieces (truncation; the
+// remainders are exact in fp32 and the last piece has at most 8 significant bits).
+__device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  uint32_t u = __float_as_uint(w);
+  hi = uint16_t(u >> 16);
+  float r1 = w - __uint_as_float(u & 0xFFFF0000u);
+  uint32_t v = __float_as_uint(r1);
+  mid = uint16_t(v >> 16);
+  float r2 = r1 - __uint_as_float(v & 0xFFFF0000u);
+  lo = uint16_t(__float_as_uint(r2) >> 16);
+}
+
+// grid: (ceil(T/64), ceil(E/64), splits); block 256 (4 waves, wave w = tokens 16w..16w+15)
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ wr, float* __restrict__ part,
+                                                            int T, int H, int E, int k_per_split) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kRtM * kRtLd];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[3][kRtN * kRtLd];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t0 = blockIdx.x * kRtM;
+  const int e0 = blockIdx.y * kRtN;
+  const int kbeg = blockIdx.z * k_per_split;
+  const int kend = min(H, kbeg + k_per_split);
+
+  // staging assignments: x: one 16-byte chunk per thread; W_r: two 4-float chunks per thread
+  const int xa_row = tid >> 2, xa_kc = tid & 3;
+  const uint16_t* xsrc = x + (size_t)min(t0 + xa_row, T - 1) * H + xa_kc * 8;
+  int wb_row[2], wb_kc[2];
+  const float* wsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int c = tid + 256 * i;
+    wb_row[i] = c >> 3;
+    wb_kc[i] = c & 7;
+    wsrc[i] = wr + (size_t)min(e0 + wb_row[i], E - 1) * H + wb_kc[i] * 4;
+  }
+
+  f32x4 acc_hi[4], acc_lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc_hi[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc_lo[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int k = kbeg; k < kend; k += kRtK) {
+    u32x4 xv = ldg16(xsrc + k);
+    f32x4 wv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wv[i] = *reinterpret_cast<const f32x4*>(wsrc[i] + k);
+    __syncthreads();  // previous step's fragment reads are done
+    *reinterpret_cast<u32x4*>(&sA[xa_row * kRtLd + xa_kc * 8]) = xv;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split3(wv[i][q], hi[q], mid[q], lo[q]);
+      const int off = wb_row[i] * kRtLd + wb_kc[i] * 4;
+      uint2 ph, pm, pl;
+      ph.x = hi[0] | (uint32_t(hi[1]) << 16);
+      ph.y = hi[2] | (uint32_t(hi[3]) << 16);
+      pm.x = mid[0] | (uint32_t(mid[1]) << 16);
+      pm.y = mid[2] | (uint32_t(mid[3]) << 16);
+      pl.x = lo[0] | (uint32_t(lo[1]) << 16);
+      pl.y = lo[2] | (uint32_t(lo[3]) << 16);
+      *reinterpret_cast<uint2*>(&sB[0][off]) = ph;
+      *reinterpret_cast<uint2*>(&sB[1][off]) = pm;
+      *reinterpret_cast<uint2*>(&sB[2][off]) = pl;
+    }
+    __syncthreads();
+    const int arow = wave * 16 + (lane & 15);
+    const int kk = (lane >> 4) * 8;
+    u32x4 a = *reinterpret_cast<const u32x4*>(&sA[arow * kRtLd + kk]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int brow = j * 16 + (lane & 15);
+      u32x4 bh = *reinterpret_cast<const u32x4*>(&sB[0][brow * kRtLd + kk]);
+      u32x4 bm = *reinterpret_cast<const u32x4*>(&sB[1][brow * kRtLd + kk]);
+      u32x4 bl = *reinterpret_cast<const u32x4*>(&sB[2][brow * kRtLd + kk]);
+      acc_hi[j] = mfma16x16x32(a, bh, acc_hi[j]);
+      acc_lo[j] = mfma16x16x32(a, bl, acc_lo[j]);
+      acc_lo[j] = mfma16x16x32(a, bm, acc_lo[j]);
+    }
+  }
+
+  float* dst = part + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + j * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + wave * 16 + (lane >> 4) * 4 + r;
+      if (t < T && e < E) dst[(size_t)t * E + e] = acc_hi[j][r] + acc_lo[j][r];
+    }
+  }
+}
+
+// Order used by every selection step: higher score first, lower index on ties.
+__device__ __forceinline__ bool beats(float v, int i, float ov, int oi) { return v > ov || (v == ov && i < oi); }
+
+// grid: ceil(T/4); block 256: one wave per token.
+// src: partial logits [splits][T][E] (from_partials) or post-sigmoid scores [T][E].
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ src, int splits, bool from_partials,
+                                                     const float* __restrict__ bias, float* __restrict__ scores_out,
+                                                     int T, int E, int G, int TG, int K, float scale,
+                                                     int32_t* __restrict__ ids, float* __restrict__ wout) {
+#pragma clang fp contract(off)
+  __shared__ float s_sc[4][256];
+  __shared__ float s_gs[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  const bool active = t < T;
+  const int gsz = E / G;
+
+  float v[4];
+  bool valid[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = 0.f;
+    if (active && e < E) {
+      if (from_partials) {
+        float L = src[(size_t)t * E + e];
+        for (int s = 1; s < splits; ++s) L = L + src[((size_t)s * T + t) * E + e];
+        if (bias) L = L + bias[e];
+        v[j] = 1.0f / (1.0f + expf(-L));
+        if (scores_out) scores_out[(size_t)t * E + e] = v[j];
+      } else {
+        v[j] = src[(size_t)t * E + e];
+      }
+      s_sc[wave][e] = v[j];
+    }
+  }
+  __syncthreads();
+
+  // group score: sum of the two largest scores of the group (one lane per group)
+  if (active && lane < G) {
+    float m1 = -INFINITY, m2 = -INFINITY;
+    const float* g = &s_sc[wave][lane * gsz];
+    for (int i = 0; i < gsz; ++i) {
+      const float s = g[i];
+      if (s > m1) {
+        m2 = m1;
+        m1 = s;
+      } else if (s > m2) {
+        m2 = s;
+      }
+    }
+    s_gs[wave][lane] = (gsz >= 2) ? (m1 + m2) : m1;
+  }
+  __syncthreads();
+
+  bool keep = false;
+  if (active && lane < G) {
+    const float mine = s_gs[wave][lane];
+    int rank = 0;
+    for (int g = 0; g < G; ++g) rank += beats(s_gs[wave][g], g, mine, lane) ? 1 : 0;
+    keep = rank < TG;
+  }
+  const unsigned long long kept = __ballot(keep);
+  if (!active) return;  // no barrier follows
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    valid[j] = e < E && ((kept >> (e / gsz)) & 1ull);
+  }
+
+  float total = 0.f;
+  float my_v = 0.f;
+  int my_e = 0;
+  for (int k = 0; k < K; ++k) {
+    float bv = 0.f;
+    int be = 0x7fffffff;
+    bool bok = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (valid[j] && (!bok || beats(v[j], e, bv, be))) {
+        bv = v[j];
+        be = e;
+        bok = true;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      const int ook = __shfl_xor(int(bok), off);
+      if (ook && (!bok || beats(ov, oe, bv, be))) {
+        bv = ov;
+        be = oe;
+        bok = true;
+      }
+    }
+    // bv/be are now the same on every lane
+    if ((be & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (be == lane + 64 * j) valid[j] = false;
+    }
+    total = total + bv;
+    if (lane == k) {
+      my_v = bv;
+      my_e = be;
+    }
+  }
+  if (lane < K) {
+    const float q = my_v / total;
+    ids[(size_t)t * K + lane] = my_e;
+    wout[(size_t)t * K + lane] = q * scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part, int T, int H, int E, int splits,
+                                int k_per_split, hipStream_t st) {
+  dim3 grid((T + kRtM - 1) / kRtM, (E + kRtN - 1) / kRtN, splits);
+  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, x, wr, part, T, H, E, k_per_split);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* src, int splits, bool from_partials, const float* bias, float* scores_out,
+                         int T, int E, int G, int TG, int K, float scale, int32_t* ids, float* w, hipStream_t st) {
+  dim3 grid((T + 3) / 4);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, st, src, splits, from_partials, bias, scores_out, T, E, G,
+                     TG, K, scale, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace beam

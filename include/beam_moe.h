@@ -1,0 +1,146 @@
+/*
+ * beam_moe.h -- forward pass of one Beam mixture-of-experts block on an
+ * AMD Instinct MI355X (gfx950), as a plain C ABI.
+ *
+ * What the block computes (Beam launch blog, "Beam 501B", Hugging Face blog,
+ * section "mixture of experts"; config.json fields n_group, topk_group,
+ * norm_topk_prob, routed_scaling_factor as listed in the oferry.com analysis):
+ *
+ *   1. router: s[t,e] = sigmoid(sum_h x[t,h] * W_r[e,h] + b[e]), in FP32;
+ *   2. the E experts form G contiguous groups of E/G; a group's score is the
+ *      sum of its two highest s; the TG best groups are kept; the K experts
+ *      with the highest s inside the kept groups are selected (no shared
+ *      expert);
+ *   3. w[t,k] = s[t,id_k] / sum_j s[t,id_j] * routed_scaling   (x2.5 for Beam);
+ *   4. every selected expert is a SwiGLU MLP:
+ *        y = W_down (silu(W_gate x) * (W_up x)), no biases;
+ *      the SwiGLU product is FP32 (launch blog, "residual stream" section);
+ *   5. out[t] = sum_k w[t,k] * y[t,k].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *   never allocates or frees device memory; scratch space is the caller's
+ *   workspace (see beam_moe_workspace_bytes).
+ * - Every call is asynchronous on `stream` (a hipStream_t, NULL = the null
+ *   stream) and performs no host synchronisation.
+ * - Arguments are validated on the host before anything is launched; on
+ *   failure a negative status is returned and no output is touched. A failed
+ *   launch returns BEAM_MOE_ERR_HIP; outputs are then undefined.
+ * - Outputs are fully overwritten, never accumulated into. Outputs must not
+ *   alias inputs.
+ * - Layouts are row-major. Weights use the [out, in] ("Linear") layout.
+ *   bf16 tensors are raw bfloat16 bit patterns (uint16). Every pointer must be
+ *   16-byte aligned.
+ * - Supported dims: 1 <= num_groups <= 64, num_experts <= 256,
+ *   num_experts % num_groups == 0, 1 <= topk_groups <= num_groups,
+ *   1 <= topk <= min(16, topk_groups * num_experts / num_groups),
+ *   hidden % 256 == 0, intermediate % 128 == 0, routed_scaling finite.
+ *   0 <= T and T * topk < 2^31; T == 0 is a valid no-op.
+ * - Determinism: no floating-point atomics are used; every output, integer
+ *   or floating point, is bitwise identical from run to run on one device.
+ * - Ties in scores are broken towards the lower group / expert index; the K
+ *   ids of a token are listed by score descending, then id ascending.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct beam_moe_dims {
+  int32_t hidden;        /* H: 5120 for Beam (launch blog, attention section)      */
+  int32_t intermediate;  /* I: 2560 for Beam (launch blog, mixture of experts)     */
+  int32_t num_experts;   /* E: 256                                                 */
+  int32_t num_groups;    /* G: 8  (config.json n_group)                            */
+  int32_t topk_groups;   /* TG: 4 (config.json topk_group)                         */
+  int32_t topk;          /* K: 8  experts per token                                */
+  float routed_scaling;  /* 2.5   (config.json routed_scaling_factor)              */
+} beam_moe_dims;
+
+enum {
+  BEAM_MOE_OK = 0,
+  BEAM_MOE_ERR_INVALID_ARG = -1, /* null pointer, misaligned pointer, negative T */
+  BEAM_MOE_ERR_UNSUPPORTED = -2, /* dims outside the supported set above        */
+  BEAM_MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+  BEAM_MOE_ERR_HIP = -4          /* a HIP launch failed                          */
+};
+
+/* Bytes of workspace that beam_moe_route, beam_moe_dispatch and
+ * beam_moe_forward need for T tokens (one size serves all three; it grows
+ * linearly in T: at Beam dims about 26 KB per token, mostly the bf16 SwiGLU
+ * activations [T*K, I] and the FP32 expert outputs [T*K, H]).
+ * Returns SIZE_MAX for invalid or unsupported dims. */
+size_t beam_moe_workspace_bytes(const beam_moe_dims* dims, int32_t T);
+
+/* Router + group-limited top-k (steps 1-3 above).
+ *   x_bf16      [T, H]  bf16 hidden states
+ *   w_router    [E, H]  fp32 router weight
+ *   logit_bias  [E]     fp32, added to the logit before the sigmoid; NULL = none
+ *   topk_ids    [T, K]  int32 out
+ *   topk_w      [T, K]  fp32 out: normalised weights times routed_scaling
+ *   scores_out  [T, E]  fp32 out, post-sigmoid scores; NULL = not written
+ *   ws, ws_bytes        workspace of at least beam_moe_workspace_bytes(dims, T)
+ * The logits are accumulated in FP32 (bf16 x times fp32 W_r, exact products). */
+int beam_moe_route(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                   const float* logit_bias, int32_t* topk_ids, float* topk_w, float* scores_out, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* Steps 2-3 on caller-supplied post-sigmoid FP32 scores [T, E].
+ * Fixed FP32 evaluation order, so results are reproducible bit for bit by any
+ * implementation that follows it:
+ *   group score      = fl32(s_first + s_second) of the group's two largest;
+ *   sum              = fl32 running sum of the K selected scores in output order;
+ *   topk_w[t,k]      = fl32(fl32(s_k / sum) * routed_scaling)   (IEEE division).
+ * Needs no workspace. */
+int beam_moe_select(const beam_moe_dims* dims, int32_t T, const float* scores, int32_t* topk_ids, float* topk_w,
+                    void* stream);
+
+/* Counting-sort dispatch of the T*K (token, slot) pairs by expert.
+ *   topk_ids        [T, K]  int32 in [0, E) (ids outside it are skipped and
+ *                           leave the outputs undefined, without faulting)
+ *   expert_counts   [E]     int32 out: pairs routed to each expert
+ *   expert_offsets  [E+1]   int32 out: exclusive prefix sum, [E] = T*K
+ *   sorted_slots    [T*K]   int32 out: values i = t*K + k, ascending expert,
+ *                           ascending i inside an expert (stable; unique) */
+int beam_moe_dispatch(const beam_moe_dims* dims, int32_t T, const int32_t* topk_ids, int32_t* expert_counts,
+                      int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole block (steps 1-5).
+ *   w_gate, w_up  [E, I, H] bf16;  w_down [E, H, I] bf16
+ *   out           [T, H] fp32 out
+ *   topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots: as above,
+ *   written as by-products (caller-owned, all required).
+ * Expert GEMMs run on bf16 MFMA with FP32 accumulation; silu(g)*u is FP32
+ * and rounded to bf16 (RNE) as the down projection's input; expert outputs
+ * and the weighted sum are FP32, summed over k in ascending k order. */
+int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                     const float* logit_bias, const void* w_gate, const void* w_up, const void* w_down, float* out,
+                     int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                     int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* Diagnostics: device time of the stages of beam_moe_forward.
+ * beam_moe_timing_enable(1) makes later beam_moe_forward calls record HIP
+ * events between their stages on the caller's stream (a marker per stage,
+ * no synchronisation; the events are created by the library on first use and
+ * kept for reuse). beam_moe_timing_read waits for the last recorded call,
+ * writes for each stage the milliseconds summed over the calls recorded since
+ * the previous read (stage_ms[s], s < *n_stages <= max_stages) and the number
+ * of calls, then starts a new recording window. Stage names come from
+ * beam_moe_stage_name. Not meant for concurrent calls from several threads. */
+int beam_moe_timing_enable(int enable);
+int beam_moe_timing_read(float* stage_ms, int32_t max_stages, int32_t* n_stages, int32_t* calls);
+const char* beam_moe_stage_name(int32_t stage);
+
+/* Static string for a status code. */
+const char* beam_moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEAM_MOE_H */

@@ -1,0 +1,256 @@
+"""GPU parity of the HIP path (through the C ABI) against the FP64 oracle.
+
+Every case prints its name before touching the GPU, so that a failing run
+names it.  Sizes: small cases run the oracle on every token and span several
+tiles with a ragged tail; the Beam-size cases (decode T=64, prefill T=16384,
+skewed T=8192) run the exact launch configuration of the benchmark and check
+sampled tokens against the oracle, and the dispatch of every token by its
+defining properties.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from grouped_top_routing_fp32_amd import binding, synth
+from oracle import beam_moe_oracle as orc
+from parity_helpers import Problem, check_dispatch_valid, compare_routing, f64, forward_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TINY = synth.WORKLOADS["tiny"].dims
+
+
+def _announce(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def beam_experts():
+    _announce("generate Beam expert weights on the device")
+    wl = synth.WORKLOADS["decode"]
+    ex = synth.make_experts(wl, DEV)
+    torch.cuda.synchronize()
+    return ex
+
+
+# --------------------------------------------------------------------------
+# shared generator: identical bits on CPU and GPU
+# --------------------------------------------------------------------------
+def test_generator_bits_match_cpu():
+    _announce("generator cpu vs gpu")
+    wl = synth.WORKLOADS["decode"]
+    a = synth.normal((2560, 5120), 0.02, 0, synth.TENSOR_GATE, 3, torch.bfloat16, DEV).cpu()
+    b = synth.normal((2560, 5120), 0.02, 0, synth.TENSOR_GATE, 3, torch.bfloat16, "cpu")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    xr = synth.x_rows(wl, [0, 17, 63], DEV).cpu()
+    assert torch.equal(xr.view(torch.int16), synth.x_rows(wl, [0, 17, 63], "cpu").view(torch.int16))
+    wr = synth.make_router(wl, DEV).cpu()
+    assert torch.equal(wr.view(torch.int32), synth.make_router(wl, "cpu").view(torch.int32))
+
+
+# --------------------------------------------------------------------------
+# selection on supplied FP32 scores: bit-exact
+# --------------------------------------------------------------------------
+def _select_case(d, scores_np):
+    scores = torch.from_numpy(scores_np.astype(np.float32)).to(DEV)
+    ids, w = binding.beam_moe_select(d, scores)
+    ids_o, w_o = orc.select_fp32(scores_np.astype(np.float32), d.num_groups, d.topk_groups, d.topk,
+                                 d.routed_scaling)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.array_equal(w.cpu().numpy().view(np.int32), w_o.view(np.int32))
+
+
+@pytest.mark.parametrize("kind", ["uniform", "coarse_ties", "group_sum_ties", "boundary_ties", "all_equal"])
+def test_select_bit_exact_beam(kind):
+    _announce(f"select beam {kind}")
+    rng = np.random.default_rng(["uniform", "coarse_ties", "group_sum_ties", "boundary_ties", "all_equal"].index(kind))
+    T, E = 333, 256
+    if kind == "uniform":
+        s = rng.random((T, E))
+    elif kind == "coarse_ties":
+        s = np.floor(rng.random((T, E)) * 8) / 8 + 0.0625
+    elif kind == "group_sum_ties":
+        # every group holds the pair (a, b) or (b, a) or (a + d, b - d) with equal sums
+        s = rng.random((T, E)) * 0.25
+        for t in range(T):
+            for g in range(8):
+                i, j = rng.choice(32, 2, replace=False)
+                s[t, g * 32 + i], s[t, g * 32 + j] = (0.75, 0.5) if g % 2 else (0.5, 0.75)
+    elif kind == "boundary_ties":
+        s = rng.random((T, E)) * 0.5
+        for t in range(T):
+            hot = rng.choice(E, 12, replace=False)
+            s[t, hot] = 0.875
+    else:
+        s = np.full((T, E), 0.5)
+    _select_case(synth.BEAM, s)
+
+
+def test_select_bit_exact_router_scores():
+    _announce("select on oracle scores (router_dispatch, 512 tokens)")
+    wl = synth.with_tokens(synth.WORKLOADS["router_dispatch"], 512)
+    X = f64(synth.make_x(wl))
+    S = orc.sigmoid(orc.router_logits(X, f64(synth.make_router(wl))))
+    _select_case(wl.dims, S)
+
+
+@pytest.mark.parametrize("dims", [TINY, synth.Dims(256, 128, 64, 8, 3, 6), synth.Dims(256, 128, 200, 8, 8, 16),
+                                  synth.Dims(256, 128, 8, 1, 1, 8), synth.Dims(256, 128, 32, 32, 5, 5),
+                                  synth.Dims(256, 128, 1, 1, 1, 1)])
+def test_select_bit_exact_shapes(dims):
+    _announce(f"select shapes {dims}")
+    rng = np.random.default_rng(dims.num_experts)
+    s = rng.random((77, dims.num_experts))
+    s[::3] = np.round(s[::3] * 4) / 4
+    _select_case(dims, s)
+
+
+def test_hand_example_on_gpu():
+    _announce("hand-worked routing example")
+    import json
+    import os
+    h = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "routing_hand_example.json")))
+    d = synth.Dims(256, 128, h["num_experts"], h["num_groups"], h["topk_groups"], h["topk"], h["routed_scaling"])
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device=DEV)
+    x[0, 0] = 1.0
+    wr = torch.zeros((16, 256), dtype=torch.float32, device=DEV)
+    wr[:, 0] = torch.tensor([math.log(a / (1 - a)) for a in h["scores"]], dtype=torch.float32)
+    ids, w, s = binding.beam_moe_route(d, x, wr, want_scores=True)
+    assert ids.cpu().tolist()[0] == h["expected_ids"]
+    np.testing.assert_allclose(w.cpu().numpy()[0], h["expected_weights"], rtol=0, atol=2e-6)
+    np.testing.assert_allclose(s.cpu().numpy()[0], h["scores"], rtol=0, atol=2e-7)
+
+
+# --------------------------------------------------------------------------
+# dispatch: bit-exact on oracle ids
+# --------------------------------------------------------------------------
+def _dispatch_case(d, ids_np):
+    ids = torch.from_numpy(ids_np.astype(np.int32)).to(DEV)
+    c, o, s = binding.beam_moe_dispatch(d, ids)
+    c2, o2, s2 = binding.beam_moe_dispatch(d, ids)
+    co, oo, so = orc.dispatch(ids_np, d.num_experts)
+    assert np.array_equal(c.cpu().numpy(), co)
+    assert np.array_equal(o.cpu().numpy(), oo)
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert torch.equal(c, c2) and torch.equal(o, o2) and torch.equal(s, s2)
+
+
+@pytest.mark.parametrize("case", ["uniform", "skewed", "one_expert", "single_token", "ragged", "large"])
+def test_dispatch_bit_exact(case):
+    _announce(f"dispatch {case}")
+    d = synth.BEAM
+    rng = np.random.default_rng(1)
+    T = {"uniform": 300, "skewed": 999, "one_expert": 40, "single_token": 1, "ragged": 37, "large": 16384}[case]
+    if case == "one_expert":
+        d = synth.Dims(5120, 2560, 256, 8, 4, 1)
+        ids = np.full((T, 1), 200)
+    elif case == "skewed":
+        p = np.arange(1, 257, dtype=np.float64) ** -1.2
+        p /= p.sum()
+        ids = np.stack([rng.choice(256, 8, replace=False, p=p) for _ in range(T)])
+    else:
+        ids = np.stack([rng.choice(256, 8, replace=False) for _ in range(T)])
+    _dispatch_case(d, ids)
+
+
+def test_dispatch_on_router_ids():
+    _announce("dispatch on oracle router ids (router_dispatch, T=4096)")
+    wl = synth.WORKLOADS["router_dispatch"]
+    d = wl.dims
+    p = Problem(wl, DEV)
+    X, ids_o, w_o, S_o, GS_o, m = p.route_oracle()
+    _dispatch_case(d, ids_o)
+
+
+# --------------------------------------------------------------------------
+# router end to end (FP32 on the GPU vs FP64 oracle)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("router_dispatch", 4096), ("skewed", 1000)])
+def test_route_end_to_end(name, T):
+    _announce(f"route e2e {name} T={T}")
+    wl = synth.with_tokens(synth.WORKLOADS[name], T)
+    d = wl.dims
+    p = Problem(wl, DEV, experts=(None, None, None))
+    ids, w, s = binding.beam_moe_route(d, p.x, p.wr, p.bias, want_scores=True)
+    X, ids_o, w_o, S_o, GS_o, m = p.route_oracle()
+    np.testing.assert_allclose(s.cpu().numpy(), S_o, rtol=0, atol=2e-6)
+    excluded = compare_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_o, w_o, S_o, m, d)
+    print(f"  excluded near-tie tokens: {excluded} of {T}")
+    assert excluded <= max(2, T // 200)
+    ids2, w2, s2 = binding.beam_moe_route(d, p.x, p.wr, p.bias, want_scores=True)
+    assert torch.equal(ids, ids2) and torch.equal(w, w2) and torch.equal(s, s2)
+    c, o, sl = binding.beam_moe_dispatch(d, ids)
+    check_dispatch_valid(ids.cpu().numpy(), c.cpu().numpy(), o.cpu().numpy(), sl.cpu().numpy(), d.num_experts)
+
+
+# --------------------------------------------------------------------------
+# whole block
+# --------------------------------------------------------------------------
+MID = {
+    # stream path (few rows per expert), several column blocks, ragged row passes
+    "mid_stream": (synth.Workload("mid_stream", 45, synth.Dims(512, 384, 64, 8, 4, 6), router_sigma=0.06), None),
+    # tiled path, 16 experts, ~225 rows each: full and ragged 256-row tiles
+    "mid_tiled": (synth.Workload("mid_tiled", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06), None),
+    # tiled path with Beam's expert count: one partial tile per expert
+    "mid_tiled_e256": (synth.Workload("mid_tiled_e256", 1100, synth.Dims(768, 256, 256, 8, 4, 8), router_sigma=0.04),
+                       None),
+    # stream path with skewed bias: some experts get more than 16 rows (several row passes)
+    "mid_stream_skew": (synth.Workload("mid_stream_skew", 60, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
+                                       zipf_s=1.2), None),
+}
+
+
+def test_forward_tiny():
+    _announce("forward tiny (all tokens)")
+    p = Problem(synth.WORKLOADS["tiny"], DEV)
+    bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
+    excluded, worst = forward_parity(p, bufs)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_forward_mid(name):
+    _announce(f"forward {name} (all tokens)")
+    wl, _ = MID[name]
+    p = Problem(wl, DEV)
+    bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
+    excluded, worst = forward_parity(p, bufs)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+    out1 = bufs.out.clone()
+    binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd, bufs=bufs)
+    assert torch.equal(out1, bufs.out)
+
+
+def _beam_forward(name, beam_experts, sample):
+    wl = synth.WORKLOADS[name]
+    p = Problem(wl, DEV, experts=beam_experts)
+    bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
+    torch.cuda.synchronize()
+    excluded, worst = forward_parity(p, bufs, sample)
+    print(f"  sampled {len(sample)} tokens, excluded {excluded}, worst error / tolerance {worst:.3f}")
+    out1 = bufs.out.clone()
+    ids1 = bufs.ids.clone()
+    slots1 = bufs.slots.clone()
+    binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd, bufs=bufs)
+    assert torch.equal(out1, bufs.out) and torch.equal(ids1, bufs.ids) and torch.equal(slots1, bufs.slots)
+    return p, bufs
+
+
+def test_forward_decode(beam_experts):
+    _announce("forward decode T=64")
+    _beam_forward("decode", beam_experts, np.arange(0, 64, 7))
+
+
+def test_forward_prefill(beam_experts):
+    _announce("forward prefill T=16384")
+    _beam_forward("prefill", beam_experts, [0, 1, 5000, 9999, 16383])
+
+
+def test_forward_skewed(beam_experts):
+    _announce("forward skewed T=8192")
+    p, bufs = _beam_forward("skewed", beam_experts, [0, 4095, 8191])
+    counts = bufs.counts.cpu().numpy()
+    assert counts.max() >= 20 * counts.mean()
