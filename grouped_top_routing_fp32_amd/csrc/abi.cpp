@@ -26,16 +26,19 @@ int tiled_gateup_rows();
 int tiled_down_rows();
 int tiled_gateup_cols();
 int tiled_down_cols();
+int scale_cols();
 hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, int H, int I,
-                                int K, hipStream_t st);
-hipError_t launch_down_stream(const uint16_t* h, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                              int max_tiles, const uint16_t* wd, float* y, int H, int I, hipStream_t st);
+                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
+                                uint8_t* hscale, int H, int I, int K, hipStream_t st);
+hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                              const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
+                              hipStream_t st);
 hipError_t launch_gateup_tiled(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                               int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, int H, int I,
-                               int K, hipStream_t st);
-hipError_t launch_down_tiled(const uint16_t* h, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                             int max_tiles, const uint16_t* wd, float* y, int H, int I, hipStream_t st);
+                               int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
+                               int H, int I, int K, hipStream_t st);
+hipError_t launch_down_tiled(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                             const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
+                             hipStream_t st);
 hipError_t launch_combine(const float* y, const float* w, float* out, int T, int H, int K, hipStream_t st);
 }  // namespace beam
 
@@ -56,7 +59,7 @@ bool dims_ok(const beam_moe_dims* d) {
   const int cand = TG * (E / G);
   if (K < 1 || K > 16 || K > cand) return false;
   if (d->hidden < 256 || d->hidden % 256 != 0) return false;
-  if (d->intermediate < 128 || d->intermediate % 128 != 0) return false;
+  if (d->intermediate < 128 || d->intermediate % 128 != 0 || d->intermediate > 32768) return false;
   if (!std::isfinite(d->routed_scaling)) return false;
   return true;
 }
@@ -81,7 +84,7 @@ struct Plan {
   int mt_a, mt_b, max_tiles_a, max_tiles_b;
   size_t off_tiles_a, off_tiles_b, off_ntiles;
   // activations
-  size_t off_h, off_y;
+  size_t off_h, off_hscale, off_y;
   size_t total;
 };
 
@@ -127,6 +130,8 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
   off = align_up(off + 2 * sizeof(int32_t));
   p->off_h = off;
   off = align_up(off + (size_t)p->n * p->I * 2);
+  p->off_hscale = off;
+  off = align_up(off + (size_t)p->n * (p->I / beam::scale_cols()));
   p->off_y = off;
   off = align_up(off + (size_t)p->n * p->H * sizeof(float));
   p->total = off;
@@ -277,6 +282,7 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   beam::Tile* tiles_b = at<beam::Tile>(ws, p.off_tiles_b);
   int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
   uint16_t* h = at<uint16_t>(ws, p.off_h);
+  uint8_t* hscale = at<uint8_t>(ws, p.off_hscale);
   float* y = at<float>(ws, p.off_y);
   hipEvent_t* ev = timing_slot();
 
@@ -294,16 +300,18 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
                                  sorted_slots, tiles_a, p.mt_a, tiles_b, p.mt_b, ntiles, st));
   BEAM_TRY(mark(ev, kStGateUp, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_gateup_stream(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, p.H, p.I, p.K,
-                                        st));
+    BEAM_TRY(beam::launch_gateup_stream(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, hscale, p.H,
+                                        p.I, p.K, st));
   else
-    BEAM_TRY(beam::launch_gateup_tiled(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, p.H, p.I, p.K,
-                                       st));
+    BEAM_TRY(beam::launch_gateup_tiled(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, hscale, p.H,
+                                       p.I, p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_down_stream(h, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I, st));
+    BEAM_TRY(beam::launch_down_stream(h, hscale, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I,
+                                      st));
   else
-    BEAM_TRY(beam::launch_down_tiled(h, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I, st));
+    BEAM_TRY(beam::launch_down_tiled(h, hscale, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I,
+                                     st));
   BEAM_TRY(mark(ev, kStCombine, st));
   BEAM_TRY(beam::launch_combine(y, topk_w, out, T, p.H, p.K, st));
   BEAM_TRY(mark(ev, kNumStages, st));

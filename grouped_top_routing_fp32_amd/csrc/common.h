@@ -7,6 +7,7 @@
 namespace beam {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -34,7 +35,56 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// Eight bf16 values (one 16-byte operand) to eight fp16 values. bf16 has 8
+// significant bits and fp16 11, so the conversion is exact for magnitudes in
+// fp16's normal range [2^-14, 65504]; smaller magnitudes become fp16
+// subnormals rounded toward zero (error below 2^-24).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16);
+    const float hi = __uint_as_float(v[i] & 0xFFFF0000u);
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return r;
+}
+
+// Same, each value multiplied by 2^s first (exact).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_scaled(u32x4 v, int s) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(v[i] << 16), s);
+    const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), s);
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return r;
+}
+
+// Power-of-two scale exponent s >= 0 for a block of SwiGLU activations whose
+// largest magnitude is maxabs: maxabs * 2^-s < 2^15, so every value of the
+// block fits fp16 (max 65504) after scaling by 2^-s.
+__device__ __forceinline__ int act_scale_exp(float maxabs) {
+  const int e = __builtin_amdgcn_frexp_expf(maxabs);  // maxabs < 2^e
+  return e > 15 ? e - 15 : 0;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
 
 // One tile of a grouped GEMM: rows [row_start, row_start + rows) of the
 // expert-sorted order, all belonging to `expert`.

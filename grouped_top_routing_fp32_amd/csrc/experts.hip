@@ -1,155 +1,189 @@
-// Grouped SwiGLU expert GEMMs of the Beam MoE block (gfx950, bf16 MFMA,
-// FP32 accumulation).
+// Grouped SwiGLU expert GEMMs of the Beam MoE block (gfx950 MFMA, FP32
+// accumulation).
 //
 // Beam launch blog, "mixture of experts" section: each expert is a SwiGLU
 // MLP with intermediate size 2560 (hidden 5120); the "residual stream"
 // section puts the SwiGLU product in FP32.  Per expert e and routed row r:
-//   h[r] = silu(W_gate[e] x[r]) * (W_up[e] x[r])      FP32, stored as bf16 (RNE)
-//   y[r] = W_down[e] h[r]                              FP32
+//   h[r] = silu(W_gate[e] x[r]) * (W_up[e] x[r])   bf16 MFMA, SwiGLU in FP32
+//   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 out
+// h is handed to the down projection as fp16 (11 significant bits against
+// bf16's 8) with a power-of-two scale 2^-s per block of 64 columns of a row
+// group, s chosen so the block's largest magnitude stays below 2^15; W_down
+// is converted from bf16 to fp16 exactly (times 2^s) as it is loaded.
 // Rows are processed in expert-sorted order (the dispatch permutation); a
 // tile table produced by the dispatch maps workgroups to (expert, rows).
 //
 // Two kernel families:
 //   *_stream_kernel  few rows per expert (decode): weights are streamed once
-//       from HBM straight into MFMA operand registers with non-temporal
-//       16-byte loads; the K dimension is split over the 4 waves and reduced
-//       in LDS in a fixed order; rows are taken 16 at a time.
+//       from HBM straight into MFMA operand registers; rows are taken 16 at a
+//       time and the scale group is (16-row pass, 64 columns).
 //   *_tiled_kernel   many rows per expert (prefill): LDS double-buffered
 //       BM x BN x 64 tiles, 8 waves, 16x16x32 MFMAs; gate and up share the A
-//       tile and the SwiGLU product is formed in registers.
+//       tile and the SwiGLU product is formed in registers; the scale group
+//       is (row tile, BN columns).
 #include "common.h"
 
 namespace beam {
 
+constexpr int kMaxScaleBlocks = 512;  // I <= 32768
+
 // ---------------------------------------------------------------------------
 // stream kernels (small row counts)
 // ---------------------------------------------------------------------------
-constexpr int kStreamN = 64;  // output columns per workgroup (per gate and per up)
-constexpr int kStreamRows = 16;
+// A workgroup owns one expert (all its rows, taken 16 at a time) and 64
+// output columns; wave w owns columns [16w, 16w+16) over the whole K range,
+// so no cross-wave reduction is needed.  Loads run U MFMA steps ahead of the
+// math (two register stages) and use ordinary cached loads: a 16-byte operand
+// load touches half of a 128-byte line, and the other half is read by the
+// next step.
+constexpr int kStreamN = 64;     // output columns per workgroup
+constexpr int kStreamRows = 16;  // rows per pass
+constexpr int kScaleCols = 64;   // SwiGLU activation columns that share one scale
 
 // grid: (max_tiles, I / 64); block 256.  One tile = all rows of one expert.
+// Writes h (fp16 bits, scaled by 2^-s) and s per (row, 64-column block).
+template <int U>
 __global__ __launch_bounds__(256) void gateup_stream_kernel(const uint16_t* __restrict__ x,
                                                             const int32_t* __restrict__ sorted_slots,
                                                             const Tile* __restrict__ tiles,
                                                             const int32_t* __restrict__ ntiles,
                                                             const uint16_t* __restrict__ wg,
                                                             const uint16_t* __restrict__ wu,
-                                                            uint16_t* __restrict__ h, int H, int I, int K) {
-  __shared__ __attribute__((aligned(16))) float red[4][8][64][4];
+                                                            uint16_t* __restrict__ h, uint8_t* __restrict__ hscale,
+                                                            int H, int I, int K) {
+  __shared__ float smax[4];
   if ((int)blockIdx.x >= ntiles[0]) return;
   const Tile tl = tiles[blockIdx.x];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n0 = blockIdx.y * kStreamN;
-  const int kq = H / 4;
-  const int kbeg = wave * kq;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = blockIdx.y * kStreamN + wave * 16 + (lane & 15);
   const int kk = (lane >> 4) * 8;
   const size_t ebase = (size_t)tl.expert * I * H;
-  const uint16_t* pg = wg + ebase + (size_t)(n0 + (lane & 15)) * H + kk;
-  const uint16_t* pu = wu + ebase + (size_t)(n0 + (lane & 15)) * H + kk;
+  const uint16_t* pg = wg + ebase + (size_t)col * H + kk;
+  const uint16_t* pu = wu + ebase + (size_t)col * H + kk;
+  const int nsb = I / kScaleCols;
+  const int steps = H / (32 * U);
 
   for (int p = 0; p < tl.rows; p += kStreamRows) {
     const int m = lane & 15;
     const bool rv = p + m < tl.rows;
     const int tok = rv ? sorted_slots[tl.row_start + p + m] / K : 0;
     const uint16_t* pa = x + (size_t)tok * H + kk;
-    f32x4 acc[8];
+    f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
+    u32x4 g0[U], u0[U], a0[U], g1[U], u1[U], a1[U];
+    auto load = [&](u32x4(&g)[U], u32x4(&uu)[U], u32x4(&a)[U], int k) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int k = kbeg; k < kbeg + kq; k += 32) {
-      u32x4 bgv[4], buv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bgv[j] = ldg16_stream(pg + (size_t)j * 16 * H + k);
-        buv[j] = ldg16_stream(pu + (size_t)j * 16 * H + k);
+      for (int u = 0; u < U; ++u) {
+        g[u] = ldg16(pg + k + 32 * u);
+        uu[u] = ldg16(pu + k + 32 * u);
+        a[u] = rv ? ldg16(pa + k + 32 * u) : u32x4{0u, 0u, 0u, 0u};
       }
-      u32x4 a = rv ? ldg16(pa + k) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto math = [&](u32x4(&g)[U], u32x4(&uu)[U], u32x4(&a)[U]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j] = mfma16x16x32(a, bgv[j], acc[j]);
-        acc[4 + j] = mfma16x16x32(a, buv[j], acc[4 + j]);
+      for (int u = 0; u < U; ++u) {
+        ag = mfma16x16x32(a[u], g[u], ag);
+        au = mfma16x16x32(a[u], uu[u], au);
       }
+    };
+    load(g0, u0, a0, 0);
+    for (int s = 0; s < steps; s += 2) {
+      if (s + 1 < steps) load(g1, u1, a1, (s + 1) * 32 * U);
+      math(g0, u0, a0);
+      if (s + 2 < steps) load(g0, u0, a0, (s + 2) * 32 * U);
+      if (s + 1 < steps) math(g1, u1, a1);
     }
+    // SwiGLU in FP32; one power-of-two scale per (16-row pass, 64-column block)
+    float v[4];
+    float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4*>(&red[wave][j][lane][0]) = acc[j];
+    for (int r = 0; r < 4; ++r) {
+      const int row = (lane >> 4) * 4 + r;
+      v[r] = (p + row < tl.rows) ? silu_f32(ag[r]) * au[r] : 0.f;
+      mx = fmaxf(mx, fabsf(v[r]));
+    }
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
     __syncthreads();
-    // 16 rows x 64 columns of h; four per thread
+    const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int o = tid + 256 * q;
-      const int j = o >> 8;
-      const int ln = (o >> 2) & 63;
-      const int r = o & 3;
-      float g = red[0][j][ln][r], u = red[0][4 + j][ln][r];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        g += red[w][j][ln][r];
-        u += red[w][4 + j][ln][r];
+    for (int r = 0; r < 4; ++r) {
+      const int row = (lane >> 4) * 4 + r;
+      if (p + row < tl.rows) {
+        const size_t grow = (size_t)(tl.row_start + p + row);
+        h[grow * I + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(v[r], -sexp));
+        if (wave == 0 && (lane & 15) == 0) hscale[grow * nsb + blockIdx.y] = (uint8_t)sexp;
       }
-      const int row = (ln >> 4) * 4 + r;
-      const int col = j * 16 + (ln & 15);
-      if (p + row < tl.rows)
-        h[(size_t)(tl.row_start + p + row) * I + n0 + col] = f32_to_bf16_rne(silu_f32(g) * u);
     }
     __syncthreads();
   }
 }
 
-// grid: (max_tiles, H / 64); block 256.
+// grid: (max_tiles, H / 64); block 256.  y[slot] = W_down[e] h (fp16 MFMA,
+// W_down converted exactly from bf16 and scaled back by 2^s per 64-column
+// block of h).
+template <int U>
 __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __restrict__ h,
+                                                          const uint8_t* __restrict__ hscale,
                                                           const int32_t* __restrict__ sorted_slots,
                                                           const Tile* __restrict__ tiles,
                                                           const int32_t* __restrict__ ntiles,
                                                           const uint16_t* __restrict__ wd, float* __restrict__ y,
                                                           int H, int I) {
-  __shared__ __attribute__((aligned(16))) float red[4][4][64][4];
+  __shared__ uint8_t ssc[kMaxScaleBlocks];
+  __shared__ int sany;
   if ((int)blockIdx.x >= ntiles[0]) return;
   const Tile tl = tiles[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n0 = blockIdx.y * kStreamN;
-  const int kq = I / 4;
-  const int kbeg = wave * kq;
+  const int col = blockIdx.y * kStreamN + wave * 16 + (lane & 15);
   const int kk = (lane >> 4) * 8;
-  const uint16_t* pb = wd + (size_t)tl.expert * H * I + (size_t)(n0 + (lane & 15)) * I + kk;
+  const uint16_t* pb = wd + (size_t)tl.expert * H * I + (size_t)col * I + kk;
+  const int nsb = I / kScaleCols;
+  const int steps = I / (32 * U);
 
   for (int p = 0; p < tl.rows; p += kStreamRows) {
     const int m = lane & 15;
     const bool rv = p + m < tl.rows;
     const uint16_t* pa = h + (size_t)(tl.row_start + p + (rv ? m : 0)) * I + kk;
-    f32x4 acc[4];
+    if (tid == 0) sany = 0;
+    __syncthreads();
+    for (int i = tid; i < nsb; i += 256) {
+      const uint8_t sv = hscale[(size_t)(tl.row_start + p) * nsb + i];
+      ssc[i] = sv;
+      if (sv) sany = 1;
+    }
+    __syncthreads();
+    const bool scaled = sany != 0;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 b0[U], a0[U], b1[U], a1[U];
+    auto load = [&](u32x4(&b)[U], u32x4(&a)[U], int k) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = kbeg; k < kbeg + kq; k += 32) {
-      u32x4 bv[4];
+      for (int u = 0; u < U; ++u) {
+        b[u] = ldg16(pb + k + 32 * u);
+        a[u] = rv ? ldg16(pa + k + 32 * u) : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto math = [&](u32x4(&b)[U], u32x4(&a)[U], int k) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = ldg16_stream(pb + (size_t)j * 16 * I + k);
-      u32x4 a = rv ? ldg16(pa + k) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x32(a, bv[j], acc[j]);
+      for (int u = 0; u < U; ++u) {
+        const u32x4 bh = scaled ? bf16x8_to_f16x8_scaled(b[u], ssc[(k + 32 * u) / kScaleCols])
+                                : bf16x8_to_f16x8(b[u]);
+        acc = mfma16x16x32_f16(a[u], bh, acc);
+      }
+    };
+    load(b0, a0, 0);
+    for (int s = 0; s < steps; s += 2) {
+      if (s + 1 < steps) load(b1, a1, (s + 1) * 32 * U);
+      math(b0, a0, s * 32 * U);
+      if (s + 2 < steps) load(b0, a0, (s + 2) * 32 * U);
+      if (s + 1 < steps) math(b1, a1, (s + 1) * 32 * U);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(&red[wave][j][lane][0]) = acc[j];
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int o = tid + 256 * q;
-      const int j = o >> 8;
-      const int ln = (o >> 2) & 63;
-      const int r = o & 3;
-      float s = red[0][j][ln][r];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) s += red[w][j][ln][r];
-      const int row = (ln >> 4) * 4 + r;
-      const int col = j * 16 + (ln & 15);
-      if (p + row < tl.rows) {
-        const int slot = sorted_slots[tl.row_start + p + row];
-        y[(size_t)slot * H + n0 + col] = s;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int row = (lane >> 4) * 4 + r;
+      if (p + row < tl.rows) y[(size_t)sorted_slots[tl.row_start + p + row] * H + col] = acc[r];
     }
     __syncthreads();
   }
@@ -191,8 +225,10 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 }
 
 // GATEUP: A rows = x[slot / K] (gathered), B = [W_gate[e] rows n0.. ; W_up[e] rows n0..],
-//         out = h[row][n] bf16.  Columns per block: BN of I.
-// !GATEUP: A rows = h[row] (contiguous), B = W_down[e] rows n0.., out = y[slot][n] fp32.
+//         bf16 MFMA; out = h[row][n] fp16 bits scaled by 2^-s, s per (tile, 64-column block)
+//         written to hscale.  Columns per block: BN of I.
+// !GATEUP: A rows = h[row] (contiguous, fp16), B = W_down[e] rows n0.. converted to fp16 while
+//         staged and scaled by 2^s of the k-step's 64-column block; fp16 MFMA; out = y[slot][n] fp32.
 template <bool GATEUP, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __restrict__ act,
                                                            const int32_t* __restrict__ sorted_slots,
@@ -200,11 +236,13 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
                                                            const int32_t* __restrict__ ntiles,
                                                            const uint16_t* __restrict__ w0,
                                                            const uint16_t* __restrict__ w1,
-                                                           void* __restrict__ out, int Kdim, int Ndim, int topk,
-                                                           int nblocks_n, int total_blocks) {
+                                                           void* __restrict__ out, uint8_t* __restrict__ hscale,
+                                                           int Kdim, int Ndim, int topk, int nblocks_n,
+                                                           int total_blocks) {
   using C = TiledCfg<GATEUP, BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLd];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::NB * kLd];
+  __shared__ float smax[8];
 
   const int lin = xcd_remap(blockIdx.x, total_blocks);
   const int tile_id = lin / nblocks_n;
@@ -259,14 +297,24 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
 
   u32x4 ra[C::A_CHUNKS], rb[C::B_CHUNKS];
   const int nk = Kdim / kBK;
+  // down projection: scale exponents of this tile's activation blocks (one per 64-wide k-step)
+  const uint8_t* tscale = GATEUP ? nullptr : hscale + (size_t)tl.row_start * (Kdim / kScaleCols);
+  int snext = GATEUP ? 0 : tscale[0];
+  auto stage_b = [&](int buf, int sexp) {
+#pragma unroll
+    for (int i = 0; i < C::B_CHUNKS; ++i) {
+      u32x4 v = rb[i];
+      if (!GATEUP) v = sexp ? bf16x8_to_f16x8_scaled(v, sexp) : bf16x8_to_f16x8(v);
+      *reinterpret_cast<u32x4*>(&sB[buf][boff[i]]) = v;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = ldg16(asrc[i]);
 #pragma unroll
   for (int i = 0; i < C::B_CHUNKS; ++i) rb[i] = ldg16(bsrc[i]);
 #pragma unroll
   for (int i = 0; i < C::A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(&sA[0][aoff[i]]) = ra[i];
-#pragma unroll
-  for (int i = 0; i < C::B_CHUNKS; ++i) *reinterpret_cast<u32x4*>(&sB[0][boff[i]]) = rb[i];
+  stage_b(0, snext);
   __syncthreads();
 
   const int kk = (lane >> 4) * 8;
@@ -281,6 +329,7 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
       for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = ldg16(asrc[i] + koff);
 #pragma unroll
       for (int i = 0; i < C::B_CHUNKS; ++i) rb[i] = ldg16(bsrc[i] + koff);
+      if (!GATEUP) snext = tscale[kt + 1];
     }
     const uint16_t* A = sA[cur];
     const uint16_t* B = sB[cur];
@@ -298,30 +347,64 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
 #pragma unroll
       for (int i = 0; i < C::RB; ++i)
 #pragma unroll
-        for (int j = 0; j < C::NACC; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < C::NACC; ++j)
+          acc[i][j] = GATEUP ? mfma16x16x32(af[i], bf[j], acc[i][j]) : mfma16x16x32_f16(af[i], bf[j], acc[i][j]);
     }
     if (more) {
 #pragma unroll
       for (int i = 0; i < C::A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(&sA[cur ^ 1][aoff[i]]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < C::B_CHUNKS; ++i) *reinterpret_cast<u32x4*>(&sB[cur ^ 1][boff[i]]) = rb[i];
+      stage_b(cur ^ 1, snext);
     }
     __syncthreads();
   }
 
   // epilogue: lane holds rows 4*(lane/16)+r and column lane%16 of each 16x16 block
+  if (GATEUP) {
+    // SwiGLU in FP32, then one power-of-two scale for the whole tile x BN block
+    float mx = 0.f;
 #pragma unroll
-  for (int i = 0; i < C::RB; ++i) {
+    for (int i = 0; i < C::RB; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wm * C::WROWS + 16 * i + (lane >> 4) * 4 + r;
-      if (row >= tl.rows) continue;
-      if (GATEUP) {
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = wm * C::WROWS + 16 * i + (lane >> 4) * 4 + r < tl.rows;
+#pragma unroll
+        for (int j = 0; j < C::CB; ++j) {
+          const float v = ok ? silu_f32(acc[i][j][r]) * acc[i][C::CB + j][r] : 0.f;
+          acc[i][j][r] = v;
+          mx = fmaxf(mx, fabsf(v));
+        }
+      }
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
+    __syncthreads();
+    float bm = smax[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) bm = fmaxf(bm, smax[w]);
+    const int sexp = act_scale_exp(bm);
+    const int nsb = Ndim / kScaleCols;
+    for (int r = tid; r < tl.rows; r += C::THREADS)
+#pragma unroll
+      for (int b = 0; b < BN / kScaleCols; ++b)
+        hscale[(size_t)(tl.row_start + r) * nsb + n0 / kScaleCols + b] = (uint8_t)sexp;
+#pragma unroll
+    for (int i = 0; i < C::RB; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * C::WROWS + 16 * i + (lane >> 4) * 4 + r;
+        if (row >= tl.rows) continue;
         uint16_t* hrow = reinterpret_cast<uint16_t*>(out) + (size_t)(tl.row_start + row) * Ndim + n0 +
                          wn * C::WCOLS + (lane & 15);
 #pragma unroll
-        for (int j = 0; j < C::CB; ++j) hrow[16 * j] = f32_to_bf16_rne(silu_f32(acc[i][j][r]) * acc[i][C::CB + j][r]);
-      } else {
+        for (int j = 0; j < C::CB; ++j) hrow[16 * j] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[i][j][r], -sexp));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::RB; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * C::WROWS + 16 * i + (lane >> 4) * 4 + r;
+        if (row >= tl.rows) continue;
         const int slot = sorted_slots[tl.row_start + row];
         float* yrow = reinterpret_cast<float*>(out) + (size_t)slot * Ndim + n0 + wn * C::WCOLS + (lane & 15);
 #pragma unroll
@@ -334,6 +417,9 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
 // Tile shapes of the tiled path.
 constexpr int kGuBM = 256, kGuBN = 128;  // gate/up: 256 rows x (128 gate + 128 up) columns
 constexpr int kDnBM = 256, kDnBN = 256;  // down: 256 rows x 256 columns
+// the down kernel reads the activation scales of the gate/up tile with the same rows
+static_assert(kGuBM == kDnBM, "gate/up and down share one tile table");
+static_assert(kGuBN % kScaleCols == 0, "scale blocks tile the gate/up columns");
 
 // ---------------------------------------------------------------------------
 // host launchers
@@ -343,37 +429,46 @@ int tiled_down_rows() { return kDnBM; }
 int tiled_gateup_cols() { return kGuBN; }
 int tiled_down_cols() { return kDnBN; }
 
+int scale_cols() { return kScaleCols; }
+
 hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, int H, int I,
-                                int K, hipStream_t st) {
+                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
+                                uint8_t* hscale, int H, int I, int K, hipStream_t st) {
   dim3 grid(max_tiles, I / kStreamN);
-  hipLaunchKernelGGL(gateup_stream_kernel, grid, dim3(256), 0, st, x, slots, tiles, ntiles, wg, wu, h, H, I, K);
+  // H % 256 == 0, so eight 32-wide steps always divide the K loop
+  hipLaunchKernelGGL(gateup_stream_kernel<8>, grid, dim3(256), 0, st, x, slots, tiles, ntiles, wg, wu, h, hscale, H,
+                     I, K);
   return hipGetLastError();
 }
 
-hipError_t launch_down_stream(const uint16_t* h, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                              int max_tiles, const uint16_t* wd, float* y, int H, int I, hipStream_t st) {
+hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                              const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
+                              hipStream_t st) {
   dim3 grid(max_tiles, H / kStreamN);
-  hipLaunchKernelGGL(down_stream_kernel, grid, dim3(256), 0, st, h, slots, tiles, ntiles, wd, y, H, I);
+  if ((I / 32) % 8 == 0)
+    hipLaunchKernelGGL(down_stream_kernel<8>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y, H, I);
+  else
+    hipLaunchKernelGGL(down_stream_kernel<4>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y, H, I);
   return hipGetLastError();
 }
 
 hipError_t launch_gateup_tiled(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                               int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, int H, int I,
-                               int K, hipStream_t st) {
+                               int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
+                               int H, int I, int K, hipStream_t st) {
   const int nbn = I / kGuBN;
   const int total = max_tiles * nbn;
   hipLaunchKernelGGL((expert_tiled_kernel<true, kGuBM, kGuBN, 4, 2>), dim3(total), dim3(512), 0, st, x, slots,
-                     tiles, ntiles, wg, wu, (void*)h, H, I, K, nbn, total);
+                     tiles, ntiles, wg, wu, (void*)h, hscale, H, I, K, nbn, total);
   return hipGetLastError();
 }
 
-hipError_t launch_down_tiled(const uint16_t* h, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                             int max_tiles, const uint16_t* wd, float* y, int H, int I, hipStream_t st) {
+hipError_t launch_down_tiled(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                             const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
+                             hipStream_t st) {
   const int nbn = H / kDnBN;
   const int total = max_tiles * nbn;
   hipLaunchKernelGGL((expert_tiled_kernel<false, kDnBM, kDnBN, 4, 2>), dim3(total), dim3(512), 0, st, h, slots,
-                     tiles, ntiles, wd, nullptr, (void*)y, I, H, 0, nbn, total);
+                     tiles, ntiles, wd, nullptr, (void*)y, const_cast<uint8_t*>(hscale), I, H, 0, nbn, total);
   return hipGetLastError();
 }
 

@@ -115,9 +115,15 @@ int beam_moe_dispatch(const beam_moe_dims* dims, int32_t T, const int32_t* topk_
  *   out           [T, H] fp32 out
  *   topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots: as above,
  *   written as by-products (caller-owned, all required).
- * Expert GEMMs run on bf16 MFMA with FP32 accumulation; silu(g)*u is FP32
- * and rounded to bf16 (RNE) as the down projection's input; expert outputs
- * and the weighted sum are FP32, summed over k in ascending k order. */
+ * Precision: the gate/up GEMMs run on bf16 MFMA with FP32 accumulation and
+ * silu(g)*u is formed in FP32. It reaches the down projection as fp16 (RNE)
+ * times a power-of-two scale shared by a block of 64 columns of a row group,
+ * chosen so the block's largest magnitude stays below 2^15 (no overflow);
+ * the down projection runs on fp16 MFMA with FP32 accumulation, with W_down
+ * converted from bf16 to fp16 exactly (magnitudes below 2^-14 after scaling
+ * become fp16 subnormals, rounded toward zero). Expert outputs and the
+ * weighted sum are FP32, summed over k in ascending k order.
+ * Supported intermediate sizes additionally satisfy intermediate <= 32768. */
 int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
                      const float* logit_bias, const void* w_gate, const void* w_up, const void* w_down, float* out,
                      int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
