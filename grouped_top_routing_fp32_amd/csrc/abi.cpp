@@ -100,7 +100,7 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
   if (rtiles < 1) rtiles = 1;
   int splits = (256 + rtiles - 1) / rtiles;
   if (splits > ksteps) splits = ksteps;
-  if (splits > 64) splits = 64;
+  if (splits > 16) splits = 16;
   if (splits < 1) splits = 1;
   const int steps_per = (ksteps + splits - 1) / splits;
   p->k_per_split = steps_per * 32;

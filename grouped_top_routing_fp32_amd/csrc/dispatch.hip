@@ -12,6 +12,7 @@
 //   dispatch_scan_kernel     one workgroup: per-unit bases, counts, offsets and
 //                            the grouped-GEMM tile tables
 //   dispatch_scatter_kernel  one workgroup per unit: stable placement
+//   dispatch_small_kernel    all three in one workgroup for small batches
 #include "common.h"
 
 namespace beam {
@@ -66,7 +67,8 @@ __device__ void write_tiles(Tile* tiles, int first, int e, int off, int cnt, int
 }
 
 // One workgroup of 256 threads; thread e owns expert e.
-// unit_hist: in = per-unit counts, out = per-unit global base of each expert.
+// unit_hist: in = per-unit counts, out = per-unit base of each expert inside
+// the expert's segment (the scatter adds the segment offset).
 // tiles_a/tiles_b (optional): tile tables with at most mt_a / mt_b rows per tile.
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ unit_hist, int units, int E, int n,
                                                             int32_t* __restrict__ counts,
@@ -77,7 +79,18 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int u = 0; u < units; ++u) {
+    int u = 0;
+    for (; u + 16 <= units; u += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = unit_hist[(size_t)(u + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        unit_hist[(size_t)(u + i) * E + e] = run;
+        run += c[i];
+      }
+    }
+    for (; u < units; ++u) {
       const int c = unit_hist[(size_t)u * E + e];
       unit_hist[(size_t)u * E + e] = run;
       run += c;
@@ -89,7 +102,6 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
     counts[e] = cnt;
     offsets[e] = off;
     if (e == E - 1) offsets[E] = off + cnt;
-    for (int u = 0; u < units; ++u) unit_hist[(size_t)u * E + e] += off;
   }
   if (tiles_a) {
     const int nt = cnt > 0 ? (cnt + mt_a - 1) / mt_a : 0;
@@ -105,8 +117,34 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
   }
 }
 
+// Ranks 64 pairs at a time in ascending index order and places them: the
+// rank of a pair among equal ids of its round comes from ballots on the id's
+// bits; `base` (one LDS array per wave) holds each expert's next position and
+// is advanced by the last lane of each run of equal ids.
+__device__ __forceinline__ void place_round(const int32_t* __restrict__ ids, int idx, int n, int E, int* base,
+                                            int32_t* __restrict__ sorted_slots) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int v = -1;
+  if (idx < n) {
+    v = ids[idx];
+    if ((unsigned)v >= (unsigned)E) v = -1;
+  }
+  const bool ok = v >= 0;
+  unsigned long long match = __ballot(ok);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool b = ok && ((v >> bit) & 1);
+    const unsigned long long m = __ballot(b);
+    match &= b ? m : ~m;
+  }
+  if (ok) sorted_slots[base[v] + __popcll(match & below)] = idx;
+  if (ok && (match >> lane) == 1ull) base[v] += __popcll(match);
+}
+
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
                                                                const int32_t* __restrict__ unit_base,
+                                                               const int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_slots) {
   __shared__ int base[4][256];
   const int tid = threadIdx.x;
@@ -125,9 +163,9 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
     }
   }
   __syncthreads();
-  // per-wave bases: unit base + earlier waves of this unit
+  // per-wave bases: segment offset + unit base + earlier waves of this unit
   if (tid < E) {
-    int run = unit_base[(size_t)blockIdx.x * E + tid];
+    int run = offsets[tid] + unit_base[(size_t)blockIdx.x * E + tid];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int c = base[w][tid];
@@ -136,31 +174,68 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
     }
   }
   __syncthreads();
-  // pass 2: stable placement, 64 pairs at a time in ascending index order
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int r = 0; r < kWavePairs; r += 64) {
-    const int idx = wbase + r + lane;
-    int v = -1;
-    if (idx < n) {
-      v = ids[idx];
-      if ((unsigned)v >= (unsigned)E) v = -1;
-    }
-    const bool ok = v >= 0;
-    unsigned long long match = __ballot(ok);
+  // pass 2: stable placement
+  for (int r = 0; r < kWavePairs; r += 64) place_round(ids, wbase + r + lane, n, E, base[wave], sorted_slots);
+}
+
+// The three steps in one workgroup, for small batches (n <= kSmallPairs):
+// wave w owns the contiguous range [w*q, (w+1)*q) of pairs, q a multiple of 64.
+constexpr int kSmallPairs = 4096;
+
+__global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_slots,
+                                                             Tile* __restrict__ tiles_a, int mt_a,
+                                                             Tile* __restrict__ tiles_b, int mt_b,
+                                                             int32_t* __restrict__ ntiles) {
+  __shared__ int base[4][256];
+  __shared__ int buf[256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int q = ((n + 255) / 256) * 64;
+  const int w0 = wave * q;
 #pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool b = ok && ((v >> bit) & 1);
-      const unsigned long long m = __ballot(b);
-      match &= b ? m : ~m;
+  for (int w = 0; w < 4; ++w) base[w][tid] = 0;
+  __syncthreads();
+  for (int r = 0; r < q; r += 64) {
+    const int idx = w0 + r + lane;
+    if (idx < n) {
+      const int v = ids[idx];
+      if ((unsigned)v < (unsigned)E) atomicAdd(&base[wave][v], 1);
     }
-    if (ok) {
-      const int rank = __popcll(match & below);
-      const int pos = base[wave][v] + rank;
-      sorted_slots[pos] = idx;
-    }
-    // the last lane of each run of equal ids advances that id's base
-    if (ok && (match >> lane) == 1ull) base[wave][v] += __popcll(match);
   }
+  __syncthreads();
+  const int e = tid;
+  const int cnt = e < E ? base[0][e] + base[1][e] + base[2][e] + base[3][e] : 0;
+  const int off = block_exclusive_scan(cnt, buf);
+  if (e < E) {
+    counts[e] = cnt;
+    offsets[e] = off;
+    if (e == E - 1) offsets[E] = off + cnt;
+    int run = off;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = base[w][e];
+      base[w][e] = run;
+      run += c;
+    }
+  }
+  if (tiles_a) {
+    const int nt = cnt > 0 ? (cnt + mt_a - 1) / mt_a : 0;
+    const int first = block_exclusive_scan(nt, buf);
+    if (e < E) write_tiles(tiles_a, first, e, off, cnt, mt_a);
+    if (e == 255) ntiles[0] = first + nt;
+  }
+  if (tiles_b) {
+    const int nt = cnt > 0 ? (cnt + mt_b - 1) / mt_b : 0;
+    const int first = block_exclusive_scan(nt, buf);
+    if (e < E) write_tiles(tiles_b, first, e, off, cnt, mt_b);
+    if (e == 255) ntiles[1] = first + nt;
+  }
+  __syncthreads();
+  for (int r = 0; r < q; r += 64) place_round(ids, w0 + r + lane, n, E, base[wave], sorted_slots);
 }
 
 // ---------------------------------------------------------------------------
@@ -171,6 +246,11 @@ int dispatch_units(int n) { return (n + kUnit - 1) / kUnit; }
 hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_slots, Tile* tiles_a, int mt_a, Tile* tiles_b, int mt_b, int32_t* ntiles,
                            hipStream_t st) {
+  if (n <= kSmallPairs) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(256), 0, st, ids, n, E, counts, offsets, sorted_slots,
+                       tiles_a, mt_a, tiles_b, mt_b, ntiles);
+    return hipGetLastError();
+  }
   const int units = dispatch_units(n);
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(units), dim3(256), 0, st, ids, n, E, unit_hist);
   hipError_t err = hipGetLastError();
@@ -179,7 +259,8 @@ hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist,
                      tiles_a, mt_a, tiles_b, mt_b, ntiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(units), dim3(256), 0, st, ids, n, E, unit_hist, sorted_slots);
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(units), dim3(256), 0, st, ids, n, E, unit_hist, offsets,
+                     sorted_slots);
   return hipGetLastError();
 }
 

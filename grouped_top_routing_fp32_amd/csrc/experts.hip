@@ -475,24 +475,31 @@ hipError_t launch_down_tiled(const uint16_t* h, const uint8_t* hscale, const int
 // ---------------------------------------------------------------------------
 // combine: out[t] = sum_k w[t,k] * y[t*K + k], k ascending, FP32
 // ---------------------------------------------------------------------------
+constexpr int kCombineCols = 1024;  // columns per workgroup (256 threads x 4)
+
+// grid: (T, ceil(H / 1024)); block 256.  The K rows of a token are loaded
+// together (up to 16), then summed in ascending k.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                       float* __restrict__ out, int H, int K) {
   const int t = blockIdx.x;
-  const float* yt = y + (size_t)t * K * H;
+  const int c = blockIdx.y * kCombineCols + threadIdx.x * 4;
+  if (c >= H) return;
+  const float* yt = y + (size_t)t * K * H + c;
   const float* wt = w + (size_t)t * K;
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const float wk = wt[k];
-      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yt + (size_t)k * H + c));
-      acc += wk * v;
-    }
-    *reinterpret_cast<f32x4*>(out + (size_t)t * H + c) = acc;
-  }
+  f32x4 v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < K) v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yt + (size_t)k * H));
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < K) acc += wt[k] * v[k];
+  *reinterpret_cast<f32x4*>(out + (size_t)t * H + c) = acc;
 }
 
 hipError_t launch_combine(const float* y, const float* w, float* out, int T, int H, int K, hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, st, y, w, out, H, K);
+  hipLaunchKernelGGL(combine_kernel, dim3(T, (H + kCombineCols - 1) / kCombineCols), dim3(256), 0, st, y, w, out, H,
+                     K);
   return hipGetLastError();
 }
 

@@ -149,8 +149,20 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     v[j] = 0.f;
     if (active && e < E) {
       if (from_partials) {
-        float L = src[(size_t)t * E + e];
-        for (int s = 1; s < splits; ++s) L = L + src[((size_t)s * T + t) * E + e];
+        // split-K partial logits, added in ascending split order; loads are
+        // issued eight at a time so they overlap
+        const size_t plane = (size_t)T * E;
+        const float* ps = src + (size_t)t * E + e;
+        float L = 0.f;
+        int s = 0;
+        for (; s + 8 <= splits; s += 8) {
+          float q[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q[i] = ps[(size_t)(s + i) * plane];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) L = (s + i == 0) ? q[i] : L + q[i];
+        }
+        for (; s < splits; ++s) L = (s == 0) ? ps[0] : L + ps[(size_t)s * plane];
         if (bias) L = L + bias[e];
         v[j] = 1.0f / (1.0f + expf(-L));
         if (scores_out) scores_out[(size_t)t * E + e] = v[j];
