@@ -40,6 +40,10 @@ hipError_t launch_down_tiled(const uint16_t* h, const uint8_t* hscale, const int
                              const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
                              hipStream_t st);
 hipError_t launch_combine(const float* y, const float* w, float* out, int T, int H, int K, hipStream_t st);
+int grouped_gemm_rows();
+hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                                 int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
+                                 int H, int I, int K, hipStream_t st);
 }  // namespace beam
 
 namespace {
@@ -111,7 +115,7 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
     p->mt_a = p->mt_b = kWholeExpert;
     p->max_tiles_a = p->max_tiles_b = p->E < p->n ? p->E : p->n;
   } else {
-    p->mt_a = beam::tiled_gateup_rows();
+    p->mt_a = beam::grouped_gemm_rows();
     p->mt_b = beam::tiled_down_rows();
     const int m = p->E < p->n ? p->E : p->n;
     p->max_tiles_a = p->n / p->mt_a + m;
@@ -303,8 +307,8 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
     BEAM_TRY(beam::launch_gateup_stream(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, hscale, p.H,
                                         p.I, p.K, st));
   else
-    BEAM_TRY(beam::launch_gateup_tiled(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, hscale, p.H,
-                                       p.I, p.K, st));
+    BEAM_TRY(beam::launch_gateup_grouped(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, hscale, p.H,
+                                         p.I, p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
   if (p.stream)
     BEAM_TRY(beam::launch_down_stream(h, hscale, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I,

@@ -38,7 +38,6 @@ constexpr int kMaxScaleBlocks = 512;  // I <= 32768
 // next step.
 constexpr int kStreamN = 64;     // output columns per workgroup
 constexpr int kStreamRows = 16;  // rows per pass
-constexpr int kScaleCols = 64;   // SwiGLU activation columns that share one scale
 
 // grid: (max_tiles, I / 64); block 256.  One tile = all rows of one expert.
 // Writes h (fp16 bits, scaled by 2^-s) and s per (row, 64-column block).
@@ -192,8 +191,8 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------
 // tiled kernels (many rows per expert)
 // ---------------------------------------------------------------------------
-constexpr int kBK = 64;
-constexpr int kLd = kBK + 8;  // LDS row stride in bf16 (144 bytes: conflict-free 16-byte fragment reads)
+constexpr int kTBK = 64;
+constexpr int kTLd = kTBK + 8;  // LDS row stride in bf16 (144 bytes: conflict-free 16-byte fragment reads)
 
 // Block tile: BM rows x NB B-rows, where the B tile is [gate BN ; up BN] for
 // the gate/up kernel (NB = 2 BN) and [down BN] for the down kernel (NB = BN).
@@ -208,11 +207,11 @@ struct TiledCfg {
   static constexpr int CB = WCOLS / 16;  // 16-col blocks per wave (per gate / up)
   static constexpr int NACC = GATEUP ? 2 * CB : CB;
   static constexpr int THREADS = 64 * WM * WN;
-  static constexpr int A_CHUNKS = BM * kBK / 8 / THREADS;  // 16-byte chunks per thread
-  static constexpr int B_CHUNKS = NB * kBK / 8 / THREADS;
+  static constexpr int A_CHUNKS = BM * kTBK / 8 / THREADS;  // 16-byte chunks per thread
+  static constexpr int B_CHUNKS = NB * kTBK / 8 / THREADS;
   static_assert(WM * WN == 8, "8 waves");
-  static_assert(A_CHUNKS * THREADS * 8 == BM * kBK, "A staging");
-  static_assert(B_CHUNKS * THREADS * 8 == NB * kBK, "B staging");
+  static_assert(A_CHUNKS * THREADS * 8 == BM * kTBK, "A staging");
+  static_assert(B_CHUNKS * THREADS * 8 == NB * kTBK, "B staging");
 };
 
 // XCD-aware block order: hardware places block b on XCD b % 8; give each XCD a
@@ -240,8 +239,8 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
                                                            int Kdim, int Ndim, int topk, int nblocks_n,
                                                            int total_blocks) {
   using C = TiledCfg<GATEUP, BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::NB * kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kTLd];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::NB * kTLd];
   __shared__ float smax[8];
 
   const int lin = xcd_remap(blockIdx.x, total_blocks);
@@ -270,7 +269,7 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
     } else {
       asrc[i] = act + (size_t)(tl.row_start + rr) * Kdim + kc * 8;
     }
-    aoff[i] = r * kLd + kc * 8;
+    aoff[i] = r * kTLd + kc * 8;
   }
   const uint16_t* bsrc[C::B_CHUNKS];
   int boff[C::B_CHUNKS];
@@ -286,7 +285,7 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
     } else {
       bsrc[i] = w0 + wexp + (size_t)(n0 + r) * Kdim + kc * 8;
     }
-    boff[i] = r * kLd + kc * 8;
+    boff[i] = r * kTLd + kc * 8;
   }
 
   f32x4 acc[C::RB][C::NACC];
@@ -296,7 +295,7 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
     for (int j = 0; j < C::NACC; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 ra[C::A_CHUNKS], rb[C::B_CHUNKS];
-  const int nk = Kdim / kBK;
+  const int nk = Kdim / kTBK;
   // down projection: scale exponents of this tile's activation blocks (one per 64-wide k-step)
   const uint8_t* tscale = GATEUP ? nullptr : hscale + (size_t)tl.row_start * (Kdim / kScaleCols);
   int snext = GATEUP ? 0 : tscale[0];
@@ -324,7 +323,7 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {
-      const int koff = (kt + 1) * kBK;
+      const int koff = (kt + 1) * kTBK;
 #pragma unroll
       for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = ldg16(asrc[i] + koff);
 #pragma unroll
@@ -334,15 +333,15 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
     const uint16_t* A = sA[cur];
     const uint16_t* B = sB[cur];
 #pragma unroll
-    for (int ks = 0; ks < kBK; ks += 32) {
+    for (int ks = 0; ks < kTBK; ks += 32) {
       u32x4 af[C::RB], bf[C::NACC];
 #pragma unroll
       for (int i = 0; i < C::RB; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(&A[(arow0 + 16 * i) * kLd + ks + kk]);
+        af[i] = *reinterpret_cast<const u32x4*>(&A[(arow0 + 16 * i) * kTLd + ks + kk]);
 #pragma unroll
       for (int j = 0; j < C::CB; ++j) {
-        bf[j] = *reinterpret_cast<const u32x4*>(&B[(brow0 + 16 * j) * kLd + ks + kk]);
-        if (GATEUP) bf[C::CB + j] = *reinterpret_cast<const u32x4*>(&B[(BN + brow0 + 16 * j) * kLd + ks + kk]);
+        bf[j] = *reinterpret_cast<const u32x4*>(&B[(brow0 + 16 * j) * kTLd + ks + kk]);
+        if (GATEUP) bf[C::CB + j] = *reinterpret_cast<const u32x4*>(&B[(BN + brow0 + 16 * j) * kTLd + ks + kk]);
       }
 #pragma unroll
       for (int i = 0; i < C::RB; ++i)
@@ -412,6 +411,242 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// tiled kernel, one wave per SIMD (many rows per expert)
+// ---------------------------------------------------------------------------
+// Block tile: 256 rows x 256 B-rows (gate/up: 128 gate + 128 up columns;
+// down: 256 columns), 4 waves as 2 x 2, each wave 128 rows x 128 B-rows =
+// 8 x 8 MFMA 16x16x32 tiles (256 accumulator registers).  K advances 32 per
+// stage; stages live in a ring of kGemmStages LDS slots.  Global loads of
+// stage t + kGemmStages - 1 are issued at step t into one of two register
+// buffers and written to LDS one step later, so a load has two steps of math
+// to arrive; the fragments of stage t + 1 are read from LDS while stage t's
+// MFMAs run.  LDS rows are 64 bytes (no padding) with the four 16-byte chunks
+// of row r permuted by f(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the
+// 16 rows read by one fragment load on distinct banks.
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;      // B-rows per block
+constexpr int kGemmStages = 4;
+constexpr int kGemmStageHalfs = kGemmBM * 32;  // bf16 elements of one operand per stage
+
+__device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// GATEUP: A = x rows gathered through the permutation, B = [W_gate rows n0..n0+127 ;
+//         W_up rows n0..n0+127], bf16 MFMA, out h fp16 (scaled) + hscale.
+// !GATEUP: A = h rows (fp16), B = W_down rows n0..n0+255 converted to fp16 (x 2^s of the
+//         stage's 64-column activation block) as they are written to LDS, fp16 MFMA,
+//         out y fp32 at row slot.
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void expert_gemm_kernel(const uint16_t* __restrict__ act,
+                                                            const int32_t* __restrict__ sorted_slots,
+                                                            const Tile* __restrict__ tiles,
+                                                            const int32_t* __restrict__ ntiles,
+                                                            const uint16_t* __restrict__ w0,
+                                                            const uint16_t* __restrict__ w1,
+                                                            void* __restrict__ out, uint8_t* __restrict__ hscale,
+                                                            int Kdim, int Ndim, int topk, int nblocks_n,
+                                                            int total_blocks) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kGemmStages][kGemmStageHalfs];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kGemmStages][kGemmStageHalfs];
+  __shared__ float smax[4];
+
+  const int lin = xcd_remap(blockIdx.x, total_blocks);
+  const int tile_id = lin / nblocks_n;
+  const int nblk = lin - tile_id * nblocks_n;
+  if (tile_id >= ntiles[0]) return;
+  const Tile tl = tiles[tile_id];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int BNc = GATEUP ? kGemmBN / 2 : kGemmBN;  // output columns per block
+  const int n0 = nblk * BNc;
+
+  // staging: thread owns chunk (tid & 3) of rows (tid >> 2) + 64 i, i = 0..3, for A and for B.
+  // Sources are 32-bit element offsets from per-block base pointers (each base spans < 2^31 elements).
+  const int sc = tid & 3;
+  uint32_t aoff[4], boff[4];
+  int soff[4];
+  const uint16_t* abase = act;
+  const uint16_t* gbase = w0 + (size_t)tl.expert * Ndim * Kdim;
+  const uint16_t* ubase = GATEUP ? w1 + (size_t)tl.expert * Ndim * Kdim : gbase;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 2) + 64 * i;
+    const int rr = min(r, tl.rows - 1);  // rows past the tile's end repeat its last row; never stored
+    if (GATEUP) {
+      aoff[i] = (uint32_t)(sorted_slots[tl.row_start + rr] / topk) * Kdim + sc * 8;
+      boff[i] = (uint32_t)(n0 + (r & 127)) * Kdim + sc * 8;  // rows 0..127 gate, 128..255 up (i >= 2)
+    } else {
+      aoff[i] = (uint32_t)(tl.row_start + rr) * Kdim + sc * 8;
+      boff[i] = (uint32_t)(n0 + r) * Kdim + sc * 8;
+    }
+    soff[i] = r * 32 + ((sc ^ gemm_swz(r)) << 3);
+  }
+  const uint8_t* tscale = GATEUP ? nullptr : hscale + (size_t)tl.row_start * (Kdim / kScaleCols);
+
+  u32x4 ra[2][4], rb[2][4];
+  auto gload = [&](int buf, int stage) {
+    const int k = stage * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[buf][i] = ldg16(abase + aoff[i] + k);
+      rb[buf][i] = ldg16((GATEUP && i >= 2 ? ubase : gbase) + boff[i] + k);
+    }
+  };
+  auto lstore = [&](int buf, int stage) {
+    const int slot = stage % kGemmStages;
+    int sexp = 0;
+    if (!GATEUP) sexp = tscale[(stage * 32) / kScaleCols];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(&sA[slot][soff[i]]) = ra[buf][i];
+      u32x4 v = rb[buf][i];
+      if (!GATEUP) v = sexp ? bf16x8_to_f16x8_scaled(v, sexp) : bf16x8_to_f16x8(v);
+      *reinterpret_cast<u32x4*>(&sB[slot][soff[i]]) = v;
+    }
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment addresses: row r = base + 16 i + (lane & 15); the chunk permutation of
+  // rows base + 16 i depends only on the parity of i (bases are multiples of 64 rows).
+  const int fc = lane >> 4;
+  const int ar = wm * 128 + (lane & 15);
+  const int br = (GATEUP ? wn * 64 : wn * 128) + (lane & 15);
+  const int aoffe = ar * 32 + ((fc ^ gemm_swz(ar)) << 3), aoffo = (ar + 16) * 32 + ((fc ^ gemm_swz(ar + 16)) << 3);
+  const int boffe = br * 32 + ((fc ^ gemm_swz(br)) << 3), boffo = (br + 16) * 32 + ((fc ^ gemm_swz(br + 16)) << 3);
+  auto afrag = [&](int stage, int i) {
+    return *reinterpret_cast<const u32x4*>(&sA[stage % kGemmStages][((i & 1) ? aoffo : aoffe) + (i >> 1) * 32 * 32]);
+  };
+  auto bfrag = [&](int stage, int j) {
+    // gate/up: j < 4 gate rows, j >= 4 the matching up rows (128 B-rows further)
+    const int jj = GATEUP ? (j & 3) : j;
+    const int extra = GATEUP && j >= 4 ? 128 * 32 : 0;
+    return *reinterpret_cast<const u32x4*>(&sB[stage % kGemmStages][((jj & 1) ? boffo : boffe) + (jj >> 1) * 32 * 32 +
+                                                                   extra]);
+  };
+  // One register set of fragments: A[i] is reloaded for the next stage right
+  // after its last use, B[j] during the last row block.
+  u32x4 fa[8], fb[8];
+  auto math = [&](int stage, bool next) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = GATEUP ? mfma16x16x32(fa[i], fb[j], acc[i][j]) : mfma16x16x32_f16(fa[i], fb[j], acc[i][j]);
+        if (i == 7 && next) fb[j] = bfrag(stage + 1, j);
+      }
+      if (next) fa[i] = afrag(stage + 1, i);
+    }
+  };
+
+  const int nk = Kdim / 32;  // >= kGemmStages (Kdim >= 128)
+  // prologue: stages 0 .. S-2 into LDS, stage S-1 in flight in register buffer 0
+#pragma unroll
+  for (int s = 0; s < kGemmStages - 1; ++s) {
+    gload(0, s);
+    lstore(0, s);
+  }
+  gload(0, kGemmStages - 1);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fa[i] = afrag(0, i);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) fb[j] = bfrag(0, j);
+  // step t: MFMAs on stage t while stage t+1's fragments are read; global loads of
+  // stage t+S go to register buffer (t+1)&1; register buffer t&1 (stage t+S-1,
+  // issued one step earlier) is written to LDS.
+  for (int t = 0; t < nk; t += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int st = t + u;
+      if (st < nk) {
+        if (st + kGemmStages < nk) gload(u ^ 1, st + kGemmStages);
+        math(st, st + 1 < nk);
+        if (st + kGemmStages - 1 < nk) lstore(u, st + kGemmStages - 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // epilogue: lane holds rows 4*(lane/16)+r and column lane%16 of each 16x16 block
+  if (GATEUP) {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = wm * 128 + 16 * i + (lane >> 4) * 4 + r < tl.rows;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = ok ? silu_f32(acc[i][j][r]) * acc[i][4 + j][r] : 0.f;
+          acc[i][j][r] = v;
+          mx = fmaxf(mx, fabsf(v));
+        }
+      }
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
+    __syncthreads();
+    const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
+    const int nsb = Ndim / kScaleCols;
+    for (int r = tid; r < tl.rows; r += 256)
+#pragma unroll
+      for (int b = 0; b < 128 / kScaleCols; ++b)
+        hscale[(size_t)(tl.row_start + r) * nsb + n0 / kScaleCols + b] = (uint8_t)sexp;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 128 + 16 * i + (lane >> 4) * 4 + r;
+        if (row < tl.rows) {
+          uint16_t* hrow = reinterpret_cast<uint16_t*>(out) + (size_t)(tl.row_start + row) * Ndim + n0 + wn * 64 +
+                           (lane & 15);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) hrow[16 * j] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[i][j][r], -sexp));
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 128 + 16 * i + (lane >> 4) * 4 + r;
+        if (row < tl.rows) {
+          const int slot = sorted_slots[tl.row_start + row];
+          float* yrow = reinterpret_cast<float*>(out) + (size_t)slot * Ndim + n0 + wn * 128 + (lane & 15);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) yrow[16 * j] = acc[i][j][r];
+        }
+      }
+  }
+}
+
+hipError_t launch_gateup_gemm(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                              int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
+                              int H, int I, int K, hipStream_t st) {
+  const int nbn = I / (kGemmBN / 2);
+  const int total = max_tiles * nbn;
+  hipLaunchKernelGGL(expert_gemm_kernel<true>, dim3(total), dim3(256), 0, st, x, slots, tiles, ntiles, wg, wu,
+                     (void*)h, hscale, H, I, K, nbn, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_gemm(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                            const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
+                            hipStream_t st) {
+  const int nbn = H / kGemmBN;
+  const int total = max_tiles * nbn;
+  hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(total), dim3(256), 0, st, h, slots, tiles, ntiles, wd, nullptr,
+                     (void*)y, const_cast<uint8_t*>(hscale), I, H, 0, nbn, total);
+  return hipGetLastError();
 }
 
 // Tile shapes of the tiled path.

@@ -1,0 +1,306 @@
+// Grouped expert GEMMs for batches with many rows per expert (prefill), gfx950.
+//
+// Beam launch post ("Welcome Beam: a 501B open model you can own, customize,
+// and scale"), section "Mixture of Experts": each of the 8 experts a token is
+// routed to is a SwiGLU MLP (hidden 5120, intermediate 2560); section
+// "Residual stream": the SwiGLU product is computed in FP32.  Per expert e and
+// routed row r (rows in expert-sorted order, tiles from the dispatch):
+//   h[r] = silu(W_gate[e] x[r]) * (W_up[e] x[r])   bf16 MFMA, FP32 SwiGLU
+//   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 out
+// h is stored as fp16 with a power-of-two scale 2^-s per (tile, 64 columns),
+// s chosen so the block's largest magnitude stays below 2^15.
+//
+// Block tile: 256 rows x 256 B-rows (gate/up: 128 gate + the same 128 up
+// columns; down: 256 output columns), K advancing 32 per stage.  8 waves (two
+// per SIMD) as 4 (rows) x 2 (columns); each wave owns 64 rows x 128 B-rows =
+// 4 x 8 tiles of v_mfma_f32_16x16x32 (128 accumulators).
+//
+// Memory: the operand tiles of one stage (32 KB) are copied global -> LDS by
+// the load unit (global_load_lds_dwordx4, no registers) into a ring of
+// kStages slots; stage t + kStages - 1 is requested at step t, so each copy has
+// kStages - 1 steps to arrive.  The copies are issued with inline assembly and
+// waited for explicitly (s_waitcnt vmcnt, then s_barrier for the other waves):
+// the compiler's own tracking of LDS copies adds a full drain at each loop head.
+// Copies that hit L2 sustain the MFMA rate; copies from HBM do not, so blocks
+// are ordered for L2 reuse: each XCD (block b runs on XCD b % 8) takes a
+// contiguous range, and inside it kTileGroup consecutive row tiles (mostly of
+// one expert, sharing weight columns) run with the same column block before
+// the column advances (neighbouring column blocks share the row tiles).
+// Down: the weight tile arrives as bf16 and is converted to fp16 in place
+// (exactly, times 2^s of the stage's activation block) one step before its
+// MFMAs, once per block rather than once per wave.
+// LDS rows are 64 bytes; the four 16-byte chunks of row r sit at position
+// chunk ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the 16 rows read by one
+// MFMA operand load fall on distinct banks.
+#include "common.h"
+
+namespace beam {
+
+namespace gg {
+
+constexpr int kBM = 256;        // rows per tile
+constexpr int kBN = 256;        // B-rows per tile
+constexpr int kBK = 32;         // K per stage
+constexpr int kStages = 4;      // LDS ring depth
+constexpr int kThreads = 512;
+constexpr int kTileGroup = 4;   // row tiles rastered together
+constexpr int kSlotHalfs = kBM * kBK;  // 8192 bf16 = 16 KB per operand
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Element offset of (row, 16-byte chunk c) inside a slot.
+__device__ __forceinline__ int slot_off(int r, int c) { return r * kBK + ((c ^ swz(r)) << 3); }
+
+// s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = (63 & 15) | (3 << 14) | (7 << 4);
+
+// One 16-byte-per-lane global -> LDS copy: lane i's 16 bytes from g land at
+// LDS byte lds_base + 16 * i (lds_base is wave-uniform).  M0 carries the LDS
+// base and is restored afterwards.  The instruction writes no register.
+__device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+__device__ __forceinline__ void raster(int b, int total, int nbn, int& tile, int& nb) {
+  const int full = total & ~7;
+  const int lin = b >= full ? b : (b & 7) * (full >> 3) + (b >> 3);
+  const int per_group = kTileGroup * nbn;
+  const int g = lin / per_group;
+  const int rem = lin - g * per_group;
+  nb = rem / kTileGroup;
+  tile = g * kTileGroup + (rem - nb * kTileGroup);
+}
+
+}  // namespace gg
+
+// GATEUP: act = x [T, H]; w0 = W_gate, w1 = W_up [E, I, H]; out = h fp16 [n, I]; hscale written.
+// !GATEUP: act = h fp16 [n, I]; w0 = W_down [E, H, I]; out = y fp32 [n, H] (row slot); hscale read.
+template <bool GATEUP>
+__global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_slots, const Tile* __restrict__ tiles,
+    const int32_t* __restrict__ ntiles, const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
+    void* __restrict__ out, uint8_t* __restrict__ hscale, int Kdim, int Ndim, int topk, int nbn, int total_blocks) {
+  using namespace gg;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kStages][kSlotHalfs];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kStages][kSlotHalfs];
+  __shared__ float smax[8];
+
+  int tile_id, nblk;
+  raster(blockIdx.x, total_blocks, nbn, tile_id, nblk);
+  if (tile_id >= ntiles[0]) return;
+  const Tile tl = tiles[tile_id];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;  // 64-row quarter
+  const int wn = wave & 1;   // column half
+  const int BNc = GATEUP ? kBN / 2 : kBN;
+  const int n0 = nblk * BNc;
+
+  // ---- copy assignments --------------------------------------------------
+  // Wave w fills rows [32w, 32w+32) of the A slot and of the B slot with two
+  // 16-row copies each; lane i of a copy lands at byte 16*i of its 1 KB, i.e.
+  // row +i/4, position i%4, and so fetches global chunk (i%4) ^ f(row).
+  const uint16_t* asrc[2];
+  const uint16_t* bsrc[2];
+  {
+    const int pos = lane & 3;
+    const uint16_t* wbase = (GATEUP && wave >= 4 ? w1 : w0) + (size_t)tl.expert * Ndim * Kdim;  // B rows 128..: up
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = 32 * wave + 16 * q + (lane >> 2);
+      const int c = pos ^ swz(r);
+      const int rr = min(r, tl.rows - 1);  // rows past the tile's end repeat its last row; never stored
+      const size_t arow = GATEUP ? (size_t)(sorted_slots[tl.row_start + rr] / topk) : (size_t)(tl.row_start + rr);
+      asrc[q] = act + arow * Kdim + c * 8;
+      bsrc[q] = wbase + (size_t)(n0 + (GATEUP ? (r & 127) : r)) * Kdim + c * 8;
+    }
+  }
+  auto issue = [&](int stage, int slot) {
+    const int k = stage * kBK;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lds_copy16(asrc[q] + k, lds_addr(&sA[slot][(32 * wave + 16 * q) * kBK]));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lds_copy16(bsrc[q] + k, lds_addr(&sB[slot][(32 * wave + 16 * q) * kBK]));
+  };
+  constexpr int vm_per_stage = 4;  // copies per wave per stage
+
+  // down: in-place bf16 -> fp16 conversion of a B slot (two 16-byte chunks per thread)
+  const uint8_t* tscale = GATEUP ? nullptr : hscale + (size_t)tl.row_start * (Kdim / kScaleCols);
+  auto convert = [&](int stage, int slot) {
+    const int sexp = tscale[(stage * kBK) / kScaleCols];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      u32x4* p = reinterpret_cast<u32x4*>(&sB[slot][(tid + kThreads * q) * 8]);
+      const u32x4 v = *p;
+      *p = sexp ? bf16x8_to_f16x8_scaled(v, sexp) : bf16x8_to_f16x8(v);
+    }
+  };
+
+  // ---- fragments and MFMAs -------------------------------------------------
+  // A fragment i: rows wm*64 + 16 i + lane%16, chunk lane/16; the chunk permutation of
+  // rows base + 16 i depends only on the parity of i (bases are multiples of 32).
+  const int fc = lane >> 4;
+  const int ar = wm * 64 + (lane & 15);
+  const int aoffe = slot_off(ar, fc), aoffo = slot_off(ar + 16, fc);
+  const int br = (GATEUP ? wn * 64 : wn * 128) + (lane & 15);
+  const int boffe = slot_off(br, fc), boffo = slot_off(br + 16, fc);
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto math = [&](int slot) {
+    const uint16_t* A = sA[slot];
+    const uint16_t* B = sB[slot];
+    u32x4 fa[4], fb[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&A[((i & 1) ? aoffo : aoffe) + (i >> 1) * 32 * kBK]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // gate/up: j < 4 gate rows, j >= 4 the matching up rows (128 B-rows further)
+      const int jj = GATEUP ? (j & 3) : j;
+      const int extra = (GATEUP && j >= 4) ? 128 * kBK : 0;
+      fb[j] = *reinterpret_cast<const u32x4*>(&B[((jj & 1) ? boffo : boffe) + (jj >> 1) * 32 * kBK + extra]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = GATEUP ? mfma16x16x32(fa[i], fb[j], acc[i][j]) : mfma16x16x32_f16(fa[i], fb[j], acc[i][j]);
+  };
+
+  // ---- main loop -----------------------------------------------------------
+  // Copies complete in order, so "at most n outstanding", n = copies issued after
+  // stage s's, means stage s has arrived for this wave; the barrier extends that to
+  // every wave.  Gate/up step t: wait for stage t, barrier (everyone is done with
+  // stage t-1's slot), request stage t+S-1 into it, MFMAs on stage t.  Down step t:
+  // wait for stage t+1 instead, barrier, request stage t+S-1, convert stage t+1 in
+  // place (the next barrier publishes it), MFMAs on stage t.
+  const int nk = Kdim / kBK;  // a multiple of 4 (Kdim % 128 == 0), so nk >= kStages
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue(s, s);
+  if (!GATEUP) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((kStages - 2) * vm_per_stage));  // stage 0 arrived
+    __builtin_amdgcn_s_barrier();
+    convert(0, 0);
+  }
+  for (int t = 0; t < nk; t += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      const int st = t + u;
+      const int need = GATEUP ? st : st + 1;                      // stage that must have arrived
+      const int later = min(kStages - 2, nk - 1 - st) - (need - st);  // stages requested after it
+      if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * vm_per_stage));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_per_stage));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      if (st + kStages - 1 < nk) issue(st + kStages - 1, (u + kStages - 1) % kStages);
+      if (!GATEUP && st + 1 < nk) convert(st + 1, (u + 1) % kStages);
+      math(u);
+    }
+  }
+
+  // ---- epilogue ----------------------------------------------------------
+  // lane holds rows 4*(lane/16)+r and column lane%16 of each 16x16 block
+  if (GATEUP) {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = wm * 64 + 16 * i + (lane >> 4) * 4 + r < tl.rows;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = ok ? silu_f32(acc[i][j][r]) * acc[i][4 + j][r] : 0.f;
+          acc[i][j][r] = v;
+          mx = fmaxf(mx, fabsf(v));
+        }
+      }
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
+    __syncthreads();
+    float bm = smax[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) bm = fmaxf(bm, smax[w]);
+    const int sexp = act_scale_exp(bm);
+    const int nsb = Ndim / kScaleCols;
+    for (int r = tid; r < tl.rows; r += kThreads)
+#pragma unroll
+      for (int b = 0; b < 128 / kScaleCols; ++b)
+        hscale[(size_t)(tl.row_start + r) * nsb + n0 / kScaleCols + b] = (uint8_t)sexp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 64 + 16 * i + (lane >> 4) * 4 + r;
+        if (row < tl.rows) {
+          uint16_t* hrow = reinterpret_cast<uint16_t*>(out) + (size_t)(tl.row_start + row) * Ndim + n0 + wn * 64 +
+                           (lane & 15);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) hrow[16 * j] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[i][j][r], -sexp));
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 64 + 16 * i + (lane >> 4) * 4 + r;
+        if (row < tl.rows) {
+          const int slot = sorted_slots[tl.row_start + row];
+          float* yrow = reinterpret_cast<float*>(out) + (size_t)slot * Ndim + n0 + wn * 128 + (lane & 15);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) yrow[16 * j] = acc[i][j][r];
+        }
+      }
+  }
+}
+
+int grouped_gemm_rows() { return gg::kBM; }
+
+static int gemm_blocks(int max_tiles, int nbn) {
+  const int groups = (max_tiles + gg::kTileGroup - 1) / gg::kTileGroup;
+  return groups * gg::kTileGroup * nbn;
+}
+
+hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                                 int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
+                                 int H, int I, int K, hipStream_t st) {
+  const int nbn = I / (gg::kBN / 2);
+  const int total = gemm_blocks(max_tiles, nbn);
+  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(total), dim3(gg::kThreads), 0, st, x, slots, tiles, ntiles, wg,
+                     wu, (void*)h, hscale, H, I, K, nbn, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
+                               hipStream_t st) {
+  const int nbn = H / gg::kBN;
+  const int total = gemm_blocks(max_tiles, nbn);
+  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(total), dim3(gg::kThreads), 0, st, h, slots, tiles, ntiles, wd,
+                     nullptr, (void*)y, const_cast<uint8_t*>(hscale), I, H, 0, nbn, total);
+  return hipGetLastError();
+}
+
+}  // namespace beam
