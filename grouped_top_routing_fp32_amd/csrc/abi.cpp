@@ -27,12 +27,13 @@ int tiled_down_rows();
 int tiled_gateup_cols();
 int tiled_down_cols();
 int scale_cols();
-hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
-                                uint8_t* hscale, int H, int I, int K, hipStream_t st);
-hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                              const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
-                              hipStream_t st);
+bool stream_lds_fits(int H, int I);
+hipError_t launch_gateup_stream(bool lds, const uint16_t* x, const int32_t* slots, const Tile* tiles,
+                                const int32_t* ntiles, int max_tiles, const uint16_t* wg, const uint16_t* wu,
+                                uint16_t* h, uint8_t* hscale, int H, int I, int K, hipStream_t st);
+hipError_t launch_down_stream(bool lds, const uint16_t* h, const uint8_t* hscale, const int32_t* slots,
+                              const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y,
+                              int H, int I, hipStream_t st);
 hipError_t launch_gateup_tiled(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
                                int H, int I, int K, hipStream_t st);
@@ -69,10 +70,13 @@ bool dims_ok(const beam_moe_dims* d) {
 }
 
 // Expert-path choice: the stream kernels serve batches with few rows per
-// expert (weights streamed once per 16 rows), the tiled kernels the rest.
-bool use_stream_path(const beam_moe_dims* d, int T) {
-  const double avg_rows = (double)T * d->topk / d->num_experts;
-  return avg_rows < 32.0;
+// expert (weights streamed once per pass of rows), the tiled kernels the rest.
+// Among the stream kernels, the variant with rows staged in LDS (passes of 8)
+// serves the smallest batches, where an expert rarely sees more than 8 rows.
+double avg_rows(const beam_moe_dims* d, int T) { return (double)T * d->topk / d->num_experts; }
+bool use_stream_path(const beam_moe_dims* d, int T) { return avg_rows(d, T) < 32.0; }
+bool use_lds_stream(const beam_moe_dims* d, int T) {
+  return avg_rows(d, T) <= 4.0 && beam::stream_lds_fits(d->hidden, d->intermediate);
 }
 
 struct Plan {
@@ -84,7 +88,7 @@ struct Plan {
   int units;
   size_t off_hist;
   // expert tiles
-  bool stream;
+  bool stream, lds_stream;
   int mt_a, mt_b, max_tiles_a, max_tiles_b;
   size_t off_tiles_a, off_tiles_b, off_ntiles;
   // activations
@@ -111,6 +115,7 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
   p->splits = (ksteps + steps_per - 1) / steps_per;
   p->units = beam::dispatch_units(p->n);
   p->stream = use_stream_path(d, T);
+  p->lds_stream = p->stream && use_lds_stream(d, T);
   if (p->stream) {
     p->mt_a = p->mt_b = kWholeExpert;
     p->max_tiles_a = p->max_tiles_b = p->E < p->n ? p->E : p->n;
@@ -304,15 +309,15 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
                                  sorted_slots, tiles_a, p.mt_a, tiles_b, p.mt_b, ntiles, st));
   BEAM_TRY(mark(ev, kStGateUp, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_gateup_stream(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, hscale, p.H,
-                                        p.I, p.K, st));
+    BEAM_TRY(beam::launch_gateup_stream(p.lds_stream, x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h,
+                                        hscale, p.H, p.I, p.K, st));
   else
     BEAM_TRY(beam::launch_gateup_grouped(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, hscale, p.H,
                                          p.I, p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_down_stream(h, hscale, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I,
-                                      st));
+    BEAM_TRY(beam::launch_down_stream(p.lds_stream, h, hscale, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd,
+                                      y, p.H, p.I, st));
   else
     BEAM_TRY(beam::launch_down_tiled(h, hscale, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I,
                                      st));

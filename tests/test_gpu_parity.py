@@ -200,6 +200,12 @@ MID = {
     # stream path with skewed bias: some experts get more than 16 rows (several row passes)
     "mid_stream_skew": (synth.Workload("mid_stream_skew", 60, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
                                        zipf_s=1.2), None),
+    # stream path, rows staged in LDS, I/32 not a multiple of 8 (four-step down stages)
+    "mid_stream_lds_i384": (synth.Workload("mid_stream_lds_i384", 40, synth.Dims(512, 384, 64, 8, 4, 4),
+                                           router_sigma=0.06), None),
+    # stream path with register operands (about 9 rows per expert) and skew: several 16-row passes
+    "mid_stream_reg_skew": (synth.Workload("mid_stream_reg_skew", 150, synth.Dims(512, 256, 64, 8, 4, 4),
+                                           router_sigma=0.06, zipf_s=1.2), None),
 }
 
 
