@@ -262,10 +262,13 @@ __global__ __launch_bounds__(512) void expert_tiled_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::NB * kTLd];
   __shared__ float smax[8];
 
-  const int lin = xcd_remap(blockIdx.x, total_blocks);
+  // The grid is sized for the most tiles a batch can have; the remap spans the
+  // blocks of the tiles this batch has, so every XCD gets an equal share.
+  const int real_blocks = min(total_blocks, ntiles[0] * nblocks_n);
+  if ((int)blockIdx.x >= real_blocks) return;
+  const int lin = xcd_remap(blockIdx.x, real_blocks);
   const int tile_id = lin / nblocks_n;
   const int nblk = lin - tile_id * nblocks_n;
-  if (tile_id >= ntiles[0]) return;
   const Tile tl = tiles[tile_id];
   const int n0 = nblk * BN;
   const int tid = threadIdx.x;
@@ -471,10 +474,13 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(const uint16_t* __r
   __shared__ __attribute__((aligned(16))) uint16_t sB[kGemmStages][kGemmStageHalfs];
   __shared__ float smax[4];
 
-  const int lin = xcd_remap(blockIdx.x, total_blocks);
+  // The grid is sized for the most tiles a batch can have; the remap spans the
+  // blocks of the tiles this batch has, so every XCD gets an equal share.
+  const int real_blocks = min(total_blocks, ntiles[0] * nblocks_n);
+  if ((int)blockIdx.x >= real_blocks) return;
+  const int lin = xcd_remap(blockIdx.x, real_blocks);
   const int tile_id = lin / nblocks_n;
   const int nblk = lin - tile_id * nblocks_n;
-  if (tile_id >= ntiles[0]) return;
   const Tile tl = tiles[tile_id];
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -32,6 +32,8 @@
 // LDS rows are 64 bytes; the four 16-byte chunks of row r sit at position
 // chunk ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the 16 rows read by one
 // MFMA operand load fall on distinct banks.
+#include <type_traits>
+
 #include "common.h"
 
 namespace beam {
@@ -98,14 +100,20 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sB[kStages][kSlotHalfs];
   __shared__ float smax[8];
 
+  // The grid is sized for the most tiles a batch can have; the raster spans the
+  // tiles this batch has, so every XCD gets an equal share and the surplus
+  // blocks (the highest indices) exit here.
+  const int nt = ntiles[0];
+  const int real_blocks = min(total_blocks, (nt + kTileGroup - 1) / kTileGroup * kTileGroup * nbn);
+  if ((int)blockIdx.x >= real_blocks) return;
   int tile_id, nblk;
-  raster(blockIdx.x, total_blocks, nbn, tile_id, nblk);
-  if (tile_id >= ntiles[0]) return;
+  raster(blockIdx.x, real_blocks, nbn, tile_id, nblk);
+  if (tile_id >= nt) return;
   const Tile tl = tiles[tile_id];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;  // 64-row quarter
+  const int wm = wave >> 1;  // row fragments 16*(4i + wm), i = 0..3
   const int wn = wave & 1;   // column half
   const int BNc = GATEUP ? kBN / 2 : kBN;
   const int n0 = nblk * BNc;
@@ -151,13 +159,15 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   };
 
   // ---- fragments and MFMAs -------------------------------------------------
-  // A fragment i: rows wm*64 + 16 i + lane%16, chunk lane/16; the chunk permutation of
-  // rows base + 16 i depends only on the parity of i (bases are multiples of 32).
+  // A fragment i: rows 64 i + 16 wm + lane%16, chunk lane/16 (the chunk permutation
+  // is the same for every i, as 64 i changes neither (r >> 1) & 3 nor (r >> 3) & 3).
+  // Interleaving the waves' fragments over the tile lets a short tile drop whole
+  // levels i on every wave alike: level i is computed only if 64 i + 16 wm < rows.
   const int fc = lane >> 4;
-  const int ar = wm * 64 + (lane & 15);
-  const int aoffe = slot_off(ar, fc), aoffo = slot_off(ar + 16, fc);
+  const int aoff = slot_off(wm * 16 + (lane & 15), fc);
   const int br = (GATEUP ? wn * 64 : wn * 128) + (lane & 15);
   const int boffe = slot_off(br, fc), boffo = slot_off(br + 16, fc);
+  const int nlev = min(4, (tl.rows - 16 * wm + 63) / 64);  // >= 0: levels with rows for this wave
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -165,12 +175,10 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto math = [&](int slot) {
+  auto math = [&](int slot, auto full) {
     const uint16_t* A = sA[slot];
     const uint16_t* B = sB[slot];
     u32x4 fa[4], fb[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4*>(&A[((i & 1) ? aoffo : aoffe) + (i >> 1) * 32 * kBK]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // gate/up: j < 4 gate rows, j >= 4 the matching up rows (128 B-rows further)
@@ -179,10 +187,14 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
       fb[j] = *reinterpret_cast<const u32x4*>(&B[((jj & 1) ? boffo : boffe) + (jj >> 1) * 32 * kBK + extra]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      if (decltype(full)::value || i < nlev) {
+        fa[i] = *reinterpret_cast<const u32x4*>(&A[aoff + i * 64 * kBK]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j] = GATEUP ? mfma16x16x32(fa[i], fb[j], acc[i][j]) : mfma16x16x32_f16(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = GATEUP ? mfma16x16x32(fa[i], fb[j], acc[i][j]) : mfma16x16x32_f16(fa[i], fb[j], acc[i][j]);
+      }
+    }
   };
 
   // ---- main loop -----------------------------------------------------------
@@ -200,25 +212,32 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     __builtin_amdgcn_s_barrier();
     convert(0, 0);
   }
-  for (int t = 0; t < nk; t += kStages) {
+  auto main_loop = [&](auto full) {
+    for (int t = 0; t < nk; t += kStages) {
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const int st = t + u;
-      const int need = GATEUP ? st : st + 1;                      // stage that must have arrived
-      const int later = min(kStages - 2, nk - 1 - st) - (need - st);  // stages requested after it
-      if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * vm_per_stage));
-      else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_per_stage));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_barrier();
-      if (st + kStages - 1 < nk) issue(st + kStages - 1, (u + kStages - 1) % kStages);
-      if (!GATEUP && st + 1 < nk) convert(st + 1, (u + 1) % kStages);
-      math(u);
+      for (int u = 0; u < kStages; ++u) {
+        const int st = t + u;
+        const int need = GATEUP ? st : st + 1;                          // stage that must have arrived
+        const int later = min(kStages - 2, nk - 1 - st) - (need - st);  // stages requested after it
+        if (later >= 2)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * vm_per_stage));
+        else if (later == 1)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_per_stage));
+        else
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        if (st + kStages - 1 < nk) issue(st + kStages - 1, (u + kStages - 1) % kStages);
+        if (!GATEUP && st + 1 < nk) convert(st + 1, (u + 1) % kStages);
+        math(u, full);
+      }
     }
-  }
+  };
+  // full tiles (the common case) run without the per-level tests
+  if (tl.rows >= kBM)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
 
   // ---- epilogue ----------------------------------------------------------
   // lane holds rows 4*(lane/16)+r and column lane%16 of each 16x16 block
@@ -228,7 +247,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = wm * 64 + 16 * i + (lane >> 4) * 4 + r < tl.rows;
+        const bool ok = 64 * i + 16 * wm + (lane >> 4) * 4 + r < tl.rows;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float v = ok ? silu_f32(acc[i][j][r]) * acc[i][4 + j][r] : 0.f;
@@ -252,7 +271,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wm * 64 + 16 * i + (lane >> 4) * 4 + r;
+        const int row = 64 * i + 16 * wm + (lane >> 4) * 4 + r;
         if (row < tl.rows) {
           uint16_t* hrow = reinterpret_cast<uint16_t*>(out) + (size_t)(tl.row_start + row) * Ndim + n0 + wn * 64 +
                            (lane & 15);
@@ -265,7 +284,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wm * 64 + 16 * i + (lane >> 4) * 4 + r;
+        const int row = 64 * i + 16 * wm + (lane >> 4) * 4 + r;
         if (row < tl.rows) {
           const int slot = sorted_slots[tl.row_start + row];
           float* yrow = reinterpret_cast<float*>(out) + (size_t)slot * Ndim + n0 + wn * 128 + (lane & 15);
