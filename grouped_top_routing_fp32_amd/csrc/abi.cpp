@@ -20,12 +20,7 @@ hipError_t launch_select(const float* src, int splits, bool from_partials, const
                          int T, int E, int G, int TG, int K, float scale, int32_t* ids, float* w, hipStream_t st);
 int dispatch_units(int n);
 hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist, int32_t* counts, int32_t* offsets,
-                           int32_t* sorted_slots, Tile* tiles_a, int mt_a, Tile* tiles_b, int mt_b, int32_t* ntiles,
-                           hipStream_t st);
-int tiled_gateup_rows();
-int tiled_down_rows();
-int tiled_gateup_cols();
-int tiled_down_cols();
+                           int32_t* sorted_slots, Tile* tiles, int mt, int32_t* ntiles, hipStream_t st);
 int scale_cols();
 bool stream_lds_fits(int H, int I);
 hipError_t launch_gateup_stream(bool lds, const uint16_t* x, const int32_t* slots, const Tile* tiles,
@@ -34,17 +29,14 @@ hipError_t launch_gateup_stream(bool lds, const uint16_t* x, const int32_t* slot
 hipError_t launch_down_stream(bool lds, const uint16_t* h, const uint8_t* hscale, const int32_t* slots,
                               const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y,
                               int H, int I, hipStream_t st);
-hipError_t launch_gateup_tiled(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                               int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
-                               int H, int I, int K, hipStream_t st);
-hipError_t launch_down_tiled(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                             const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
-                             hipStream_t st);
 hipError_t launch_combine(const float* y, const float* w, float* out, int T, int H, int K, hipStream_t st);
 int grouped_gemm_rows();
 hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
                                  int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
                                  int H, int I, int K, hipStream_t st);
+hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
+                               hipStream_t st);
 }  // namespace beam
 
 namespace {
@@ -70,7 +62,7 @@ bool dims_ok(const beam_moe_dims* d) {
 }
 
 // Expert-path choice: the stream kernels serve batches with few rows per
-// expert (weights streamed once per pass of rows), the tiled kernels the rest.
+// expert (weights streamed once per pass of rows), the grouped GEMMs the rest.
 // Among the stream kernels, the variant with rows staged in LDS (passes of 8)
 // serves the smallest batches, where an expert rarely sees more than 8 rows.
 double avg_rows(const beam_moe_dims* d, int T) { return (double)T * d->topk / d->num_experts; }
@@ -89,8 +81,11 @@ struct Plan {
   size_t off_hist;
   // expert tiles
   bool stream, lds_stream;
-  int mt_a, mt_b, max_tiles_a, max_tiles_b;
-  size_t off_tiles_a, off_tiles_b, off_ntiles;
+  // one tile table serves both projections: whole experts (stream path) or
+  // row tiles of the grouped GEMMs, whose down kernel reads the activation
+  // scales of the gate/up tile its rows belong to
+  int mt, max_tiles;
+  size_t off_tiles, off_ntiles;
   // activations
   size_t off_h, off_hscale, off_y;
   size_t total;
@@ -116,27 +111,23 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
   p->units = beam::dispatch_units(p->n);
   p->stream = use_stream_path(d, T);
   p->lds_stream = p->stream && use_lds_stream(d, T);
+  const int touched = p->E < p->n ? p->E : p->n;  // most experts with rows
   if (p->stream) {
-    p->mt_a = p->mt_b = kWholeExpert;
-    p->max_tiles_a = p->max_tiles_b = p->E < p->n ? p->E : p->n;
+    p->mt = kWholeExpert;
+    p->max_tiles = touched;
   } else {
-    p->mt_a = beam::grouped_gemm_rows();
-    p->mt_b = beam::tiled_down_rows();
-    const int m = p->E < p->n ? p->E : p->n;
-    p->max_tiles_a = p->n / p->mt_a + m;
-    p->max_tiles_b = p->n / p->mt_b + m;
+    p->mt = beam::grouped_gemm_rows();
+    p->max_tiles = p->n / p->mt + touched;
   }
   size_t off = 0;
   p->off_part = off;
   off = align_up(off + (size_t)p->splits * T * p->E * sizeof(float));
   p->off_hist = off;
   off = align_up(off + (size_t)p->units * p->E * sizeof(int32_t));
-  p->off_tiles_a = off;
-  off = align_up(off + (size_t)(p->max_tiles_a + 1) * kTileBytes);
-  p->off_tiles_b = off;
-  off = align_up(off + (size_t)(p->max_tiles_b + 1) * kTileBytes);
+  p->off_tiles = off;
+  off = align_up(off + (size_t)(p->max_tiles + 1) * kTileBytes);
   p->off_ntiles = off;
-  off = align_up(off + 2 * sizeof(int32_t));
+  off = align_up(off + sizeof(int32_t));
   p->off_h = off;
   off = align_up(off + (size_t)p->n * p->I * 2);
   p->off_hscale = off;
@@ -264,7 +255,7 @@ int beam_moe_dispatch(const beam_moe_dims* d, int32_t T, const int32_t* topk_ids
   make_plan(d, T, &p);
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
   return hip_status(beam::launch_dispatch(topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), expert_counts,
-                                          expert_offsets, sorted_slots, nullptr, 0, nullptr, 0, nullptr,
+                                          expert_offsets, sorted_slots, nullptr, 0, nullptr,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -287,8 +278,7 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   const uint16_t* wu = static_cast<const uint16_t*>(w_up);
   const uint16_t* wd = static_cast<const uint16_t*>(w_down);
   float* part = at<float>(ws, p.off_part);
-  beam::Tile* tiles_a = at<beam::Tile>(ws, p.off_tiles_a);
-  beam::Tile* tiles_b = at<beam::Tile>(ws, p.off_tiles_b);
+  beam::Tile* tiles = at<beam::Tile>(ws, p.off_tiles);
   int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
   uint16_t* h = at<uint16_t>(ws, p.off_h);
   uint8_t* hscale = at<uint8_t>(ws, p.off_hscale);
@@ -306,21 +296,20 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
                                d->topk, d->routed_scaling, topk_ids, topk_w, st));
   BEAM_TRY(mark(ev, kStDispatch, st));
   BEAM_TRY(beam::launch_dispatch(topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), expert_counts, expert_offsets,
-                                 sorted_slots, tiles_a, p.mt_a, tiles_b, p.mt_b, ntiles, st));
+                                 sorted_slots, tiles, p.mt, ntiles, st));
   BEAM_TRY(mark(ev, kStGateUp, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_gateup_stream(p.lds_stream, x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h,
-                                        hscale, p.H, p.I, p.K, st));
+    BEAM_TRY(beam::launch_gateup_stream(p.lds_stream, x, sorted_slots, tiles, ntiles, p.max_tiles, wg, wu, h, hscale,
+                                        p.H, p.I, p.K, st));
   else
-    BEAM_TRY(beam::launch_gateup_grouped(x, sorted_slots, tiles_a, ntiles, p.max_tiles_a, wg, wu, h, hscale, p.H,
-                                         p.I, p.K, st));
+    BEAM_TRY(beam::launch_gateup_grouped(x, sorted_slots, tiles, ntiles, p.max_tiles, wg, wu, h, hscale, p.H, p.I,
+                                         p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_down_stream(p.lds_stream, h, hscale, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd,
-                                      y, p.H, p.I, st));
+    BEAM_TRY(beam::launch_down_stream(p.lds_stream, h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y, p.H,
+                                      p.I, st));
   else
-    BEAM_TRY(beam::launch_down_tiled(h, hscale, sorted_slots, tiles_b, ntiles + 1, p.max_tiles_b, wd, y, p.H, p.I,
-                                     st));
+    BEAM_TRY(beam::launch_down_grouped(h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y, p.H, p.I, st));
   BEAM_TRY(mark(ev, kStCombine, st));
   BEAM_TRY(beam::launch_combine(y, topk_w, out, T, p.H, p.K, st));
   BEAM_TRY(mark(ev, kNumStages, st));

@@ -69,12 +69,11 @@ __device__ void write_tiles(Tile* tiles, int first, int e, int off, int cnt, int
 // One workgroup of 256 threads; thread e owns expert e.
 // unit_hist: in = per-unit counts, out = per-unit base of each expert inside
 // the expert's segment (the scatter adds the segment offset).
-// tiles_a/tiles_b (optional): tile tables with at most mt_a / mt_b rows per tile.
+// tiles (optional): tile table with at most mt rows per tile, count in ntiles[0].
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ unit_hist, int units, int E, int n,
                                                             int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets, Tile* __restrict__ tiles_a,
-                                                            int mt_a, Tile* __restrict__ tiles_b, int mt_b,
-                                                            int32_t* __restrict__ ntiles) {
+                                                            int32_t* __restrict__ offsets, Tile* __restrict__ tiles,
+                                                            int mt, int32_t* __restrict__ ntiles) {
   __shared__ int buf[256];
   const int e = threadIdx.x;
   int run = 0;
@@ -103,17 +102,11 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
     offsets[e] = off;
     if (e == E - 1) offsets[E] = off + cnt;
   }
-  if (tiles_a) {
-    const int nt = cnt > 0 ? (cnt + mt_a - 1) / mt_a : 0;
+  if (tiles) {
+    const int nt = cnt > 0 ? (cnt + mt - 1) / mt : 0;
     const int first = block_exclusive_scan(nt, buf);
-    if (e < E) write_tiles(tiles_a, first, e, off, cnt, mt_a);
+    if (e < E) write_tiles(tiles, first, e, off, cnt, mt);
     if (e == 255) ntiles[0] = first + nt;
-  }
-  if (tiles_b) {
-    const int nt = cnt > 0 ? (cnt + mt_b - 1) / mt_b : 0;
-    const int first = block_exclusive_scan(nt, buf);
-    if (e < E) write_tiles(tiles_b, first, e, off, cnt, mt_b);
-    if (e == 255) ntiles[1] = first + nt;
   }
 }
 
@@ -186,8 +179,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ sorted_slots,
-                                                             Tile* __restrict__ tiles_a, int mt_a,
-                                                             Tile* __restrict__ tiles_b, int mt_b,
+                                                             Tile* __restrict__ tiles, int mt,
                                                              int32_t* __restrict__ ntiles) {
   __shared__ int base[4][256];
   __shared__ int buf[256];
@@ -222,17 +214,11 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
       run += c;
     }
   }
-  if (tiles_a) {
-    const int nt = cnt > 0 ? (cnt + mt_a - 1) / mt_a : 0;
+  if (tiles) {
+    const int nt = cnt > 0 ? (cnt + mt - 1) / mt : 0;
     const int first = block_exclusive_scan(nt, buf);
-    if (e < E) write_tiles(tiles_a, first, e, off, cnt, mt_a);
+    if (e < E) write_tiles(tiles, first, e, off, cnt, mt);
     if (e == 255) ntiles[0] = first + nt;
-  }
-  if (tiles_b) {
-    const int nt = cnt > 0 ? (cnt + mt_b - 1) / mt_b : 0;
-    const int first = block_exclusive_scan(nt, buf);
-    if (e < E) write_tiles(tiles_b, first, e, off, cnt, mt_b);
-    if (e == 255) ntiles[1] = first + nt;
   }
   __syncthreads();
   for (int r = 0; r < q; r += 64) place_round(ids, w0 + r + lane, n, E, base[wave], sorted_slots);
@@ -244,11 +230,10 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
 int dispatch_units(int n) { return (n + kUnit - 1) / kUnit; }
 
 hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist, int32_t* counts, int32_t* offsets,
-                           int32_t* sorted_slots, Tile* tiles_a, int mt_a, Tile* tiles_b, int mt_b, int32_t* ntiles,
-                           hipStream_t st) {
+                           int32_t* sorted_slots, Tile* tiles, int mt, int32_t* ntiles, hipStream_t st) {
   if (n <= kSmallPairs) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(256), 0, st, ids, n, E, counts, offsets, sorted_slots,
-                       tiles_a, mt_a, tiles_b, mt_b, ntiles);
+                       tiles, mt, ntiles);
     return hipGetLastError();
   }
   const int units = dispatch_units(n);
@@ -256,7 +241,7 @@ hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, st, unit_hist, units, E, n, counts, offsets,
-                     tiles_a, mt_a, tiles_b, mt_b, ntiles);
+                     tiles, mt, ntiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(units), dim3(256), 0, st, ids, n, E, unit_hist, offsets,

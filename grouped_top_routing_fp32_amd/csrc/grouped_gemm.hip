@@ -11,27 +11,27 @@
 // s chosen so the block's largest magnitude stays below 2^15.
 //
 // Block tile: 256 rows x 256 B-rows (gate/up: 128 gate + the same 128 up
-// columns; down: 256 output columns), K advancing 32 per stage.  8 waves (two
-// per SIMD) as 4 (rows) x 2 (columns); each wave owns 64 rows x 128 B-rows =
-// 4 x 8 tiles of v_mfma_f32_16x16x32 (128 accumulators).
+// columns; down: 256 output columns), K advancing 64 per stage.  8 waves (two
+// per SIMD) as 4 (rows) x 2 (columns); each wave owns 4 x 8 tiles of
+// v_mfma_f32_16x16x32 (128 accumulators): row fragments 64 i + 16 wm, so a
+// short tile drops whole levels i on every wave alike.
 //
-// Memory: the operand tiles of one stage (32 KB) are copied global -> LDS by
-// the load unit (global_load_lds_dwordx4, no registers) into a ring of
-// kStages slots; stage t + kStages - 1 is requested at step t, so each copy has
-// kStages - 1 steps to arrive.  The copies are issued with inline assembly and
-// waited for explicitly (s_waitcnt vmcnt, then s_barrier for the other waves):
-// the compiler's own tracking of LDS copies adds a full drain at each loop head.
-// Copies that hit L2 sustain the MFMA rate; copies from HBM do not, so blocks
-// are ordered for L2 reuse: each XCD (block b runs on XCD b % 8) takes a
-// contiguous range, and inside it kTileGroup consecutive row tiles (mostly of
-// one expert, sharing weight columns) run with the same column block before
-// the column advances (neighbouring column blocks share the row tiles).
-// Down: the weight tile arrives as bf16 and is converted to fp16 in place
-// (exactly, times 2^s of the stage's activation block) one step before its
-// MFMAs, once per block rather than once per wave.
-// LDS rows are 64 bytes; the four 16-byte chunks of row r sit at position
-// chunk ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the 16 rows read by one
-// MFMA operand load fall on distinct banks.
+// Memory: a stage's operand tiles (2 x 32 KB) are copied global -> LDS by the
+// load unit (global_load_lds_dwordx4, no registers), each copy fetching 8 rows
+// x 128 contiguous bytes (one cache line per row: half-line requests measured
+// about 15% slower); two stages fit in LDS and stage t + 1 is requested at
+// the start of step t.  The copies are issued with inline assembly and waited
+// for explicitly (s_waitcnt vmcnt, then s_barrier for the other waves): the
+// compiler's own tracking of LDS copies adds a full drain at each loop head.
+// Down: the weight stage is loaded into registers, converted to fp16 (times
+// 2^s of the stage's 64-column activation block) and written to LDS by the
+// threads themselves, in the same layout the copies produce.
+// Blocks are ordered for L2 reuse: each XCD (block b runs on XCD b % 8) takes
+// a contiguous range, and inside it kTileGroup consecutive row tiles (sharing
+// an expert's weight columns) run with the same column block before the column
+// advances (neighbouring column blocks share the row tiles).
+// LDS rows are 128 bytes; chunk c of row r sits at position c ^ ((r >> 1) & 7),
+// so the 16 rows read by one MFMA operand load cover all 64 banks once.
 #include <type_traits>
 
 #include "common.h"
@@ -42,16 +42,13 @@ namespace gg {
 
 constexpr int kBM = 256;        // rows per tile
 constexpr int kBN = 256;        // B-rows per tile
-constexpr int kBK = 32;         // K per stage
-constexpr int kStages = 4;      // LDS ring depth
+constexpr int kBK = 64;         // K per stage
 constexpr int kThreads = 512;
-constexpr int kTileGroup = 4;   // row tiles rastered together
-constexpr int kSlotHalfs = kBM * kBK;  // 8192 bf16 = 16 KB per operand
+constexpr int kTileGroup = 8;   // row tiles rastered together
+constexpr int kSlotHalfs = kBM * kBK;  // 16384 elements = 32 KB per operand
+static_assert(kBK == kScaleCols, "down reads one activation scale per stage");
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// Element offset of (row, 16-byte chunk c) inside a slot.
-__device__ __forceinline__ int slot_off(int r, int c) { return r * kBK + ((c ^ swz(r)) << 3); }
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -96,8 +93,8 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     const int32_t* __restrict__ ntiles, const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
     void* __restrict__ out, uint8_t* __restrict__ hscale, int Kdim, int Ndim, int topk, int nbn, int total_blocks) {
   using namespace gg;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kStages][kSlotHalfs];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kStages][kSlotHalfs];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kSlotHalfs];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kSlotHalfs];
   __shared__ float smax[8];
 
   // The grid is sized for the most tiles a batch can have; the raster spans the
@@ -118,55 +115,62 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   const int BNc = GATEUP ? kBN / 2 : kBN;
   const int n0 = nblk * BNc;
 
-  // ---- copy assignments --------------------------------------------------
-  // Wave w fills rows [32w, 32w+32) of the A slot and of the B slot with two
-  // 16-row copies each; lane i of a copy lands at byte 16*i of its 1 KB, i.e.
-  // row +i/4, position i%4, and so fetches global chunk (i%4) ^ f(row).
-  const uint16_t* asrc[2];
-  const uint16_t* bsrc[2];
+  // ---- stage loads -----------------------------------------------------------
+  // Wave w fills rows [32w, 32w+32) of the A slot and of the B slot, 8 rows per
+  // 1 KB copy: lane i lands at byte 16 i, i.e. row + i/8, position i%8, and so
+  // fetches chunk (i%8) ^ swz(row).
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
   {
-    const int pos = lane & 3;
     const uint16_t* wbase = (GATEUP && wave >= 4 ? w1 : w0) + (size_t)tl.expert * Ndim * Kdim;  // B rows 128..: up
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = 32 * wave + 16 * q + (lane >> 2);
-      const int c = pos ^ swz(r);
+    for (int q = 0; q < 4; ++q) {
+      const int r = 32 * wave + 8 * q + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
       const int rr = min(r, tl.rows - 1);  // rows past the tile's end repeat its last row; never stored
       const size_t arow = GATEUP ? (size_t)(sorted_slots[tl.row_start + rr] / topk) : (size_t)(tl.row_start + rr);
       asrc[q] = act + arow * Kdim + c * 8;
       bsrc[q] = wbase + (size_t)(n0 + (GATEUP ? (r & 127) : r)) * Kdim + c * 8;
     }
   }
-  auto issue = [&](int stage, int slot) {
+  auto issue_a = [&](int stage, int slot) {
     const int k = stage * kBK;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) lds_copy16(asrc[q] + k, lds_addr(&sA[slot][(32 * wave + 16 * q) * kBK]));
-#pragma unroll
-    for (int q = 0; q < 2; ++q) lds_copy16(bsrc[q] + k, lds_addr(&sB[slot][(32 * wave + 16 * q) * kBK]));
+    for (int q = 0; q < 4; ++q) lds_copy16(asrc[q] + k, lds_addr(&sA[slot][(32 * wave + 8 * q) * kBK]));
   };
-  constexpr int vm_per_stage = 4;  // copies per wave per stage
-
-  // down: in-place bf16 -> fp16 conversion of a B slot (two 16-byte chunks per thread)
-  const uint8_t* tscale = GATEUP ? nullptr : hscale + (size_t)tl.row_start * (Kdim / kScaleCols);
-  auto convert = [&](int stage, int slot) {
-    const int sexp = tscale[(stage * kBK) / kScaleCols];
+  auto issue_b = [&](int stage, int slot) {
+    const int k = stage * kBK;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      u32x4* p = reinterpret_cast<u32x4*>(&sB[slot][(tid + kThreads * q) * 8]);
-      const u32x4 v = *p;
-      *p = sexp ? bf16x8_to_f16x8_scaled(v, sexp) : bf16x8_to_f16x8(v);
+    for (int q = 0; q < 4; ++q) lds_copy16(bsrc[q] + k, lds_addr(&sB[slot][(32 * wave + 8 * q) * kBK]));
+  };
+  // down: weight stage through registers
+  u32x4 breg[4];
+  const uint8_t* tscale = GATEUP ? nullptr : hscale + (size_t)tl.row_start * (Kdim / kScaleCols);
+  auto load_b = [&](int stage) {
+    const int k = stage * kBK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) breg[q] = ldg16(bsrc[q] + k);
+  };
+  auto store_b = [&](int stage, int slot) {
+    const int sexp = tscale[stage];  // kBK == kScaleCols: one activation block per stage
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = sexp ? bf16x8_to_f16x8_scaled(breg[q], sexp) : bf16x8_to_f16x8(breg[q]);
+      *reinterpret_cast<u32x4*>(&sB[slot][(32 * wave + 8 * q) * kBK + lane * 8]) = v;
     }
   };
 
   // ---- fragments and MFMAs -------------------------------------------------
-  // A fragment i: rows 64 i + 16 wm + lane%16, chunk lane/16 (the chunk permutation
-  // is the same for every i, as 64 i changes neither (r >> 1) & 3 nor (r >> 3) & 3).
-  // Interleaving the waves' fragments over the tile lets a short tile drop whole
-  // levels i on every wave alike: level i is computed only if 64 i + 16 wm < rows.
+  // Every fragment row is a multiple of 16 plus lane%16, so its chunk permutation
+  // is swz(lane%16) throughout.  Sub-step s of a stage reads chunks 4s + lane/16.
+  const int l16 = lane & 15;
+  const int sw = swz(l16);
   const int fc = lane >> 4;
-  const int aoff = slot_off(wm * 16 + (lane & 15), fc);
-  const int br = (GATEUP ? wn * 64 : wn * 128) + (lane & 15);
-  const int boffe = slot_off(br, fc), boffo = slot_off(br + 16, fc);
+  const int aoff0 = (wm * 16 + l16) * kBK + ((fc ^ sw) << 3);
+  const int aoff1 = (wm * 16 + l16) * kBK + (((4 + fc) ^ sw) << 3);
+  const int brow = (GATEUP ? wn * 64 : wn * 128) + l16;
+  const int boff0 = brow * kBK + ((fc ^ sw) << 3);
+  const int boff1 = brow * kBK + (((4 + fc) ^ sw) << 3);
   const int nlev = min(4, (tl.rows - 16 * wm + 63) / 64);  // >= 0: levels with rows for this wave
 
   f32x4 acc[4][8];
@@ -175,21 +179,23 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto math = [&](int slot, auto full) {
+  auto math = [&](int slot, int sub, auto full) {
     const uint16_t* A = sA[slot];
     const uint16_t* B = sB[slot];
+    const int ao = sub ? aoff1 : aoff0;
+    const int bo = sub ? boff1 : boff0;
     u32x4 fa[4], fb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // gate/up: j < 4 gate rows, j >= 4 the matching up rows (128 B-rows further)
       const int jj = GATEUP ? (j & 3) : j;
       const int extra = (GATEUP && j >= 4) ? 128 * kBK : 0;
-      fb[j] = *reinterpret_cast<const u32x4*>(&B[((jj & 1) ? boffo : boffe) + (jj >> 1) * 32 * kBK + extra]);
+      fb[j] = *reinterpret_cast<const u32x4*>(&B[bo + jj * 16 * kBK + extra]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (decltype(full)::value || i < nlev) {
-        fa[i] = *reinterpret_cast<const u32x4*>(&A[aoff + i * 64 * kBK]);
+        fa[i] = *reinterpret_cast<const u32x4*>(&A[ao + i * 64 * kBK]);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           acc[i][j] = GATEUP ? mfma16x16x32(fa[i], fb[j], acc[i][j]) : mfma16x16x32_f16(fa[i], fb[j], acc[i][j]);
@@ -198,39 +204,37 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   };
 
   // ---- main loop -----------------------------------------------------------
-  // Copies complete in order, so "at most n outstanding", n = copies issued after
-  // stage s's, means stage s has arrived for this wave; the barrier extends that to
-  // every wave.  Gate/up step t: wait for stage t, barrier (everyone is done with
-  // stage t-1's slot), request stage t+S-1 into it, MFMAs on stage t.  Down step t:
-  // wait for stage t+1 instead, barrier, request stage t+S-1, convert stage t+1 in
-  // place (the next barrier publishes it), MFMAs on stage t.
-  const int nk = Kdim / kBK;  // a multiple of 4 (Kdim % 128 == 0), so nk >= kStages
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue(s, s);
-  if (!GATEUP) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((kStages - 2) * vm_per_stage));  // stage 0 arrived
-    __builtin_amdgcn_s_barrier();
-    convert(0, 0);
+  // Stage t lives in slot t % 2.  Step t: wait for this wave's copies of stage t
+  // (nothing later is in flight), barrier (stage t complete for all waves, and
+  // everyone is done with the other slot), request stage t + 1 into the other
+  // slot, MFMAs on stage t.  Down loads stage t + 1's weights into registers
+  // before the MFMAs and writes them, converted, to the other slot after them;
+  // the next barrier publishes them.
+  const int nk = Kdim / kBK;  // Kdim % 128 == 0, so nk >= 2
+  issue_a(0, 0);
+  if (GATEUP) {
+    issue_b(0, 0);
+  } else {
+    load_b(0);
+    store_b(0, 0);
   }
   auto main_loop = [&](auto full) {
-    for (int t = 0; t < nk; t += kStages) {
-#pragma unroll
-      for (int u = 0; u < kStages; ++u) {
-        const int st = t + u;
-        const int need = GATEUP ? st : st + 1;                          // stage that must have arrived
-        const int later = min(kStages - 2, nk - 1 - st) - (need - st);  // stages requested after it
-        if (later >= 2)
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * vm_per_stage));
-        else if (later == 1)
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm(vm_per_stage));
+    for (int st = 0; st < nk; ++st) {
+      const int slot = st & 1;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      const bool more = st + 1 < nk;
+      if (more) {
+        issue_a(st + 1, slot ^ 1);
+        if (GATEUP)
+          issue_b(st + 1, slot ^ 1);
         else
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();
-        if (st + kStages - 1 < nk) issue(st + kStages - 1, (u + kStages - 1) % kStages);
-        if (!GATEUP && st + 1 < nk) convert(st + 1, (u + 1) % kStages);
-        math(u, full);
+          load_b(st + 1);
       }
+      math(slot, 0, full);
+      math(slot, 1, full);
+      if (!GATEUP && more) store_b(st + 1, slot ^ 1);
     }
   };
   // full tiles (the common case) run without the per-level tests
@@ -305,7 +309,7 @@ static int gemm_blocks(int max_tiles, int nbn) {
 hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
                                  int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
                                  int H, int I, int K, hipStream_t st) {
-  const int nbn = I / (gg::kBN / 2);
+  const int nbn = I / (gg::kBN / 2);  // I % 128 == 0
   const int total = gemm_blocks(max_tiles, nbn);
   hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(total), dim3(gg::kThreads), 0, st, x, slots, tiles, ntiles, wg,
                      wu, (void*)h, hscale, H, I, K, nbn, total);
@@ -315,7 +319,7 @@ hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const 
 hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
                                const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
                                hipStream_t st) {
-  const int nbn = H / gg::kBN;
+  const int nbn = H / gg::kBN;  // H % 256 == 0
   const int total = gemm_blocks(max_tiles, nbn);
   hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(total), dim3(gg::kThreads), 0, st, h, slots, tiles, ntiles, wd,
                      nullptr, (void*)y, const_cast<uint8_t*>(hscale), I, H, 0, nbn, total);
