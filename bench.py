@@ -14,6 +14,13 @@ roofline figure of the dominant kernel.
 Prints one JSON line.  Its headline is the decode batch (T=64, HBM-bound);
 the prefill batch (T=16384, MFMA-bound) is reported in the same line under
 "prefill" with its own roofline.
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+this script (FETCH_SIZE, then WRITE_SIZE) with --copy-calibration, which adds
+one plain elementwise copy of known size whose counter readings give the
+scale factors.  `python bench.py --summarize-pmc FETCH_DIR WRITE_DIR` turns
+the two runs into the traffic file under profiles/; the roofline reports it
+only while the expert kernel sources still hash to what was measured.
 """
 from __future__ import annotations
 
@@ -27,9 +34,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import hashlib
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 METRIC = "MoE-layer tokens/s (decode T=64, prefill T=16K); % HBM BW / bf16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_hbm_traffic_decode_prefill.txt")
+# sources whose change invalidates a traffic measurement of the expert kernels
+KERNEL_SOURCES = ["grouped_top_routing_fp32_amd/csrc/" + f
+                  for f in ("common.h", "experts.hip", "grouped_gemm.hip", "abi.cpp")]
+COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
+GATE_UP_KERNELS = {"decode": "gateup_stream", "prefill": "grouped_gemm_kernel<true>"}
 
 
 def parse():
@@ -40,7 +55,91 @@ def parse():
     ap.add_argument("--workloads", default="decode,prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic file from two rocprofv3 --pmc runs and exit")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter_csv(d, counter):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc csv run: [(kernel, value)]."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path) as f:
+            per = {}
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = r["Dispatch_Id"]
+                name, val = per.get(key, (r["Kernel_Name"], 0.0))
+                per[key] = (name, val + float(r["Counter_Value"]))
+            rows += [per[k] for k in sorted(per, key=int)]
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    fetch = read_counter_csv(fetch_dir, "FETCH_SIZE")
+    write = read_counter_csv(write_dir, "WRITE_SIZE")
+
+    def copy_kib(rows):
+        vals = [v for n, v in rows if "neg" in n.lower()]
+        if not vals:
+            raise SystemExit("no calibration copy kernel in the counter run (was --copy-calibration given?)")
+        return sum(vals) / len(vals)
+
+    f_scale = COPY_BYTES / 1024.0 / copy_kib(fetch)
+    w_scale = COPY_BYTES / 1024.0 / copy_kib(write)
+    lines = ["# HBM traffic per launch of the gate/up kernel, from rocprofv3 counters",
+             "# fetch:  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "# write:  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "# summary: python3 bench.py --summarize-pmc <FETCH_DIR> <WRITE_DIR>",
+             f"# calibration: elementwise copy (torch.neg) of {COPY_BYTES} bytes read and written;"
+             f" FETCH_SIZE reads {copy_kib(fetch):.0f} KiB (scale {f_scale:.4f}),"
+             f" WRITE_SIZE reads {copy_kib(write):.0f} KiB (scale {w_scale:.4f})",
+             f"# expert kernel sources sha256[:16] = {kernel_source_hash()}"]
+    for wl, pat in GATE_UP_KERNELS.items():
+        fv = [v for n, v in fetch if pat in n]
+        wv = [v for n, v in write if pat in n]
+        if not fv or not wv:
+            continue
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        traffic = (fk * f_scale + wk * w_scale) * 1024.0
+        lines.append(f"workload={wl} kernel={pat} dispatches={len(fv)} fetch_kib={fk:.0f} write_kib={wk:.0f} "
+                     f"traffic_bytes={traffic:.0f} source_sha={kernel_source_hash()}")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def measured_traffic(workload):
+    """Scaled HBM bytes per gate/up launch, if measured on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    sha = kernel_source_hash()
+    for ln in text.splitlines():
+        if ln.startswith("#") or not ln.strip():
+            continue
+        kv = dict(tok.split("=", 1) for tok in ln.split() if "=" in tok)
+        if kv.get("workload") == workload and kv.get("source_sha") == sha:
+            return int(kv["traffic_bytes"])
+    return None
 
 
 def time_workload(name, experts, steps, warmup):
@@ -105,15 +204,17 @@ def roofline(r, bound):
     b, f, layer_bytes, expert_flops = accounting(r)
     kernel = "gate_up"
     dur_s = r["stage_ms"][kernel] / 1e3
+    traffic = measured_traffic(r["wl"].name)
     if bound == "hbm":
         achieved = b[kernel] / dur_s / 1e9
         return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": b[kernel], "avg_launch_ms": round(r["stage_ms"][kernel], 4)}
     achieved = f[kernel] / dur_s / 1e12
     return {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "algorithmic_flops_per_launch": f[kernel], "avg_launch_ms": round(r["stage_ms"][kernel], 4)}
+            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "algorithmic_flops_per_launch": f[kernel], "algorithmic_bytes_per_launch": b[kernel],
+            "avg_launch_ms": round(r["stage_ms"][kernel], 4)}
 
 
 def layer_summary(r):
@@ -169,8 +270,23 @@ def cpu_baseline(r, target_s):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def copy_calibration():
+    """A plain elementwise copy of COPY_BYTES (read once, written once), outside any timed region."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Beam MoE block here runs on a single MI355X "
               "(no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
@@ -185,6 +301,8 @@ def main():
     print(f"[bench] generating Beam expert weights (20.1 GB bf16) on the device", file=sys.stderr, flush=True)
     experts = synth.make_experts(synth.WORKLOADS["decode"], "cuda")
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration()
     results = {}
     for name in names:
         print(f"[bench] timing {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)

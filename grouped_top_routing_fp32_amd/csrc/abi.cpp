@@ -42,7 +42,7 @@ hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const i
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kTileBytes = 16;          // sizeof(beam::Tile)
+constexpr int kTileBytes = 32;          // sizeof(beam::Tile)
 constexpr int kWholeExpert = 1 << 30;   // tile height meaning "all rows of the expert"
 constexpr int64_t kMaxPairs = 1 << 28;  // T * K limit
 

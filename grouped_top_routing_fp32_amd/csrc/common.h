@@ -87,13 +87,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// One tile of a grouped GEMM: rows [row_start, row_start + rows) of the
-// expert-sorted order, all belonging to `expert`.
+// One row tile of the grouped expert GEMMs (or one whole expert on the stream
+// path), written by the dispatch: rows [row_start, row_start + rows) of the
+// expert-sorted order, all belonging to `expert`.  An expert's consecutive
+// tiles are cut into groups of at most kTileGroupMax; each tile carries its
+// group's first index and size, which the GEMM block order uses to run a
+// group's tiles side by side (they share the expert's weight columns).
+constexpr int kTileGroupMax = 8;
 struct Tile {
   int32_t expert;
   int32_t row_start;
   int32_t rows;
-  int32_t pad;
+  int32_t group_first;
+  int32_t group_size;
+  int32_t pad[3];
 };
+static_assert(sizeof(Tile) == 32, "tile table entry");
 
 }  // namespace beam

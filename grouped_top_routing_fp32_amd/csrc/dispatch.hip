@@ -54,14 +54,19 @@ __device__ int block_exclusive_scan(int v, int* buf) {
   return incl - v;
 }
 
-// Writes the tiles of one expert: rows [off, off + cnt) cut into pieces of at most `mt` rows.
+// Writes the tiles of one expert: rows [off, off + cnt) cut into pieces of at
+// most `mt` rows, tile i at index first + i, in groups of kTileGroupMax tiles.
 __device__ void write_tiles(Tile* tiles, int first, int e, int off, int cnt, int mt) {
+  const int nt = (cnt + mt - 1) / mt;
   for (int i = 0, r = 0; r < cnt; ++i, r += mt) {
+    const int g0 = i / kTileGroupMax * kTileGroupMax;
     Tile tl;
     tl.expert = e;
     tl.row_start = off + r;
     tl.rows = min(mt, cnt - r);
-    tl.pad = 0;
+    tl.group_first = first + g0;
+    tl.group_size = min(kTileGroupMax, nt - g0);
+    tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
     tiles[first + i] = tl;
   }
 }

@@ -27,9 +27,9 @@
 // 2^s of the stage's 64-column activation block) and written to LDS by the
 // threads themselves, in the same layout the copies produce.
 // Blocks are ordered for L2 reuse: each XCD (block b runs on XCD b % 8) takes
-// a contiguous range, and inside it kTileGroup consecutive row tiles (sharing
-// an expert's weight columns) run with the same column block before the column
-// advances (neighbouring column blocks share the row tiles).
+// a contiguous range of a linear order in which an expert's row tiles sweep
+// the column blocks together, so blocks dispatched one after another share the
+// weight columns or the row tile.
 // LDS rows are 128 bytes; chunk c of row r sits at position c ^ ((r >> 1) & 7),
 // so the 16 rows read by one MFMA operand load cover all 64 banks once.
 #include <type_traits>
@@ -44,7 +44,6 @@ constexpr int kBM = 256;        // rows per tile
 constexpr int kBN = 256;        // B-rows per tile
 constexpr int kBK = 64;         // K per stage
 constexpr int kThreads = 512;
-constexpr int kTileGroup = 8;   // row tiles rastered together
 constexpr int kSlotHalfs = kBM * kBK;  // 16384 elements = 32 KB per operand
 static_assert(kBK == kScaleCols, "down reads one activation scale per stage");
 
@@ -73,14 +72,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
-__device__ __forceinline__ void raster(int b, int total, int nbn, int& tile, int& nb) {
+// XCD-aware order: block b runs on XCD b % 8; each XCD takes a contiguous
+// range of the linear block order.
+__device__ __forceinline__ int xcd_lin(int b, int total) {
   const int full = total & ~7;
-  const int lin = b >= full ? b : (b & 7) * (full >> 3) + (b >> 3);
-  const int per_group = kTileGroup * nbn;
-  const int g = lin / per_group;
-  const int rem = lin - g * per_group;
-  nb = rem / kTileGroup;
-  tile = g * kTileGroup + (rem - nb * kTileGroup);
+  return b >= full ? b : (b & 7) * (full >> 3) + (b >> 3);
 }
 
 }  // namespace gg
@@ -97,16 +93,21 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kSlotHalfs];
   __shared__ float smax[8];
 
-  // The grid is sized for the most tiles a batch can have; the raster spans the
+  // The grid is sized for the most tiles a batch can have; the order spans the
   // tiles this batch has, so every XCD gets an equal share and the surplus
-  // blocks (the highest indices) exit here.
-  const int nt = ntiles[0];
-  const int real_blocks = min(total_blocks, (nt + kTileGroup - 1) / kTileGroup * kTileGroup * nbn);
+  // blocks (the highest indices) exit here.  Linear order: tile group by tile
+  // group (an expert's tiles, at most kTileGroupMax), inside a group column
+  // block by column block, the group's tiles in snake order, so consecutive
+  // blocks share either the weight columns or (at each turn) the row tile.
+  const int real_blocks = min(total_blocks, ntiles[0] * nbn);
   if ((int)blockIdx.x >= real_blocks) return;
-  int tile_id, nblk;
-  raster(blockIdx.x, real_blocks, nbn, tile_id, nblk);
-  if (tile_id >= nt) return;
-  const Tile tl = tiles[tile_id];
+  const int lin = xcd_lin(blockIdx.x, real_blocks);
+  const Tile tg = tiles[lin / nbn];  // a tile of the block's group
+  const int r = lin - nbn * tg.group_first;
+  const int nblk = r / tg.group_size;
+  int j = r - nblk * tg.group_size;
+  if (nblk & 1) j = tg.group_size - 1 - j;
+  const Tile tl = tiles[tg.group_first + j];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -301,10 +302,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
 
 int grouped_gemm_rows() { return gg::kBM; }
 
-static int gemm_blocks(int max_tiles, int nbn) {
-  const int groups = (max_tiles + gg::kTileGroup - 1) / gg::kTileGroup;
-  return groups * gg::kTileGroup * nbn;
-}
+static int gemm_blocks(int max_tiles, int nbn) { return max_tiles * nbn; }
 
 hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
                                  int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
