@@ -40,9 +40,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 METRIC = "MoE-layer tokens/s (decode T=64, prefill T=16K); % HBM BW / bf16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_hbm_traffic_decode_prefill.txt")
-# sources whose change invalidates a traffic measurement of the expert kernels
+# sources whose code (comments aside) decides the expert kernels' memory traffic:
+# the kernels, the launch plan and the tile table the dispatch writes
 KERNEL_SOURCES = ["grouped_top_routing_fp32_amd/csrc/" + f
-                  for f in ("common.h", "experts.hip", "grouped_gemm.hip", "abi.cpp")]
+                  for f in ("common.h", "experts.hip", "grouped_gemm.hip", "dispatch.hip", "abi.cpp")]
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
 GATE_UP_KERNELS = {"decode": "gateup_stream", "prefill": "grouped_gemm_kernel<true>"}
 
@@ -59,14 +60,21 @@ def parse():
                     help="also run a plain 1 GiB elementwise copy (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic file from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
+                    help="write a per-workload kernel time table from a rocprofv3 --kernel-trace run and exit")
     return ap.parse_args()
 
 
 def kernel_source_hash():
+    """Hash of KERNEL_SOURCES with comments and whitespace removed."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -123,6 +131,62 @@ def summarize_pmc(fetch_dir, write_dir):
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_trace(trace_dir, out_md):
+    """Per-workload kernel durations of the library's kernels from a kernel-trace run of this script.
+
+    Forward calls are cut at each router_logits_kernel dispatch; a call is a prefill
+    call if it ran the grouped GEMM, a decode call if it ran a stream kernel."""
+    import csv
+    import glob
+    path = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))[0]
+    with open(path) as f:
+        rows = [r for r in csv.DictReader(f) if "beam::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    calls, cur = [], []
+    for r in rows:
+        if "router_logits_kernel" in r["Kernel_Name"] and cur:
+            calls.append(cur)
+            cur = []
+        cur.append(r)
+    if cur:
+        calls.append(cur)
+
+    def short(name):
+        name = name.replace("void ", "")
+        return name[:name.index("(")] if "(" in name else name
+
+    per = {}
+    for c in calls:
+        wl = "prefill" if any("grouped_gemm" in r["Kernel_Name"] for r in c) else "decode"
+        for r in c:
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per.setdefault(wl, {}).setdefault(short(r["Kernel_Name"]), []).append(us)
+    out = ["# rocprofv3 kernel times: Beam MoE block forward, decode T=64 and prefill T=16384", "",
+           "Command (repository root on the GPU host):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp",
+           "rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- \\",
+           "    python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+           "python3 bench.py --summarize-trace <TRACE_DIR> <this file>", "```", "",
+           "Each forward call is cut at its router_logits_kernel dispatch; calls that ran the grouped GEMM are",
+           "prefill, the others decode.  Warmup and timed calls are both counted.  Durations are the",
+           "dispatch end minus start timestamps.", ""]
+    for wl in ("decode", "prefill"):
+        if wl not in per:
+            continue
+        ks = per[wl]
+        total = sum(sum(v) for v in ks.values()) / max(len(v) for v in ks.values())
+        out += [f"## {wl}", "", "| kernel | dispatches | average (us) | min (us) | max (us) | share |",
+                "|---|---|---|---|---|---|"]
+        for k, v in sorted(ks.items(), key=lambda kv: -sum(kv[1]) / len(kv[1])):
+            avg = sum(v) / len(v)
+            out.append(f"| `{k}` | {len(v)} | {avg:.1f} | {min(v):.1f} | {max(v):.1f} | "
+                       f"{100 * sum(v) / len(v) / total:.1f}% |")
+        out.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
 
 
 def measured_traffic(workload):
@@ -286,6 +350,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Beam MoE block here runs on a single MI355X "

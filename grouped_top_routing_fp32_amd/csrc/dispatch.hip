@@ -1,7 +1,7 @@
 // Counting-sort dispatch of the Beam MoE block (gfx950).
 //
-// Every token runs exactly K experts (Beam launch blog, "mixture of experts"
-// section), so the T*K (token, slot) pairs are grouped by expert for the
+// Every token runs exactly K experts (「Reflection 发布 Beam 501B 开源模型，支持 1M tokens 上下文」,
+// section 专家混合模型, mixture of experts), so the T*K (token, slot) pairs are grouped by expert for the
 // grouped expert GEMMs: a per-expert histogram, an exclusive scan and a
 // stable scatter.  The scatter ranks equal ids inside a wavefront with
 // ballots on the id's bits (a wave-level multisplit), never with atomics on

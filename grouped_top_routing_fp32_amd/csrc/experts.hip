@@ -1,10 +1,11 @@
 // Expert kernels of the Beam MoE block for batches with few rows per expert
 // (decode), and the weighted combine (gfx950, FP32 accumulation).
 //
-// Beam launch post ("Welcome Beam: a 501B open model you can own, customize,
-// and scale"), section "Mixture of Experts": each expert is a SwiGLU MLP with
-// intermediate size 2560 (hidden 5120); section "Residual stream": the SwiGLU
-// product is computed in FP32.  Per expert e and routed row r:
+// "Welcome Beam: a 501B open model you can own, customize, and scale", its
+// mixture-of-experts paragraph, and the Chinese translation of that post,
+// 「Reflection 发布 Beam 501B 开源模型，支持 1M tokens 上下文」, section 专家混合模型:
+// each expert is a SwiGLU MLP with intermediate size 2560 (hidden 5120);
+// section 残差流 (residual stream): the SwiGLU product is computed in FP32.  Per expert e and routed row r:
 //   h[r] = silu(W_gate[e] x[r]) * (W_up[e] x[r])   bf16 MFMA, SwiGLU in FP32
 //   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 out
 // h is handed to the down projection as fp16 (11 significant bits against

@@ -1,9 +1,11 @@
 // Grouped expert GEMMs for batches with many rows per expert (prefill), gfx950.
 //
-// Beam launch post ("Welcome Beam: a 501B open model you can own, customize,
-// and scale"), section "Mixture of Experts": each of the 8 experts a token is
-// routed to is a SwiGLU MLP (hidden 5120, intermediate 2560); section
-// "Residual stream": the SwiGLU product is computed in FP32.  Per expert e and
+// "Welcome Beam: a 501B open model you can own, customize, and scale", its
+// mixture-of-experts paragraph, and the Chinese translation of that post,
+// 「Reflection 发布 Beam 501B 开源模型，支持 1M tokens 上下文」, section 专家混合模型:
+// each of the 8 experts a token is routed to is a SwiGLU MLP (hidden 5120,
+// intermediate 2560); section 残差流 (residual stream): the SwiGLU product is
+// computed in FP32.  Per expert e and
 // routed row r (rows in expert-sorted order, tiles from the dispatch):
 //   h[r] = silu(W_gate[e] x[r]) * (W_up[e] x[r])   bf16 MFMA, FP32 SwiGLU
 //   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 out

@@ -1,10 +1,13 @@
 // Router and group-limited top-k selection of the Beam MoE block (gfx950).
 //
-// Beam launch blog, section "mixture of experts": every expert gets a sigmoid
-// score; experts form n_group groups; a group is ranked by the sum of its two
-// best scores; the topk_group best groups are kept; the top-k experts inside
-// them are chosen; their weights are normalised and multiplied by 2.5.  The
-// "residual stream" section puts the router in FP32.
+// 「Reflection 发布 Beam 501B 开源模型，支持 1M tokens 上下文」 (the Chinese
+// translation of the Hugging Face post "Welcome Beam: a 501B open model you
+// can own, customize, and scale"), section 专家混合模型 (mixture of experts):
+// every expert gets a sigmoid score; experts form n_group groups; a group is
+// ranked by the sum of its two best scores; the topk_group best groups are
+// kept; the top-k experts inside them are chosen; their weights are
+// normalised and multiplied by 2.5.  Section 残差流 (residual stream) puts
+// the router in FP32.
 //
 // Two kernels:
 //   router_logits_kernel  FP32-exact logits on bf16 MFMA.  x is bf16, W_r is

@@ -2,9 +2,12 @@
  * beam_moe.h -- forward pass of one Beam mixture-of-experts block on an
  * AMD Instinct MI355X (gfx950), as a plain C ABI.
  *
- * What the block computes (Beam launch blog, "Beam 501B", Hugging Face blog,
- * section "mixture of experts"; config.json fields n_group, topk_group,
- * norm_topk_prob, routed_scaling_factor as listed in the oferry.com analysis):
+ * What the block computes (「Reflection 发布 Beam 501B 开源模型，支持 1M tokens 上下文」,
+ * the Chinese translation of the Hugging Face post "Welcome Beam: a 501B open
+ * model you can own, customize, and scale", section 专家混合模型 (mixture of
+ * experts); config.json fields n_group, topk_group, norm_topk_prob,
+ * routed_scaling_factor as listed in 「Reflection 放出 501B 的 Beam 权重：四套
+ * 精度、滑动窗口和一场榜单落差」, section "config.json 里还有六处能直接抄的细节"):
  *
  *   1. router: s[t,e] = sigmoid(sum_h x[t,h] * W_r[e,h] + b[e]), in FP32;
  *   2. the E experts form G contiguous groups of E/G; a group's score is the
@@ -14,7 +17,7 @@
  *   3. w[t,k] = s[t,id_k] / sum_j s[t,id_j] * routed_scaling   (x2.5 for Beam);
  *   4. every selected expert is a SwiGLU MLP:
  *        y = W_down (silu(W_gate x) * (W_up x)), no biases;
- *      the SwiGLU product is FP32 (launch blog, "residual stream" section);
+ *      the SwiGLU product is FP32 (same translation, section 残差流);
  *   5. out[t] = sum_k w[t,k] * y[t,k].
  *
  * Conventions shared by every entry point
@@ -53,8 +56,8 @@ extern "C" {
 #endif
 
 typedef struct beam_moe_dims {
-  int32_t hidden;        /* H: 5120 for Beam (launch blog, attention section)      */
-  int32_t intermediate;  /* I: 2560 for Beam (launch blog, mixture of experts)     */
+  int32_t hidden;        /* H: 5120 for Beam (same translation, section 注意力)   */
+  int32_t intermediate;  /* I: 2560 for Beam (same translation, 专家混合模型)     */
   int32_t num_experts;   /* E: 256                                                 */
   int32_t num_groups;    /* G: 8  (config.json n_group)                            */
   int32_t topk_groups;   /* TG: 4 (config.json topk_group)                         */

@@ -4,13 +4,17 @@ TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
 links this module; only the tests, the smoke check and the benchmark's CPU
 baseline leg do.  It shares no code with the HIP path.
 
-Source of every step: the Beam launch blog ("Beam 501B", Hugging Face blog,
-in the Chinese translation on hot.xinyuan-ai.com, section "专家混合模型" /
-mixture of experts, and section "残差流" for the FP32 policy), the rewrite on
-tech.fxxz.com (section "混合专家系统"), the bilingual excerpt of the English
-original (MoE paragraph), and the config.json fields quoted on oferry.com
-(section "config.json 里还有六处能直接抄的细节": n_group 8, topk_group 4,
-norm_topk_prob true, routed_scaling_factor 2.5).  What those passages fix:
+Source of every step: the Hugging Face post on Beam in its Chinese
+translation, 「Reflection 发布 Beam 501B 开源模型，支持 1M tokens 上下文」 (section
+专家混合模型 / mixture of experts, and section 残差流 / residual stream for the
+FP32 policy); the bilingual excerpt of the English original, "Welcome Beam: a
+501B open model you can own, customize, and scale" (its mixture-of-experts
+paragraph); the tech.fxxz.com rewrite (section 混合专家系统); and the
+config.json fields quoted in 「Reflection 放出 501B 的 Beam 权重：四套精度、
+滑动窗口和一场榜单落差」 (section "config.json 里还有六处能直接抄的细节":
+n_group 8, topk_group 4, norm_topk_prob true, routed_scaling_factor 2.5).
+In the function notes below, "blog" means that Chinese translation.  What
+those passages fix:
 
 * router: a sigmoid score for every expert (blog, MoE section);
 * experts are split into n_group groups; a group is ranked by the sum of the
