@@ -87,6 +87,33 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = (63 & 15) | (3 << 14) | (7 << 4);
+
+// One 16-byte-per-lane global -> LDS copy by the load unit: lane i's 16 bytes
+// from g land at LDS byte lds_base + 16 * i (lds_base wave-uniform, carried in
+// M0, which is restored afterwards).  The instruction writes no register and
+// counts in vmcnt like a load; callers wait with s_waitcnt and publish with a
+// barrier.  Written as inline assembly: the compiler's builtin for it drains
+// every outstanding load at each loop head.
+__device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+
+// Wave-uniform LDS byte address of p.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
 // One row tile of the grouped expert GEMMs (or one whole expert on the stream
 // path), written by the dispatch: rows [row_start, row_start + rows) of the
 // expert-sorted order, all belonging to `expert`.  An expert's consecutive

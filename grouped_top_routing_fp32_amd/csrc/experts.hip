@@ -21,8 +21,8 @@
 // is needed, and weights go from memory straight into MFMA operand registers.
 //   *_stream_kernel      activation operands loaded from memory with the
 //                        weights; passes of 16 rows
-//   *_stream_lds_kernel  activation rows of a pass (up to 8) staged in LDS
-//                        first, so the K loop issues only weight loads
+//   *_stream_lds_kernel  weights and the pass's activation rows (up to 8)
+//                        copied into LDS in whole 256-byte row segments
 // Batches with many rows per expert use the grouped GEMMs (grouped_gemm.hip).
 #include "common.h"
 
@@ -189,38 +189,54 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
 int scale_cols() { return kScaleCols; }
 
 // ---------------------------------------------------------------------------
-// stream kernels with the activation rows staged in LDS (very few rows per expert)
+// stream kernels with every operand staged in LDS (very few rows per expert)
 // ---------------------------------------------------------------------------
-// Same work split as the register-operand kernels, but a pass takes at most 8 rows and copies them, whole-K, into
-// LDS once; the K loop then issues only weight loads to memory and reads its
-// activation operands from LDS.  Rows are padded by 8 elements so the 8 rows
-// of one operand read fall on distinct banks.  Rows 8..15 of each MFMA operand
-// are zero.  The pass size (8) is shared with the matching down kernel, which
-// relies on it for the activation scales.
-constexpr int kLdsRows = 8;
+// Same work split as the register-operand kernels (one expert per workgroup,
+// 64 output columns, each wave 16 columns over the whole K), but weights and
+// the pass's activation rows (at most kLdsRows) reach the MFMAs through LDS.
+// Per stage of kSk = 128 of K, the load unit copies the workgroup's weight rows
+// and the activation rows into a ring slot (global_load_lds), each copy taking
+// 4 rows x 256 contiguous bytes: register operand loads touch 16 rows x 64
+// bytes each, which caps the stream near 6.0 TB/s, while whole 256-byte row
+// segments stream at about 6.5 TB/s.  Inside a slot every row is 256 bytes and
+// its 16-byte chunk c sits at position c ^ (r & 15), so the 16 rows read by one
+// MFMA operand load fall on distinct banks.  A copy of row r fetches, for its
+// lane at position p, the chunk p ^ (r & 15).
+constexpr int kLdsRows = 8;  // activation rows per pass
+constexpr int kSk = 128;     // K per stage
+constexpr int kSSlots = 3;   // ring depth
 
-// Copies rows [0, nrows) of the pass into LDS (row stride K + 8 elements);
-// src_row(r) gives the global row start.  256 threads, four 16-byte chunks in flight each.
-template <typename RowFn>
-__device__ __forceinline__ void stage_rows(uint16_t* lds, int nrows, int Kdim, RowFn src_row) {
-  const int per_row = Kdim / 8;
-  const int total = nrows * per_row;
-  for (int c0 = threadIdx.x; c0 < total; c0 += 4 * 256) {
-    u32x4 v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = c0 + q * 256;
-      if (c < total) v[q] = ldg16(src_row(c / per_row) + (c % per_row) * 8);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = c0 + q * 256;
-      if (c < total) *reinterpret_cast<u32x4*>(&lds[(c / per_row) * (Kdim + 8) + (c % per_row) * 8]) = v[q];
-    }
-  }
+// Stage geometry for SK elements of K per stage: rows of SK * 2 bytes; one copy
+// (1 KB) covers RPI rows with LPR lanes per row.
+template <int SK>
+struct StageGeom {
+  static constexpr int kRowBytes = SK * 2;
+  static constexpr int kRPI = 1024 / kRowBytes;
+  static constexpr int kLPR = 64 / kRPI;
+  static_assert(kRPI >= 1 && kRPI * kRowBytes == 1024, "a copy covers whole rows");
+  // the swizzle XORs a chunk index with (row & 15): rows need at least 16 chunks
+  // of 16 bytes so that every swizzled chunk stays inside its row's segment
+  static_assert(kRowBytes >= 256, "stage rows of at least 16 chunks");
+};
+
+// Source of lane `lane` for a copy whose lanes cover row r at positions
+// lane % LPR: the chunk (lane % LPR) ^ (r & 15) of the row starting at row_ptr.
+template <int SK>
+__device__ __forceinline__ const uint16_t* stage_src(const uint16_t* row_ptr, int r, int lane) {
+  const int pos = lane % StageGeom<SK>::kLPR;
+  return row_ptr + ((pos ^ (r & 15)) << 3);
 }
 
-template <int U, int R>
+// Byte offset of (row, chunk) in a slot.
+template <int SK>
+__device__ __forceinline__ int stage_off(int row, int chunk) {
+  return row * StageGeom<SK>::kRowBytes + ((chunk ^ (row & 15)) << 4);
+}
+
+// grid: (max_tiles, I / 64); block 256; dynamic LDS kSSlots * 136 * 256 bytes.
+// Slot rows: 0..63 gate rows of the workgroup's columns, 64..127 the up rows,
+// 128..135 the activation rows of the pass.
+template <int SLOTS, int SK>
 __global__ __launch_bounds__(256) void gateup_stream_lds_kernel(const uint16_t* __restrict__ x,
                                                                 const int32_t* __restrict__ sorted_slots,
                                                                 const Tile* __restrict__ tiles,
@@ -229,51 +245,74 @@ __global__ __launch_bounds__(256) void gateup_stream_lds_kernel(const uint16_t* 
                                                                 const uint16_t* __restrict__ wu,
                                                                 uint16_t* __restrict__ h,
                                                                 uint8_t* __restrict__ hscale, int H, int I, int K) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t sx[];  // R x (H + 8)
+  using G = StageGeom<SK>;
+  constexpr int kRows = 128 + kLdsRows;
+  constexpr int kSlot = kRows * G::kRowBytes;
+  constexpr int kWCopies = 32 / G::kRPI;  // weight copies per wave per stage (32 rows)
+  constexpr int kCopies = kWCopies + 1;   // plus one copy (or part of one) of activation rows
+  extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   __shared__ float smax[4];
   if ((int)blockIdx.x >= ntiles[0]) return;
   const Tile tl = tiles[blockIdx.x];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = blockIdx.y * 64 + wave * 16 + (lane & 15);
-  const int kk = (lane >> 4) * 8;
-  const size_t ebase = (size_t)tl.expert * I * H;
-  const uint16_t* pg = wg + ebase + (size_t)col * H + kk;
-  const uint16_t* pu = wu + ebase + (size_t)col * H + kk;
-  const int nsb = I / kScaleCols;
-  const int steps = H / (32 * U);
   const int m = lane & 15;
+  const int col = blockIdx.y * 64 + wave * 16 + m;
+  const int nsb = I / kScaleCols;
+  const int nst = H / SK;
+  const size_t ebase = (size_t)tl.expert * I * H;
 
-  for (int p = 0; p < tl.rows; p += R) {
-    const int nrows = min(R, tl.rows - p);
-    const bool rv = m < nrows;
-    const uint16_t* pa = sx + (rv ? m : 0) * (H + 8) + kk;
+  // weight copies: wave w fills slot rows 32w .. 32w+31 (w < 2: gate, else up)
+  const uint16_t* wsrc[kWCopies];
+#pragma unroll
+  for (int q = 0; q < kWCopies; ++q) {
+    const int r = 32 * wave + G::kRPI * q + lane / G::kLPR;
+    const uint16_t* base = (r < 64 ? wg : wu) + ebase + (size_t)(blockIdx.y * 64 + (r & 63)) * H;
+    wsrc[q] = stage_src<SK>(base, r, lane);
+  }
+
+  for (int p = 0; p < tl.rows; p += kLdsRows) {
+    const int nrows = min(kLdsRows, tl.rows - p);
+    // activation copies: wave w fills activation rows 2w, 2w+1 (lanes 0 .. 2 LPR - 1)
+    const int xr = 2 * wave + min(1, lane / G::kLPR);
+    const int tok = sorted_slots[tl.row_start + p + min(xr, nrows - 1)] / K;
+    const uint16_t* xsrc = stage_src<SK>(x + (size_t)tok * H, 128 + xr, lane);
+    auto issue = [&](int st, int slot) {
+      unsigned char* sl = ring + slot * kSlot;
+      const int k = st * SK;
+#pragma unroll
+      for (int q = 0; q < kWCopies; ++q) lds_copy16(wsrc[q] + k, lds_addr(sl + (32 * wave + G::kRPI * q) * G::kRowBytes));
+      if (lane < 2 * G::kLPR) lds_copy16(xsrc + k, lds_addr(sl + (128 + 2 * wave) * G::kRowBytes));
+    };
     f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
-    u32x4 g0[U], u0[U], a[U], g1[U], u1[U];
-    auto load = [&](u32x4(&g)[U], u32x4(&uu)[U], int k) {
+    const bool rv = m < nrows;
+    const int arow = 128 + (rv ? m : 0);
+    const int grow = wave * 16 + m, urow = 64 + wave * 16 + m;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        g[u] = ldg16(pg + k + 32 * u);
-        uu[u] = ldg16(pu + k + 32 * u);
+    for (int s = 0; s < SLOTS - 1; ++s)
+      if (s < nst) issue(s, s);
+    for (int st = 0; st < nst; ++st) {
+      const int later = min(SLOTS - 2, nst - 1 - st);  // stages requested after stage st
+      if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();  // stage st complete for all waves; stage st - 1's slot is free
+      if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+      const unsigned char* sl = ring + (st % SLOTS) * kSlot;
+#pragma unroll
+      for (int s = 0; s < SK / 32; ++s) {
+        const int c = 4 * s + (lane >> 4);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(arow, c));
+        const u32x4 g = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(grow, c));
+        const u32x4 u = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(urow, c));
+        const u32x4 az = rv ? a : u32x4{0u, 0u, 0u, 0u};
+        ag = mfma16x16x32(az, g, ag);
+        au = mfma16x16x32(az, u, au);
       }
-    };
-    auto math = [&](u32x4(&g)[U], u32x4(&uu)[U], int k) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = rv ? *reinterpret_cast<const u32x4*>(pa + k + 32 * u) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        ag = mfma16x16x32(a[u], g[u], ag);
-        au = mfma16x16x32(a[u], uu[u], au);
-      }
-    };
-    load(g0, u0, 0);  // the first weights are on their way while the rows are staged
-    stage_rows(sx, nrows, H, [&](int r) { return x + (size_t)(sorted_slots[tl.row_start + p + r] / K) * H; });
-    __syncthreads();
-    for (int s = 0; s < steps; s += 2) {
-      if (s + 1 < steps) load(g1, u1, (s + 1) * 32 * U);
-      math(g0, u0, s * 32 * U);
-      if (s + 2 < steps) load(g0, u0, (s + 2) * 32 * U);
-      if (s + 1 < steps) math(g1, u1, (s + 1) * 32 * U);
     }
     // SwiGLU in FP32; one power-of-two scale per (pass, 64 columns)
     float v[4];
@@ -286,22 +325,25 @@ __global__ __launch_bounds__(256) void gateup_stream_lds_kernel(const uint16_t* 
     }
     mx = wave_max(mx);
     if (lane == 0) smax[wave] = mx;
-    __syncthreads();  // also: every wave is done reading sx before the next pass restages it
+    __syncthreads();  // also: every wave is done with the ring before the next pass refills it
     const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = (lane >> 4) * 4 + r;
       if (row < nrows) {
-        const size_t grow = (size_t)(tl.row_start + p + row);
-        h[grow * I + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(v[r], -sexp));
-        if (wave == 0 && (lane & 15) == 0) hscale[grow * nsb + blockIdx.y] = (uint8_t)sexp;
+        const size_t gr = (size_t)(tl.row_start + p + row);
+        h[gr * I + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(v[r], -sexp));
+        if (wave == 0 && m == 0) hscale[gr * nsb + blockIdx.y] = (uint8_t)sexp;
       }
     }
     __syncthreads();  // smax is rewritten by the next pass
   }
 }
 
-template <int U, int R>
+// grid: (max_tiles, H / 64); block 256; dynamic LDS SLOTS * 72 * 256 bytes + the
+// pass's scales.  Slot rows: 0..63 W_down rows of the workgroup's columns,
+// 64..71 the activation rows (h, fp16) of the pass.
+template <int SLOTS, int SK>
 __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __restrict__ h,
                                                               const uint8_t* __restrict__ hscale,
                                                               const int32_t* __restrict__ sorted_slots,
@@ -309,34 +351,47 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
                                                               const int32_t* __restrict__ ntiles,
                                                               const uint16_t* __restrict__ wd, float* __restrict__ y,
                                                               int H, int I) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t sh[];  // R x (I + 8), then the scales
+  using G = StageGeom<SK>;
+  constexpr int kRows = 64 + kLdsRows;
+  constexpr int kSlot = kRows * G::kRowBytes;
+  constexpr int kWCopies = 16 / G::kRPI;  // weight copies per wave per stage (16 rows)
+  constexpr int kCopies = kWCopies + 1;   // plus one copy (or part of one) of activation rows
+  extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   __shared__ int sany;
+  uint8_t* ssc = ring + SLOTS * kSlot;  // the pass's activation scales
   if ((int)blockIdx.x >= ntiles[0]) return;
   const Tile tl = tiles[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = blockIdx.y * 64 + wave * 16 + (lane & 15);
-  const int kk = (lane >> 4) * 8;
-  const uint16_t* pb = wd + (size_t)tl.expert * H * I + (size_t)col * I + kk;
-  const int nsb = I / kScaleCols;
-  const int steps = I / (32 * U);
   const int m = lane & 15;
-  uint8_t* ssc = reinterpret_cast<uint8_t*>(sh + R * (I + 8));
+  const int col = blockIdx.y * 64 + wave * 16 + m;
+  const int nsb = I / kScaleCols;
+  const int nst = I / SK;
 
-  for (int p = 0; p < tl.rows; p += R) {
-    const int nrows = min(R, tl.rows - p);
-    const bool rv = m < nrows;
-    const uint16_t* pa = sh + (rv ? m : 0) * (I + 8) + kk;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 b0[U], b1[U], a[U];
-    auto load = [&](u32x4(&b)[U], int k) {
+  const uint16_t* wsrc[kWCopies];
 #pragma unroll
-      for (int u = 0; u < U; ++u) b[u] = ldg16(pb + k + 32 * u);
+  for (int q = 0; q < kWCopies; ++q) {
+    const int r = 16 * wave + G::kRPI * q + lane / G::kLPR;
+    const uint16_t* base = wd + (size_t)tl.expert * H * I + (size_t)(blockIdx.y * 64 + r) * I;
+    wsrc[q] = stage_src<SK>(base, r, lane);
+  }
+
+  for (int p = 0; p < tl.rows; p += kLdsRows) {
+    const int nrows = min(kLdsRows, tl.rows - p);
+    const int xr = 2 * wave + min(1, lane / G::kLPR);
+    const uint16_t* xsrc = stage_src<SK>(h + (size_t)(tl.row_start + p + min(xr, nrows - 1)) * I, 64 + xr, lane);
+    auto issue = [&](int st, int slot) {
+      unsigned char* sl = ring + slot * kSlot;
+      const int k = st * SK;
+#pragma unroll
+      for (int q = 0; q < kWCopies; ++q) lds_copy16(wsrc[q] + k, lds_addr(sl + (16 * wave + G::kRPI * q) * G::kRowBytes));
+      if (lane < 2 * G::kLPR) lds_copy16(xsrc + k, lds_addr(sl + (64 + 2 * wave) * G::kRowBytes));
     };
-    load(b0, 0);
+#pragma unroll
+    for (int s = 0; s < SLOTS - 1; ++s)
+      if (s < nst) issue(s, s);
     if (tid == 0) sany = 0;
-    stage_rows(sh, nrows, I, [&](int r) { return h + (size_t)(tl.row_start + p + r) * I; });
     __syncthreads();
     for (int i = tid; i < nsb; i += 256) {
       const uint8_t sv = hscale[(size_t)(tl.row_start + p) * nsb + i];
@@ -345,27 +400,38 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
     }
     __syncthreads();
     const bool scaled = sany != 0;
-    auto math = [&](u32x4(&b)[U], int k) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool rv = m < nrows;
+    const int arow = 64 + (rv ? m : 0);
+    const int brow = wave * 16 + m;
+    for (int st = 0; st < nst; ++st) {
+      const int later = min(SLOTS - 2, nst - 1 - st);
+      if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+      const unsigned char* sl = ring + (st % SLOTS) * kSlot;
 #pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = rv ? *reinterpret_cast<const u32x4*>(pa + k + 32 * u) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const u32x4 bh = scaled ? bf16x8_to_f16x8_scaled(b[u], ssc[(k + 32 * u) / kScaleCols]) : bf16x8_to_f16x8(b[u]);
-        acc = mfma16x16x32_f16(a[u], bh, acc);
+      for (int s = 0; s < SK / 32; ++s) {
+        const int c = 4 * s + (lane >> 4);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(arow, c));
+        const u32x4 b = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(brow, c));
+        const int kb = (st * SK + 32 * s) / kScaleCols;
+        const u32x4 bh = scaled ? bf16x8_to_f16x8_scaled(b, ssc[kb]) : bf16x8_to_f16x8(b);
+        acc = mfma16x16x32_f16(rv ? a : u32x4{0u, 0u, 0u, 0u}, bh, acc);
       }
-    };
-    for (int s = 0; s < steps; s += 2) {
-      if (s + 1 < steps) load(b1, (s + 1) * 32 * U);
-      math(b0, s * 32 * U);
-      if (s + 2 < steps) load(b0, (s + 2) * 32 * U);
-      if (s + 1 < steps) math(b1, (s + 1) * 32 * U);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = (lane >> 4) * 4 + r;
       if (row < nrows) y[(size_t)sorted_slots[tl.row_start + p + row] * H + col] = acc[r];
     }
-    __syncthreads();  // every wave is done with sh and ssc before the next pass restages them
+    __syncthreads();  // every wave is done with the ring and the scales before the next pass
   }
 }
 
@@ -375,29 +441,34 @@ constexpr int kStreamU = 8;
 // LDS of one gfx950 compute unit, the most one workgroup can take.
 constexpr size_t kLdsBytesPerCU = 160 * 1024;
 
-size_t gateup_stream_lds_bytes(int H) { return (size_t)kLdsRows * (H + 8) * 2; }
-size_t down_stream_lds_bytes(int I) { return (size_t)kLdsRows * (I + 8) * 2 + I / kScaleCols; }
-
-// Whether the LDS-staged stream kernels can run at this shape (their staged rows fit in LDS).
-bool stream_lds_fits(int H, int I) {
-  return gateup_stream_lds_bytes(H) <= kLdsBytesPerCU && down_stream_lds_bytes(I) <= kLdsBytesPerCU;
+size_t gateup_stream_lds_bytes() { return (size_t)kSSlots * (128 + kLdsRows) * StageGeom<kSk>::kRowBytes; }
+size_t down_stream_lds_bytes(int I) {
+  return (size_t)kSSlots * (64 + kLdsRows) * StageGeom<kSk>::kRowBytes + I / kScaleCols;
 }
 
-// Launchers of the stream path.  `lds` picks the variant with activation rows staged in
-// LDS (passes of 8 rows; requires stream_lds_fits); gate/up and down must use the same
-// variant, since the down kernel reads one activation scale per pass of gate/up.
+// Whether the LDS-staged stream kernels can run at this shape: K of both
+// projections in whole stages, and the down kernel's scales fit in LDS.
+bool stream_lds_fits(int H, int I) {
+  return H % kSk == 0 && I % kSk == 0 && gateup_stream_lds_bytes() <= kLdsBytesPerCU &&
+         down_stream_lds_bytes(I) <= kLdsBytesPerCU;
+}
+
+// Launchers of the stream path.  `lds` picks the LDS-staged kernels (passes of 8
+// rows; requires stream_lds_fits); gate/up and down must use the same variant,
+// since the down kernel reads one activation scale per pass of gate/up.
 hipError_t launch_gateup_stream(bool lds, const uint16_t* x, const int32_t* slots, const Tile* tiles,
                                 const int32_t* ntiles, int max_tiles, const uint16_t* wg, const uint16_t* wu,
                                 uint16_t* h, uint8_t* hscale, int H, int I, int K, hipStream_t st) {
-  // H % 256 == 0: the K loop (H / 256 steps of eight) divides; I % 64 == 0: the column grid divides
+  // H % 256 == 0: the K loop divides (H / 256 register stages of eight steps, or
+  // H / 128 LDS stages); I % 64 == 0: the column grid divides
   dim3 grid(max_tiles, I / 64);
   if (lds) {
-    const size_t bytes = gateup_stream_lds_bytes(H);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<kStreamU, kLdsRows>),
+    const size_t bytes = gateup_stream_lds_bytes();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<kSSlots, kSk>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gateup_stream_lds_kernel<kStreamU, kLdsRows>), grid, dim3(256), bytes, st, x, slots, tiles,
-                       ntiles, wg, wu, h, hscale, H, I, K);
+    hipLaunchKernelGGL((gateup_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, x, slots, tiles, ntiles, wg,
+                       wu, h, hscale, H, I, K);
   } else {
     hipLaunchKernelGGL(gateup_stream_kernel<kStreamU>, grid, dim3(256), 0, st, x, slots, tiles, ntiles, wg, wu, h,
                        hscale, H, I, K);
@@ -409,25 +480,20 @@ hipError_t launch_down_stream(bool lds, const uint16_t* h, const uint8_t* hscale
                               const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y,
                               int H, int I, hipStream_t st) {
   dim3 grid(max_tiles, H / 64);
-  // I % 128 == 0: I / 32 is a multiple of 4; eight-step stages need I % 256 == 0, else four
-  const bool u8 = (I / 32) % 8 == 0;
   if (lds) {
     const size_t bytes = down_stream_lds_bytes(I);
-    const void* fn = u8 ? reinterpret_cast<const void*>(&down_stream_lds_kernel<8, kLdsRows>)
-                        : reinterpret_cast<const void*>(&down_stream_lds_kernel<4, kLdsRows>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_stream_lds_kernel<kSSlots, kSk>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
-    if (u8)
-      hipLaunchKernelGGL((down_stream_lds_kernel<8, kLdsRows>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
-                         ntiles, wd, y, H, I);
-    else
-      hipLaunchKernelGGL((down_stream_lds_kernel<4, kLdsRows>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
-                         ntiles, wd, y, H, I);
-  } else if (u8) {
-    hipLaunchKernelGGL(down_stream_kernel<8>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y, H, I);
-  } else {
-    hipLaunchKernelGGL(down_stream_kernel<4>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y, H, I);
+    hipLaunchKernelGGL((down_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, h, hscale, slots, tiles, ntiles,
+                       wd, y, H, I);
+    return hipGetLastError();
   }
+  // I % 128 == 0: I / 32 is a multiple of 4; eight-step stages need I % 256 == 0, else four
+  if ((I / 32) % 8 == 0)
+    hipLaunchKernelGGL(down_stream_kernel<8>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y, H, I);
+  else
+    hipLaunchKernelGGL(down_stream_kernel<4>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y, H, I);
   return hipGetLastError();
 }
 

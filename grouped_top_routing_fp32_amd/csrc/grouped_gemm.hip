@@ -51,29 +51,6 @@ static_assert(kBK == kScaleCols, "down reads one activation scale per stage");
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLgkm0 = (63 & 15) | (3 << 14) | (7 << 4);
-
-// One 16-byte-per-lane global -> LDS copy: lane i's 16 bytes from g land at
-// LDS byte lds_base + 16 * i (lds_base is wave-uniform).  M0 carries the LDS
-// base and is restored afterwards.  The instruction writes no register.
-__device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds_base)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-
 // XCD-aware order: block b runs on XCD b % 8; each XCD takes a contiguous
 // range of the linear block order.
 __device__ __forceinline__ int xcd_lin(int b, int total) {
