@@ -27,16 +27,17 @@ hipError_t launch_gateup_stream(bool lds, const uint16_t* x, const int32_t* slot
                                 const int32_t* ntiles, int max_tiles, const uint16_t* wg, const uint16_t* wu,
                                 uint16_t* h, uint8_t* hscale, int H, int I, int K, hipStream_t st);
 hipError_t launch_down_stream(bool lds, const uint16_t* h, const uint8_t* hscale, const int32_t* slots,
-                              const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y,
-                              int H, int I, hipStream_t st);
-hipError_t launch_combine(const float* y, const float* w, float* out, int T, int H, int K, hipStream_t st);
+                              const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd,
+                              uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st);
+hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
+                          hipStream_t st);
 int grouped_gemm_rows();
 hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
                                  int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
                                  int H, int I, int K, hipStream_t st);
 hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
-                               hipStream_t st);
+                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16,
+                               uint8_t* yscale, int H, int I, hipStream_t st);
 }  // namespace beam
 
 namespace {
@@ -87,7 +88,7 @@ struct Plan {
   int mt, max_tiles;
   size_t off_tiles, off_ntiles;
   // activations
-  size_t off_h, off_hscale, off_y;
+  size_t off_h, off_hscale, off_y, off_yscale;
   size_t total;
 };
 
@@ -133,7 +134,9 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
   p->off_hscale = off;
   off = align_up(off + (size_t)p->n * (p->I / beam::scale_cols()));
   p->off_y = off;
-  off = align_up(off + (size_t)p->n * p->H * sizeof(float));
+  off = align_up(off + (size_t)p->n * p->H * 2);
+  p->off_yscale = off;
+  off = align_up(off + (size_t)p->n * (p->H / beam::scale_cols()));
   p->total = off;
 }
 
@@ -282,7 +285,8 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
   uint16_t* h = at<uint16_t>(ws, p.off_h);
   uint8_t* hscale = at<uint8_t>(ws, p.off_hscale);
-  float* y = at<float>(ws, p.off_y);
+  uint16_t* y16 = at<uint16_t>(ws, p.off_y);
+  uint8_t* yscale = at<uint8_t>(ws, p.off_yscale);
   hipEvent_t* ev = timing_slot();
 
 #define BEAM_TRY(expr)                                  \
@@ -306,12 +310,13 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
                                          p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_down_stream(p.lds_stream, h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y, p.H,
-                                      p.I, st));
+    BEAM_TRY(beam::launch_down_stream(p.lds_stream, h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y16,
+                                      yscale, p.H, p.I, st));
   else
-    BEAM_TRY(beam::launch_down_grouped(h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y, p.H, p.I, st));
+    BEAM_TRY(beam::launch_down_grouped(h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y16, yscale, p.H, p.I,
+                                       st));
   BEAM_TRY(mark(ev, kStCombine, st));
-  BEAM_TRY(beam::launch_combine(y, topk_w, out, T, p.H, p.K, st));
+  BEAM_TRY(beam::launch_combine(y16, yscale, topk_w, out, T, p.H, p.K, st));
   BEAM_TRY(mark(ev, kNumStages, st));
 #undef BEAM_TRY
   return BEAM_MOE_OK;

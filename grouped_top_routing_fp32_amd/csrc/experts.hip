@@ -7,11 +7,12 @@
 // each expert is a SwiGLU MLP with intermediate size 2560 (hidden 5120);
 // section 残差流 (residual stream): the SwiGLU product is computed in FP32.  Per expert e and routed row r:
 //   h[r] = silu(W_gate[e] x[r]) * (W_up[e] x[r])   bf16 MFMA, SwiGLU in FP32
-//   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 out
+//   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 accumulation
 // h is handed to the down projection as fp16 (11 significant bits against
 // bf16's 8) with a power-of-two scale 2^-s per block of 64 columns of a pass
 // of rows, s chosen so the block's largest magnitude stays below 2^15; W_down
-// is converted from bf16 to fp16 exactly (times 2^s) as it is loaded.
+// is converted from bf16 to fp16 exactly (times 2^s) as it is loaded.  y goes
+// to the combine the same way: fp16 scaled by 2^-s per (row group, 64 columns).
 // Rows are processed in expert-sorted order (the dispatch permutation); a
 // tile table produced by the dispatch maps workgroups to experts.
 //
@@ -117,19 +118,47 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(const uint16_t* __re
   }
 }
 
+// Writes one pass of y: fp16 bits of acc * 2^-s, s from the largest magnitude
+// of the pass's rows in the workgroup's 64 columns, and s per (row, block).
+__device__ __forceinline__ void store_y_pass(const f32x4& acc, int nrows, const int32_t* __restrict__ slot_of,
+                                             uint16_t* __restrict__ y16, uint8_t* __restrict__ yscale, int H,
+                                             int col, float* smax) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float mx = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if ((lane >> 4) * 4 + r < nrows) mx = fmaxf(mx, fabsf(acc[r]));
+  mx = wave_max(mx);
+  if (lane == 0) smax[wave] = mx;
+  __syncthreads();
+  const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = (lane >> 4) * 4 + r;
+    if (row < nrows) {
+      const size_t slot = (size_t)slot_of[row];
+      y16[slot * H + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[r], -sexp));
+      if (wave == 0 && (lane & 15) == 0) yscale[slot * (H / kScaleCols) + blockIdx.y] = (uint8_t)sexp;
+    }
+  }
+}
+
 // grid: (max_tiles, H / 64); block 256.  y[slot] = W_down[e] h (fp16 MFMA,
 // W_down converted exactly from bf16 and scaled back by 2^s per 64-column
-// block of h).
+// block of h), stored as fp16 with its own scale (store_y_pass).
 template <int U>
 __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __restrict__ h,
                                                           const uint8_t* __restrict__ hscale,
                                                           const int32_t* __restrict__ sorted_slots,
                                                           const Tile* __restrict__ tiles,
                                                           const int32_t* __restrict__ ntiles,
-                                                          const uint16_t* __restrict__ wd, float* __restrict__ y,
+                                                          const uint16_t* __restrict__ wd,
+                                                          uint16_t* __restrict__ y16, uint8_t* __restrict__ yscale,
                                                           int H, int I) {
   __shared__ uint8_t ssc[kMaxScaleBlocks];
   __shared__ int sany;
+  __shared__ float smax[4];
   if ((int)blockIdx.x >= ntiles[0]) return;
   const Tile tl = tiles[blockIdx.x];
   const int tid = threadIdx.x;
@@ -177,12 +206,8 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __rest
       if (s + 2 < steps) load(b0, a0, (s + 2) * 32 * U);
       if (s + 1 < steps) math(b1, a1, (s + 1) * 32 * U);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      if (p + row < tl.rows) y[(size_t)sorted_slots[tl.row_start + p + row] * H + col] = acc[r];
-    }
-    __syncthreads();  // ssc and sany are rewritten by the next pass
+    store_y_pass(acc, min(kStreamRows, tl.rows - p), sorted_slots + tl.row_start + p, y16, yscale, H, col, smax);
+    __syncthreads();  // ssc, sany and smax are rewritten by the next pass
   }
 }
 
@@ -341,7 +366,7 @@ __global__ __launch_bounds__(256) void gateup_stream_lds_kernel(const uint16_t* 
 }
 
 // grid: (max_tiles, H / 64); block 256; dynamic LDS SLOTS * 72 * 256 bytes + the
-// pass's scales.  Slot rows: 0..63 W_down rows of the workgroup's columns,
+// pass's scales.  y leaves as in down_stream_kernel.  Slot rows: 0..63 W_down rows of the workgroup's columns,
 // 64..71 the activation rows (h, fp16) of the pass.
 template <int SLOTS, int SK>
 __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __restrict__ h,
@@ -349,8 +374,9 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
                                                               const int32_t* __restrict__ sorted_slots,
                                                               const Tile* __restrict__ tiles,
                                                               const int32_t* __restrict__ ntiles,
-                                                              const uint16_t* __restrict__ wd, float* __restrict__ y,
-                                                              int H, int I) {
+                                                              const uint16_t* __restrict__ wd,
+                                                              uint16_t* __restrict__ y16,
+                                                              uint8_t* __restrict__ yscale, int H, int I) {
   using G = StageGeom<SK>;
   constexpr int kRows = 64 + kLdsRows;
   constexpr int kSlot = kRows * G::kRowBytes;
@@ -358,6 +384,7 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
   constexpr int kCopies = kWCopies + 1;   // plus one copy (or part of one) of activation rows
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   __shared__ int sany;
+  __shared__ float smax[4];
   uint8_t* ssc = ring + SLOTS * kSlot;  // the pass's activation scales
   if ((int)blockIdx.x >= ntiles[0]) return;
   const Tile tl = tiles[blockIdx.x];
@@ -426,11 +453,7 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
         acc = mfma16x16x32_f16(rv ? a : u32x4{0u, 0u, 0u, 0u}, bh, acc);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      if (row < nrows) y[(size_t)sorted_slots[tl.row_start + p + row] * H + col] = acc[r];
-    }
+    store_y_pass(acc, nrows, sorted_slots + tl.row_start + p, y16, yscale, H, col, smax);
     __syncthreads();  // every wave is done with the ring and the scales before the next pass
   }
 }
@@ -477,23 +500,25 @@ hipError_t launch_gateup_stream(bool lds, const uint16_t* x, const int32_t* slot
 }
 
 hipError_t launch_down_stream(bool lds, const uint16_t* h, const uint8_t* hscale, const int32_t* slots,
-                              const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y,
-                              int H, int I, hipStream_t st) {
+                              const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd,
+                              uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st) {
   dim3 grid(max_tiles, H / 64);
   if (lds) {
     const size_t bytes = down_stream_lds_bytes(I);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_stream_lds_kernel<kSSlots, kSk>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((down_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, h, hscale, slots, tiles, ntiles,
-                       wd, y, H, I);
+    hipLaunchKernelGGL((down_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
+                       ntiles, wd, y16, yscale, H, I);
     return hipGetLastError();
   }
   // I % 128 == 0: I / 32 is a multiple of 4; eight-step stages need I % 256 == 0, else four
   if ((I / 32) % 8 == 0)
-    hipLaunchKernelGGL(down_stream_kernel<8>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y, H, I);
+    hipLaunchKernelGGL(down_stream_kernel<8>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y16,
+                       yscale, H, I);
   else
-    hipLaunchKernelGGL(down_stream_kernel<4>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y, H, I);
+    hipLaunchKernelGGL(down_stream_kernel<4>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y16,
+                       yscale, H, I);
   return hipGetLastError();
 }
 
@@ -502,29 +527,40 @@ hipError_t launch_down_stream(bool lds, const uint16_t* h, const uint8_t* hscale
 // ---------------------------------------------------------------------------
 constexpr int kCombineCols = 1024;  // columns per workgroup (256 threads x 4)
 
-// grid: (T, ceil(H / 1024)); block 256.  The K rows of a token are loaded
-// together (up to 16), then summed in ascending k.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
-                                                      float* __restrict__ out, int H, int K) {
+// grid: (T, ceil(H / 1024)); block 256.  The K rows of a token (fp16, each with
+// its 64-column scale) are loaded together (up to 16), then summed in
+// ascending k in FP32.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y16,
+                                                      const uint8_t* __restrict__ yscale,
+                                                      const float* __restrict__ w, float* __restrict__ out, int H,
+                                                      int K) {
   const int t = blockIdx.x;
   const int c = blockIdx.y * kCombineCols + threadIdx.x * 4;
   if (c >= H) return;
-  const float* yt = y + (size_t)t * K * H + c;
-  const float* wt = w + (size_t)t * K;
-  f32x4 v[16];
+  const size_t row0 = (size_t)t * K;
+  const int nsb = H / kScaleCols;
+  f32x4 yv[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k)
-    if (k < K) v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yt + (size_t)k * H));
+    if (k < K) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(y16 + (row0 + k) * H + c);
+      const int s = yscale[(row0 + k) * nsb + c / kScaleCols];
+      yv[k][0] = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.x & 0xFFFFu)), s);
+      yv[k][1] = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.x >> 16)), s);
+      yv[k][2] = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.y & 0xFFFFu)), s);
+      yv[k][3] = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.y >> 16)), s);
+    }
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < 16; ++k)
-    if (k < K) acc += wt[k] * v[k];
+    if (k < K) acc += w[row0 + k] * yv[k];
   *reinterpret_cast<f32x4*>(out + (size_t)t * H + c) = acc;
 }
 
-hipError_t launch_combine(const float* y, const float* w, float* out, int T, int H, int K, hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T, (H + kCombineCols - 1) / kCombineCols), dim3(256), 0, st, y, w, out, H,
-                     K);
+hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(combine_kernel, dim3(T, (H + kCombineCols - 1) / kCombineCols), dim3(256), 0, st, y16, yscale, w,
+                     out, H, K);
   return hipGetLastError();
 }
 

@@ -8,9 +8,9 @@
 // computed in FP32.  Per expert e and
 // routed row r (rows in expert-sorted order, tiles from the dispatch):
 //   h[r] = silu(W_gate[e] x[r]) * (W_up[e] x[r])   bf16 MFMA, FP32 SwiGLU
-//   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 out
-// h is stored as fp16 with a power-of-two scale 2^-s per (tile, 64 columns),
-// s chosen so the block's largest magnitude stays below 2^15.
+//   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 accumulation
+// h and y are stored as fp16 with a power-of-two scale 2^-s per (tile, 64
+// columns), s chosen so the block's largest magnitude stays below 2^15.
 //
 // Block tile: 256 rows x 256 B-rows (gate/up: 128 gate + the same 128 up
 // columns; down: 256 output columns), K advancing 64 per stage.  8 waves (two
@@ -48,6 +48,7 @@ constexpr int kBK = 64;         // K per stage
 constexpr int kThreads = 512;
 constexpr int kSlotHalfs = kBM * kBK;  // 16384 elements = 32 KB per operand
 static_assert(kBK == kScaleCols, "down reads one activation scale per stage");
+static_assert(kBN == 4 * kScaleCols, "the down output tile spans four scale blocks");
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
@@ -61,16 +62,20 @@ __device__ __forceinline__ int xcd_lin(int b, int total) {
 }  // namespace gg
 
 // GATEUP: act = x [T, H]; w0 = W_gate, w1 = W_up [E, I, H]; out = h fp16 [n, I]; hscale written.
-// !GATEUP: act = h fp16 [n, I]; w0 = W_down [E, H, I]; out = y fp32 [n, H] (row slot); hscale read.
+// !GATEUP: act = h fp16 [n, I]; w0 = W_down [E, H, I]; hscale read; out = y fp16 [n, H] (row slot),
+//          scaled by 2^-s with s per (tile, 64 columns) written to oscale [n, H / 64].
 template <bool GATEUP>
 __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_slots, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
-    void* __restrict__ out, uint8_t* __restrict__ hscale, int Kdim, int Ndim, int topk, int nbn, int total_blocks) {
+    void* __restrict__ out, uint8_t* __restrict__ hscale, uint8_t* __restrict__ oscale, int Kdim, int Ndim, int topk,
+    int nbn, int total_blocks) {
   using namespace gg;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kSlotHalfs];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kSlotHalfs];
-  __shared__ float smax[8];
+  // two stages of A, then two of B
+  __shared__ __attribute__((aligned(16))) uint16_t ring[4 * kSlotHalfs];
+  __shared__ float smax[16];
+  uint16_t(*sA)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring);
+  uint16_t(*sB)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring + 2 * kSlotHalfs);
 
   // The grid is sized for the most tiles a batch can have; the order spans the
   // tiles this batch has, so every XCD gets an equal share and the surplus
@@ -264,18 +269,52 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
         }
       }
   } else {
+    // Output tile as fp16 scaled by 2^-s per 64 columns, s from the tile's largest
+    // magnitude in those columns.  Wave (wm, wn) holds columns wn*128 + 16 j +
+    // lane%16, i.e. the 64-column blocks 2 wn (j < 4) and 2 wn + 1 (j >= 4).
+    // (Staging the tile in LDS to store whole rows measured slower.)
+    float mx[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = 64 * i + 16 * wm + (lane >> 4) * 4 + r < tl.rows;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx[j >> 2] = fmaxf(mx[j >> 2], ok ? fabsf(acc[i][j][r]) : 0.f);
+      }
+    mx[0] = wave_max(mx[0]);
+    mx[1] = wave_max(mx[1]);
+    if (lane == 0) {
+      smax[2 * wave] = mx[0];
+      smax[2 * wave + 1] = mx[1];
+    }
+    __syncthreads();
+    // scale of 64-column block b = 2 wn' + half: max over the four row waves wm'
+    auto block_exp = [&](int b) {
+      float m = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) m = fmaxf(m, smax[2 * ((w2 << 1) | (b >> 1)) + (b & 1)]);
+      return act_scale_exp(m);
+    };
+    const int sexp0 = block_exp(2 * wn), sexp1 = block_exp(2 * wn + 1);
+    uint16_t* y16 = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 64 * i + 16 * wm + (lane >> 4) * 4 + r;
         if (row < tl.rows) {
-          const int slot = sorted_slots[tl.row_start + row];
-          float* yrow = reinterpret_cast<float*>(out) + (size_t)slot * Ndim + n0 + wn * 128 + (lane & 15);
+          uint16_t* yrow = y16 + (size_t)sorted_slots[tl.row_start + row] * Ndim + n0 + wn * 128 + (lane & 15);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) yrow[16 * j] = acc[i][j][r];
+          for (int j = 0; j < 8; ++j)
+            yrow[16 * j] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[i][j][r], -(j < 4 ? sexp0 : sexp1)));
         }
       }
+    const int nsb = Ndim / kScaleCols;
+    for (int q = tid; q < tl.rows * 4; q += kThreads) {
+      const int row = q >> 2, b = q & 3;
+      oscale[(size_t)sorted_slots[tl.row_start + row] * nsb + n0 / kScaleCols + b] = (uint8_t)block_exp(b);
+    }
   }
 }
 
@@ -289,17 +328,17 @@ hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const 
   const int nbn = I / (gg::kBN / 2);  // I % 128 == 0
   const int total = gemm_blocks(max_tiles, nbn);
   hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(total), dim3(gg::kThreads), 0, st, x, slots, tiles, ntiles, wg,
-                     wu, (void*)h, hscale, H, I, K, nbn, total);
+                     wu, (void*)h, hscale, nullptr, H, I, K, nbn, total);
   return hipGetLastError();
 }
 
 hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, float* y, int H, int I,
-                               hipStream_t st) {
+                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16,
+                               uint8_t* yscale, int H, int I, hipStream_t st) {
   const int nbn = H / gg::kBN;  // H % 256 == 0
   const int total = gemm_blocks(max_tiles, nbn);
   hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(total), dim3(gg::kThreads), 0, st, h, slots, tiles, ntiles, wd,
-                     nullptr, (void*)y, const_cast<uint8_t*>(hscale), I, H, 0, nbn, total);
+                     nullptr, (void*)y16, const_cast<uint8_t*>(hscale), yscale, I, H, 0, nbn, total);
   return hipGetLastError();
 }
 

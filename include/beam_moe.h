@@ -75,8 +75,9 @@ enum {
 
 /* Bytes of workspace that beam_moe_route, beam_moe_dispatch and
  * beam_moe_forward need for T tokens (one size serves all three; it grows
- * linearly in T: at Beam dims about 26 KB per token, mostly the bf16 SwiGLU
- * activations [T*K, I] and the FP32 expert outputs [T*K, H]).
+ * linearly in T: at Beam dims about 122 KB per token, mostly the fp16 SwiGLU
+ * activations [T*K, I] and the fp16 expert outputs [T*K, H], each with a
+ * power-of-two scale per 64 columns).
  * Returns SIZE_MAX for invalid or unsupported dims. */
 size_t beam_moe_workspace_bytes(const beam_moe_dims* dims, int32_t T);
 
