@@ -74,11 +74,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     acc_lo[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int k = kbeg; k < kend; k += kRtK) {
-    u32x4 xv = ldg16(xsrc + k);
-    f32x4 wv[2];
+  // operands of step k are loaded during step k - 32 (one step in flight)
+  u32x4 xv = ldg16(xsrc + kbeg);
+  f32x4 wv[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wv[i] = *reinterpret_cast<const f32x4*>(wsrc[i] + k);
+  for (int i = 0; i < 2; ++i) wv[i] = *reinterpret_cast<const f32x4*>(wsrc[i] + kbeg);
+  for (int k = kbeg; k < kend; k += kRtK) {
     __syncthreads();  // previous step's fragment reads are done
     *reinterpret_cast<u32x4*>(&sA[xa_row * kRtLd + xa_kc * 8]) = xv;
 #pragma unroll
@@ -99,6 +100,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       *reinterpret_cast<uint2*>(&sB[2][off]) = pl;
     }
     __syncthreads();
+    if (k + kRtK < kend) {
+      xv = ldg16(xsrc + k + kRtK);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) wv[i] = *reinterpret_cast<const f32x4*>(wsrc[i] + k + kRtK);
+    }
     const int arow = wave * 16 + (lane & 15);
     const int kk = (lane >> 4) * 8;
     u32x4 a = *reinterpret_cast<const u32x4*>(&sA[arow * kRtLd + kk]);
