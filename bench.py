@@ -62,6 +62,11 @@ def parse():
                     help="write the traffic file from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
                     help="write a per-workload kernel time table from a rocprofv3 --kernel-trace run and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the decode/prefill line: tokens/s and roofline fractions over batch sizes T")
+    ap.add_argument("--sweep-tokens", default="1,2,4,8,16,32,64,128,256,512,1024,2048,4096,8192,16384")
+    ap.add_argument("--summarize-sweep", nargs=2, metavar=("SWEEP_JSON", "OUT_MD"),
+                    help="write a markdown table from a --sweep JSON line and exit")
     return ap.parse_args()
 
 
@@ -131,6 +136,29 @@ def summarize_pmc(fetch_dir, write_dir):
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_sweep(sweep_json, out_md):
+    """Markdown table of a `bench.py --sweep` JSON line."""
+    with open(sweep_json) as f:
+        d = json.loads(f.read().strip().splitlines()[-1])
+    out = ["# T sweep: Beam MoE block forward, batch sizes 1 .. 16384 on one MI355X", "",
+           "Command (repository root on the GPU host):", "", "```",
+           "python3 bench.py --sweep --steps 20 --warmup 3 > <SWEEP_JSON>",
+           "python3 bench.py --summarize-sweep <SWEEP_JSON> <this file>", "```", "",
+           "Per point: mean ms per forward step over the timed steps (fewer steps for large T), the",
+           "expert path the library chose, and the layer's fraction of the HBM roofline (bytes of the",
+           "touched experts' weights, router, x and out over the step time, against 8 TB/s) and of",
+           "the bf16 MFMA roofline (expert FLOPs over the step time, against 2.5 PFLOP/s).", "",
+           "| T | ms / step | tokens/s | path | experts touched | HBM fraction | MFMA fraction | gate/up ms | down ms |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for p in d["points"]:
+        out.append(f"| {p['T']} | {p['ms_per_step']:.3f} | {p['tokens_per_s']:,.0f} | {p['path']} | "
+                   f"{p['experts_touched']} | {p['layer_hbm_frac']:.3f} | {p['layer_mfma_frac']:.3f} | "
+                   f"{p['stage_ms']['gate_up']:.3f} | {p['stage_ms']['down']:.3f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def summarize_trace(trace_dir, out_md):
@@ -207,10 +235,14 @@ def measured_traffic(workload):
 
 
 def time_workload(name, experts, steps, warmup):
+    from grouped_top_routing_fp32_amd import synth
+    return time_wl(synth.WORKLOADS[name], experts, steps, warmup)
+
+
+def time_wl(wl, experts, steps, warmup):
     import torch
     from grouped_top_routing_fp32_amd import binding, synth
 
-    wl = synth.WORKLOADS[name]
     d = wl.dims
     x = synth.make_x(wl, "cuda")
     wr = synth.make_router(wl, "cuda")
@@ -334,6 +366,40 @@ def cpu_baseline(r, target_s):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def expert_path(wl):
+    """Which expert kernels the library runs for this batch (its rule: at most 4 rows per
+    expert on average -> stream kernels, else the grouped GEMMs)."""
+    avg = wl.tokens * wl.dims.topk / wl.dims.num_experts
+    return "stream" if avg <= 4 else "grouped GEMM"
+
+
+def sweep(args, experts):
+    """Tokens/s and both roofline fractions of the whole layer over batch sizes T."""
+    from grouped_top_routing_fp32_amd import synth
+    base = synth.WORKLOADS["decode"]
+    points = []
+    for T in [int(t) for t in args.sweep_tokens.split(",") if t]:
+        wl = synth.with_tokens(base, T)
+        steps = max(3, min(args.steps, int(2000 / max(1, T))))  # keep large batches short
+        r = time_wl(wl, experts, steps, args.warmup)
+        s = layer_summary(r)
+        hbm, mfma = s["layer_hbm_frac"], s["layer_mfma_frac"]
+        points.append({"T": T, "steps": steps, "ms_per_step": round(r["ms_per_step"], 4),
+                       "tokens_per_s": round(T / (r["ms_per_step"] / 1e3), 1), "path": expert_path(wl),
+                       "experts_touched": r["n_touched"], "max_rows_per_expert": r["max_count"],
+                       "layer_hbm_gbs": s["layer_hbm_gbs"], "layer_hbm_frac": hbm,
+                       "layer_expert_tflops": s["layer_expert_tflops"], "layer_mfma_frac": mfma,
+                       "bound": "hbm" if hbm >= mfma else "mfma", "stage_ms": s["stage_ms"]})
+        print(f"[bench] sweep T={T}: {r['ms_per_step']:.4f} ms, hbm {hbm:.3f}, mfma {mfma:.3f}",
+              file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "MoE-layer tokens/s and roofline fractions over batch size T", "unit": "tokens/s",
+                      "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "Beam MoE block forward, T swept", "hidden": base.dims.hidden,
+                                 "intermediate": base.dims.intermediate, "experts": base.dims.num_experts,
+                                 "topk": base.dims.topk},
+                      "points": points}), flush=True)
+
+
 def copy_calibration():
     """A plain elementwise copy of COPY_BYTES (read once, written once), outside any timed region."""
     import torch
@@ -354,6 +420,9 @@ def main():
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
         return
+    if args.summarize_sweep:
+        summarize_sweep(*args.summarize_sweep)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Beam MoE block here runs on a single MI355X "
               "(no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
@@ -370,6 +439,9 @@ def main():
     torch.cuda.synchronize()
     if args.copy_calibration:
         copy_calibration()
+    if args.sweep:
+        sweep(args, experts)
+        return
     results = {}
     for name in names:
         print(f"[bench] timing {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)

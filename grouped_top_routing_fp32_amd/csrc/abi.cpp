@@ -22,13 +22,13 @@ int dispatch_units(int n);
 hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_slots, Tile* tiles, int mt, int32_t* ntiles, hipStream_t st);
 int scale_cols();
-bool stream_lds_fits(int H, int I);
-hipError_t launch_gateup_stream(bool lds, const uint16_t* x, const int32_t* slots, const Tile* tiles,
-                                const int32_t* ntiles, int max_tiles, const uint16_t* wg, const uint16_t* wu,
-                                uint16_t* h, uint8_t* hscale, int H, int I, int K, hipStream_t st);
-hipError_t launch_down_stream(bool lds, const uint16_t* h, const uint8_t* hscale, const int32_t* slots,
-                              const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd,
-                              uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st);
+bool stream_fits(int H, int I);
+hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
+                                int H, int I, int K, hipStream_t st);
+hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                              const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16,
+                              uint8_t* yscale, int H, int I, hipStream_t st);
 hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
                           hipStream_t st);
 int grouped_gemm_rows();
@@ -62,14 +62,14 @@ bool dims_ok(const beam_moe_dims* d) {
   return true;
 }
 
-// Expert-path choice: the stream kernels serve batches with few rows per
-// expert (weights streamed once per pass of rows), the grouped GEMMs the rest.
-// Among the stream kernels, the variant with rows staged in LDS (passes of 8)
-// serves the smallest batches, where an expert rarely sees more than 8 rows.
-double avg_rows(const beam_moe_dims* d, int T) { return (double)T * d->topk / d->num_experts; }
-bool use_stream_path(const beam_moe_dims* d, int T) { return avg_rows(d, T) < 32.0; }
-bool use_lds_stream(const beam_moe_dims* d, int T) {
-  return avg_rows(d, T) <= 4.0 && beam::stream_lds_fits(d->hidden, d->intermediate);
+// Expert-path choice: the stream kernels serve batches with at most 4 rows per
+// expert on average, the grouped GEMMs the rest.  The stream kernels read an
+// expert's weights once per pass of 8 rows, the grouped GEMMs once per 256-row
+// tile, so the stream kernels win only while an expert rarely sees more than
+// one pass (measured at Beam dims: T = 128 runs 3.5 ms on the stream kernels,
+// T = 160 .. 1024 run 4.0 .. 4.3 ms on the grouped GEMMs).
+bool use_stream_path(const beam_moe_dims* d, int T) {
+  return (double)T * d->topk / d->num_experts <= 4.0 && beam::stream_fits(d->hidden, d->intermediate);
 }
 
 struct Plan {
@@ -81,7 +81,7 @@ struct Plan {
   int units;
   size_t off_hist;
   // expert tiles
-  bool stream, lds_stream;
+  bool stream;
   // one tile table serves both projections: whole experts (stream path) or
   // row tiles of the grouped GEMMs, whose down kernel reads the activation
   // scales of the gate/up tile its rows belong to
@@ -111,7 +111,6 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
   p->splits = (ksteps + steps_per - 1) / steps_per;
   p->units = beam::dispatch_units(p->n);
   p->stream = use_stream_path(d, T);
-  p->lds_stream = p->stream && use_lds_stream(d, T);
   const int touched = p->E < p->n ? p->E : p->n;  // most experts with rows
   if (p->stream) {
     p->mt = kWholeExpert;
@@ -303,15 +302,15 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
                                  sorted_slots, tiles, p.mt, ntiles, st));
   BEAM_TRY(mark(ev, kStGateUp, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_gateup_stream(p.lds_stream, x, sorted_slots, tiles, ntiles, p.max_tiles, wg, wu, h, hscale,
-                                        p.H, p.I, p.K, st));
+    BEAM_TRY(beam::launch_gateup_stream(x, sorted_slots, tiles, ntiles, p.max_tiles, wg, wu, h, hscale, p.H, p.I,
+                                        p.K, st));
   else
     BEAM_TRY(beam::launch_gateup_grouped(x, sorted_slots, tiles, ntiles, p.max_tiles, wg, wu, h, hscale, p.H, p.I,
                                          p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
   if (p.stream)
-    BEAM_TRY(beam::launch_down_stream(p.lds_stream, h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y16,
-                                      yscale, p.H, p.I, st));
+    BEAM_TRY(beam::launch_down_stream(h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y16, yscale, p.H, p.I,
+                                      st));
   else
     BEAM_TRY(beam::launch_down_grouped(h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y16, yscale, p.H, p.I,
                                        st));

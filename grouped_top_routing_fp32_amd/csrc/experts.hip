@@ -19,105 +19,17 @@
 // With few rows per expert the step is bound by streaming each touched
 // expert's weights from HBM once: a workgroup owns one expert and 64 output
 // columns, each wave 16 columns over the whole K, so no cross-wave reduction
-// is needed, and weights go from memory straight into MFMA operand registers.
-//   *_stream_kernel      activation operands loaded from memory with the
-//                        weights; passes of 16 rows
-//   *_stream_lds_kernel  weights and the pass's activation rows (up to 8)
-//                        copied into LDS in whole 256-byte row segments
-// Batches with many rows per expert use the grouped GEMMs (grouped_gemm.hip).
+// is needed; weights and the pass's activation rows (up to 8) are copied into
+// LDS in whole 256-byte row segments.  Batches with more rows per expert use
+// the grouped GEMMs (grouped_gemm.hip), which read an expert's weights once
+// per 256-row tile rather than once per pass.
 #include "common.h"
 
 namespace beam {
 
-constexpr int kMaxScaleBlocks = 512;  // I <= 32768
-
 // ---------------------------------------------------------------------------
-// stream kernels, register operands
+// stream kernels (few rows per expert)
 // ---------------------------------------------------------------------------
-// Loads run U MFMA steps ahead of the math (two register stages) and use
-// ordinary cached loads: a 16-byte operand load touches half of a 128-byte line,
-// and the other half is read by the next step.
-constexpr int kStreamRows = 16;  // rows per pass
-
-// grid: (max_tiles, I / 64); block 256.  One tile = all rows of one expert.
-// Writes h (fp16 bits, scaled by 2^-s) and s per (row, 64-column block).
-template <int U>
-__global__ __launch_bounds__(256) void gateup_stream_kernel(const uint16_t* __restrict__ x,
-                                                            const int32_t* __restrict__ sorted_slots,
-                                                            const Tile* __restrict__ tiles,
-                                                            const int32_t* __restrict__ ntiles,
-                                                            const uint16_t* __restrict__ wg,
-                                                            const uint16_t* __restrict__ wu,
-                                                            uint16_t* __restrict__ h, uint8_t* __restrict__ hscale,
-                                                            int H, int I, int K) {
-  __shared__ float smax[4];
-  if ((int)blockIdx.x >= ntiles[0]) return;
-  const Tile tl = tiles[blockIdx.x];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = blockIdx.y * 64 + wave * 16 + (lane & 15);
-  const int kk = (lane >> 4) * 8;
-  const size_t ebase = (size_t)tl.expert * I * H;
-  const uint16_t* pg = wg + ebase + (size_t)col * H + kk;
-  const uint16_t* pu = wu + ebase + (size_t)col * H + kk;
-  const int nsb = I / kScaleCols;
-  const int steps = H / (32 * U);
-
-  for (int p = 0; p < tl.rows; p += kStreamRows) {
-    const int m = lane & 15;
-    const bool rv = p + m < tl.rows;
-    const int tok = rv ? sorted_slots[tl.row_start + p + m] / K : 0;
-    const uint16_t* pa = x + (size_t)tok * H + kk;
-    f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
-    u32x4 g0[U], u0[U], a0[U], g1[U], u1[U], a1[U];
-    auto load = [&](u32x4(&g)[U], u32x4(&uu)[U], u32x4(&a)[U], int k) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        g[u] = ldg16(pg + k + 32 * u);
-        uu[u] = ldg16(pu + k + 32 * u);
-        a[u] = rv ? ldg16(pa + k + 32 * u) : u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    auto math = [&](u32x4(&g)[U], u32x4(&uu)[U], u32x4(&a)[U]) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        ag = mfma16x16x32(a[u], g[u], ag);
-        au = mfma16x16x32(a[u], uu[u], au);
-      }
-    };
-    load(g0, u0, a0, 0);
-    for (int s = 0; s < steps; s += 2) {
-      if (s + 1 < steps) load(g1, u1, a1, (s + 1) * 32 * U);
-      math(g0, u0, a0);
-      if (s + 2 < steps) load(g0, u0, a0, (s + 2) * 32 * U);
-      if (s + 1 < steps) math(g1, u1, a1);
-    }
-    // SwiGLU in FP32; one power-of-two scale per (16-row pass, 64 columns)
-    float v[4];
-    float mx = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      v[r] = (p + row < tl.rows) ? silu_f32(ag[r]) * au[r] : 0.f;
-      mx = fmaxf(mx, fabsf(v[r]));
-    }
-    mx = wave_max(mx);
-    if (lane == 0) smax[wave] = mx;
-    __syncthreads();
-    const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      if (p + row < tl.rows) {
-        const size_t grow = (size_t)(tl.row_start + p + row);
-        h[grow * I + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(v[r], -sexp));
-        if (wave == 0 && (lane & 15) == 0) hscale[grow * nsb + blockIdx.y] = (uint8_t)sexp;
-      }
-    }
-    __syncthreads();  // smax is rewritten by the next pass
-  }
-}
-
 // Writes one pass of y: fp16 bits of acc * 2^-s, s from the largest magnitude
 // of the pass's rows in the workgroup's 64 columns, and s per (row, block).
 __device__ __forceinline__ void store_y_pass(const f32x4& acc, int nrows, const int32_t* __restrict__ slot_of,
@@ -144,81 +56,11 @@ __device__ __forceinline__ void store_y_pass(const f32x4& acc, int nrows, const 
   }
 }
 
-// grid: (max_tiles, H / 64); block 256.  y[slot] = W_down[e] h (fp16 MFMA,
-// W_down converted exactly from bf16 and scaled back by 2^s per 64-column
-// block of h), stored as fp16 with its own scale (store_y_pass).
-template <int U>
-__global__ __launch_bounds__(256) void down_stream_kernel(const uint16_t* __restrict__ h,
-                                                          const uint8_t* __restrict__ hscale,
-                                                          const int32_t* __restrict__ sorted_slots,
-                                                          const Tile* __restrict__ tiles,
-                                                          const int32_t* __restrict__ ntiles,
-                                                          const uint16_t* __restrict__ wd,
-                                                          uint16_t* __restrict__ y16, uint8_t* __restrict__ yscale,
-                                                          int H, int I) {
-  __shared__ uint8_t ssc[kMaxScaleBlocks];
-  __shared__ int sany;
-  __shared__ float smax[4];
-  if ((int)blockIdx.x >= ntiles[0]) return;
-  const Tile tl = tiles[blockIdx.x];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = blockIdx.y * 64 + wave * 16 + (lane & 15);
-  const int kk = (lane >> 4) * 8;
-  const uint16_t* pb = wd + (size_t)tl.expert * H * I + (size_t)col * I + kk;
-  const int nsb = I / kScaleCols;
-  const int steps = I / (32 * U);
-
-  for (int p = 0; p < tl.rows; p += kStreamRows) {
-    const int m = lane & 15;
-    const bool rv = p + m < tl.rows;
-    const uint16_t* pa = h + (size_t)(tl.row_start + p + (rv ? m : 0)) * I + kk;
-    if (tid == 0) sany = 0;
-    __syncthreads();
-    for (int i = tid; i < nsb; i += 256) {
-      const uint8_t sv = hscale[(size_t)(tl.row_start + p) * nsb + i];
-      ssc[i] = sv;
-      if (sv) sany = 1;
-    }
-    __syncthreads();
-    const bool scaled = sany != 0;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 b0[U], a0[U], b1[U], a1[U];
-    auto load = [&](u32x4(&b)[U], u32x4(&a)[U], int k) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        b[u] = ldg16(pb + k + 32 * u);
-        a[u] = rv ? ldg16(pa + k + 32 * u) : u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    auto math = [&](u32x4(&b)[U], u32x4(&a)[U], int k) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const u32x4 bh = scaled ? bf16x8_to_f16x8_scaled(b[u], ssc[(k + 32 * u) / kScaleCols]) : bf16x8_to_f16x8(b[u]);
-        acc = mfma16x16x32_f16(a[u], bh, acc);
-      }
-    };
-    load(b0, a0, 0);
-    for (int s = 0; s < steps; s += 2) {
-      if (s + 1 < steps) load(b1, a1, (s + 1) * 32 * U);
-      math(b0, a0, s * 32 * U);
-      if (s + 2 < steps) load(b0, a0, (s + 2) * 32 * U);
-      if (s + 1 < steps) math(b1, a1, (s + 1) * 32 * U);
-    }
-    store_y_pass(acc, min(kStreamRows, tl.rows - p), sorted_slots + tl.row_start + p, y16, yscale, H, col, smax);
-    __syncthreads();  // ssc, sany and smax are rewritten by the next pass
-  }
-}
-
 int scale_cols() { return kScaleCols; }
 
-// ---------------------------------------------------------------------------
-// stream kernels with every operand staged in LDS (very few rows per expert)
-// ---------------------------------------------------------------------------
-// Same work split as the register-operand kernels (one expert per workgroup,
-// 64 output columns, each wave 16 columns over the whole K), but weights and
-// the pass's activation rows (at most kLdsRows) reach the MFMAs through LDS.
+// One expert per workgroup, 64 output columns, each wave 16 columns over the
+// whole K; weights and the pass's activation rows (at most kLdsRows) reach the
+// MFMAs through LDS.
 // Per stage of kSk = 128 of K, the load unit copies the workgroup's weight rows
 // and the activation rows into a ring slot (global_load_lds), each copy taking
 // 4 rows x 256 contiguous bytes: register operand loads touch 16 rows x 64
@@ -366,7 +208,7 @@ __global__ __launch_bounds__(256) void gateup_stream_lds_kernel(const uint16_t* 
 }
 
 // grid: (max_tiles, H / 64); block 256; dynamic LDS SLOTS * 72 * 256 bytes + the
-// pass's scales.  y leaves as in down_stream_kernel.  Slot rows: 0..63 W_down rows of the workgroup's columns,
+// pass's scales.  y leaves through store_y_pass.  Slot rows: 0..63 W_down rows of the workgroup's columns,
 // 64..71 the activation rows (h, fp16) of the pass.
 template <int SLOTS, int SK>
 __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __restrict__ h,
@@ -458,9 +300,6 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
   }
 }
 
-// Stream kernel shape: eight 32-wide K steps per register stage.
-constexpr int kStreamU = 8;
-
 // LDS of one gfx950 compute unit, the most one workgroup can take.
 constexpr size_t kLdsBytesPerCU = 160 * 1024;
 
@@ -469,56 +308,39 @@ size_t down_stream_lds_bytes(int I) {
   return (size_t)kSSlots * (64 + kLdsRows) * StageGeom<kSk>::kRowBytes + I / kScaleCols;
 }
 
-// Whether the LDS-staged stream kernels can run at this shape: K of both
-// projections in whole stages, and the down kernel's scales fit in LDS.
-bool stream_lds_fits(int H, int I) {
+// Whether the stream kernels can run at this shape: K of both projections in
+// whole stages, and the staged rows and the down kernel's scales fit in LDS.
+bool stream_fits(int H, int I) {
   return H % kSk == 0 && I % kSk == 0 && gateup_stream_lds_bytes() <= kLdsBytesPerCU &&
          down_stream_lds_bytes(I) <= kLdsBytesPerCU;
 }
 
-// Launchers of the stream path.  `lds` picks the LDS-staged kernels (passes of 8
-// rows; requires stream_lds_fits); gate/up and down must use the same variant,
-// since the down kernel reads one activation scale per pass of gate/up.
-hipError_t launch_gateup_stream(bool lds, const uint16_t* x, const int32_t* slots, const Tile* tiles,
-                                const int32_t* ntiles, int max_tiles, const uint16_t* wg, const uint16_t* wu,
-                                uint16_t* h, uint8_t* hscale, int H, int I, int K, hipStream_t st) {
-  // H % 256 == 0: the K loop divides (H / 256 register stages of eight steps, or
-  // H / 128 LDS stages); I % 64 == 0: the column grid divides
-  dim3 grid(max_tiles, I / 64);
-  if (lds) {
-    const size_t bytes = gateup_stream_lds_bytes();
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<kSSlots, kSk>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gateup_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, x, slots, tiles, ntiles, wg,
-                       wu, h, hscale, H, I, K);
-  } else {
-    hipLaunchKernelGGL(gateup_stream_kernel<kStreamU>, grid, dim3(256), 0, st, x, slots, tiles, ntiles, wg, wu, h,
-                       hscale, H, I, K);
-  }
+// Launchers of the stream path (passes of kLdsRows rows; requires stream_fits).
+// Gate/up and down run together: the down kernel reads one activation scale per
+// pass of gate/up.
+hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
+                                int H, int I, int K, hipStream_t st) {
+  dim3 grid(max_tiles, I / 64);  // I % 64 == 0
+  const size_t bytes = gateup_stream_lds_bytes();
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<kSSlots, kSk>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gateup_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, x, slots, tiles, ntiles,
+                     wg, wu, h, hscale, H, I, K);
   return hipGetLastError();
 }
 
-hipError_t launch_down_stream(bool lds, const uint16_t* h, const uint8_t* hscale, const int32_t* slots,
-                              const Tile* tiles, const int32_t* ntiles, int max_tiles, const uint16_t* wd,
-                              uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st) {
-  dim3 grid(max_tiles, H / 64);
-  if (lds) {
-    const size_t bytes = down_stream_lds_bytes(I);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_stream_lds_kernel<kSSlots, kSk>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((down_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
-                       ntiles, wd, y16, yscale, H, I);
-    return hipGetLastError();
-  }
-  // I % 128 == 0: I / 32 is a multiple of 4; eight-step stages need I % 256 == 0, else four
-  if ((I / 32) % 8 == 0)
-    hipLaunchKernelGGL(down_stream_kernel<8>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y16,
-                       yscale, H, I);
-  else
-    hipLaunchKernelGGL(down_stream_kernel<4>, grid, dim3(256), 0, st, h, hscale, slots, tiles, ntiles, wd, y16,
-                       yscale, H, I);
+hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                              const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16,
+                              uint8_t* yscale, int H, int I, hipStream_t st) {
+  dim3 grid(max_tiles, H / 64);  // H % 64 == 0
+  const size_t bytes = down_stream_lds_bytes(I);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_stream_lds_kernel<kSSlots, kSk>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((down_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
+                     ntiles, wd, y16, yscale, H, I);
   return hipGetLastError();
 }
 

@@ -118,7 +118,13 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
       bsrc[q] = wbase + (size_t)(n0 + (GATEUP ? (r & 127) : r)) * Kdim + c * 8;
     }
   }
+  // A wave whose 32 rows all lie past the tile's end copies no activations: no MFMA
+  // reads those LDS rows (a computed fragment starts below the tile's end, so its
+  // rows are in the range of a wave that copies).  The main loop waits for all
+  // copies at every step, so waves may issue different numbers of copies.
+  const bool copy_a = 32 * wave < tl.rows;
   auto issue_a = [&](int stage, int slot) {
+    if (!copy_a) return;
     const int k = stage * kBK;
 #pragma unroll
     for (int q = 0; q < 4; ++q) lds_copy16(asrc[q] + k, lds_addr(&sA[slot][(32 * wave + 8 * q) * kBK]));

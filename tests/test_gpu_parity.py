@@ -190,22 +190,24 @@ def test_route_end_to_end(name, T):
 # whole block
 # --------------------------------------------------------------------------
 MID = {
-    # stream path (few rows per expert), several column blocks, ragged row passes
-    "mid_stream": (synth.Workload("mid_stream", 45, synth.Dims(512, 384, 64, 8, 4, 6), router_sigma=0.06), None),
-    # tiled path, 16 experts, ~225 rows each: full and ragged 256-row tiles
+    # stream path (at most 4 rows per expert on average), several column blocks,
+    # experts with more than one 8-row pass
+    "mid_stream": (synth.Workload("mid_stream", 40, synth.Dims(512, 384, 64, 8, 4, 6), router_sigma=0.06), None),
+    # grouped path, 16 experts, ~225 rows each: full and ragged 256-row tiles
     "mid_tiled": (synth.Workload("mid_tiled", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06), None),
-    # tiled path with Beam's expert count: one partial tile per expert
+    # grouped path with Beam's expert count: one partial tile per expert
     "mid_tiled_e256": (synth.Workload("mid_tiled_e256", 1100, synth.Dims(768, 256, 256, 8, 4, 8), router_sigma=0.04),
                        None),
-    # stream path with skewed bias: some experts get more than 16 rows (several row passes)
+    # stream path with skewed bias: some experts get more than 16 rows (several passes)
     "mid_stream_skew": (synth.Workload("mid_stream_skew", 60, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
                                        zipf_s=1.2), None),
-    # stream path, rows staged in LDS, I/32 not a multiple of 8 (four-step down stages)
-    "mid_stream_lds_i384": (synth.Workload("mid_stream_lds_i384", 40, synth.Dims(512, 384, 64, 8, 4, 4),
-                                           router_sigma=0.06), None),
-    # stream path with register operands (about 9 rows per expert) and skew: several 16-row passes
-    "mid_stream_reg_skew": (synth.Workload("mid_stream_reg_skew", 150, synth.Dims(512, 256, 64, 8, 4, 4),
-                                           router_sigma=0.06, zipf_s=1.2), None),
+    # stream path, I/32 not a multiple of 8
+    "mid_stream_i384": (synth.Workload("mid_stream_i384", 40, synth.Dims(512, 384, 64, 8, 4, 4),
+                                       router_sigma=0.06), None),
+    # grouped path just above the stream threshold (about 9 rows per expert) with skew:
+    # mostly near-empty tiles, whose idle waves copy no activations
+    "mid_grouped_skew": (synth.Workload("mid_grouped_skew", 150, synth.Dims(512, 256, 64, 8, 4, 4),
+                                        router_sigma=0.06, zipf_s=1.2), None),
 }
 
 
@@ -231,7 +233,10 @@ def test_forward_mid(name):
 
 
 def _beam_forward(name, beam_experts, sample):
-    wl = synth.WORKLOADS[name]
+    return _beam_forward_wl(synth.WORKLOADS[name], beam_experts, sample)
+
+
+def _beam_forward_wl(wl, beam_experts, sample):
     p = Problem(wl, DEV, experts=beam_experts)
     bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
     torch.cuda.synchronize()
@@ -260,3 +265,13 @@ def test_forward_skewed(beam_experts):
     p, bufs = _beam_forward("skewed", beam_experts, [0, 4095, 8191])
     counts = bufs.counts.cpu().numpy()
     assert counts.max() >= 20 * counts.mean()
+
+
+# Beam dims across the batch sizes where the expert path changes form: T <= 128
+# stream kernels (T = 128: several experts with more than one 8-row pass); from
+# T = 160 the grouped GEMMs, first with nearly empty tiles, then partial ones.
+@pytest.mark.parametrize("T", [1, 8, 128, 160, 512, 1024, 2048])
+def test_forward_beam_sizes(beam_experts, T):
+    _announce(f"forward Beam T={T}")
+    wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
+    _beam_forward_wl(wl, beam_experts, sorted({0, T // 2, T - 1}))
