@@ -33,7 +33,10 @@ Readings where the pages are silent (each one is repeated where it is used):
 * a group of a single expert scores that expert alone (top-2 of one value);
 * SwiGLU is silu(x W_gate^T) * (x W_up^T), followed by W_down, with no
   biases, weights in the [out, in] layout;
-* no normalisation epsilon, no capacity limit, no token dropping.
+* no normalisation epsilon, no capacity limit, no token dropping;
+* an optional selection-only per-expert bias (DeepSeek-V3 scheme, which the
+  blog's MoE section names; the pages show no such vector in use) is added to
+  the scores for ranking groups and choosing experts, never for the weights.
 
 All arithmetic is float64 on float64 copies of the given (bf16-rounded or
 fp32) inputs, except :func:`select_fp32`, which follows a fixed FP32
@@ -122,26 +125,41 @@ def normalised_weights(S, ids, routed_scaling):
     return sel / sel.sum(axis=1, keepdims=True) * routed_scaling
 
 
-def route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling):
+def selection_values(S, select_bias=None):
+    """C = S + b: the values groups and experts are ranked by.
+
+    With no bias C = S.  A selection-only bias (the DeepSeek-V3 scheme the
+    blog's MoE section names) moves the choice, never the weights, which stay
+    the normalised unbiased scores.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    if select_bias is None:
+        return S
+    return S + np.asarray(select_bias, dtype=np.float64)[None, :]
+
+
+def route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling, select_bias=None):
     """Router + group-limited selection + weights, all FP64.
 
-    Returns (ids [T,K] int32, w [T,K] f64, S [T,E] f64, GS [T,G] f64).
+    Returns (ids [T,K] int32, w [T,K] f64, S [T,E] f64, GS [T,G] f64); GS is
+    taken over the selection values (S, or S + select_bias).
     """
     S = sigmoid(router_logits(x, w_router, logit_bias))
-    GS = group_scores(S, num_groups)
-    ids = select_experts(S, kept_groups(GS, topk_groups), topk)
+    C = selection_values(S, select_bias)
+    GS = group_scores(C, num_groups)
+    ids = select_experts(C, kept_groups(GS, topk_groups), topk)
     w = normalised_weights(S, ids, routed_scaling)
     return ids, w, S, GS
 
 
-def route_margins(S, num_groups, topk_groups, topk):
+def route_margins(S, num_groups, topk_groups, topk, select_bias=None):
     """Per-token distance from a routing decision flip, in FP64.
 
-    m_t = min(GS_(TG) - GS_(TG+1), S_(K) - S_(K+1) over the kept groups'
-    candidates), with (j) the j-th largest.  A missing (TG+1)-th group or
-    (K+1)-th candidate contributes +inf.
+    m_t = min(GS_(TG) - GS_(TG+1), C_(K) - C_(K+1) over the kept groups'
+    candidates), with (j) the j-th largest and C the selection values.  A
+    missing (TG+1)-th group or (K+1)-th candidate contributes +inf.
     """
-    S = np.asarray(S, dtype=np.float64)
+    S = selection_values(S, select_bias)
     T, E = S.shape
     GS = group_scores(S, num_groups)
     mask = kept_groups(GS, topk_groups)
@@ -157,14 +175,16 @@ def route_margins(S, num_groups, topk_groups, topk):
     return m
 
 
-def select_fp32(scores, num_groups, topk_groups, topk, routed_scaling):
+def select_fp32(scores, num_groups, topk_groups, topk, routed_scaling, select_bias=None):
     """Selection on caller-supplied FP32 scores with a fixed FP32 evaluation order.
 
     Same rule as :func:`route` after the sigmoid, but every floating-point
     value that decides or forms an output is an IEEE FP32 result:
 
-    * GS = fl32(first + second) of the group's two largest scores;
-    * sum = fl32 running sum of the selected scores in output order
+    * C = fl32(S + b) with a selection bias b, else C = S;
+    * GS = fl32(first + second) of the group's two largest values of C;
+    * ids: the K largest C among the kept groups, C descending, id ascending;
+    * sum = fl32 running sum of the selected unbiased scores in output order
       (((S_0 + S_1) + S_2) + ...);
     * w_k = fl32(fl32(S_k / sum) * fl32(routed_scaling)).
 
@@ -173,6 +193,7 @@ def select_fp32(scores, num_groups, topk_groups, topk, routed_scaling):
     """
     S = np.asarray(scores, dtype=np.float32)
     T, E = S.shape
+    C = S if select_bias is None else (S + np.asarray(select_bias, dtype=np.float32)[None, :]).astype(np.float32)
     gs = E // num_groups
     scale = np.float32(routed_scaling)
     ids = np.empty((T, topk), dtype=np.int32)
@@ -180,12 +201,12 @@ def select_fp32(scores, num_groups, topk_groups, topk, routed_scaling):
     for t in range(T):
         GS = np.empty(num_groups, dtype=np.float32)
         for g in range(num_groups):
-            blk = S[t, g * gs:(g + 1) * gs]
+            blk = C[t, g * gs:(g + 1) * gs]
             order = _ranked(blk)
             GS[g] = blk[order[0]] + (blk[order[1]] if gs >= 2 else np.float32(0.0))
         keep = _ranked(GS)[:topk_groups]
         cand = np.concatenate([np.arange(g * gs, (g + 1) * gs) for g in sorted(keep)])
-        order = np.lexsort((cand, -S[t, cand]))
+        order = np.lexsort((cand, -C[t, cand]))
         sel = cand[order[:topk]]
         ids[t] = sel
         total = np.float32(0.0)
@@ -260,22 +281,22 @@ def expert_outputs(x, ids, expert_weights):
 
 
 def moe_forward(x, w_router, logit_bias, expert_weights, num_groups, topk_groups, topk,
-                routed_scaling):
+                routed_scaling, select_bias=None):
     """Whole block for the given token rows: route, dispatch, experts, combine.
 
     Routing is per token, so any subset of a batch's rows may be passed; the
     dispatch by-products then describe that subset.  Returns a dict with ids,
     w, S, GS, counts, offsets, slots and out [T, H] (FP64).
     """
-    ids, w, S, GS = route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling)
+    ids, w, S, GS = route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling, select_bias)
     counts, offsets, slots = dispatch(ids, np.asarray(w_router).shape[0])
     y = expert_outputs(x, ids, expert_weights)
     out = combine(y, w)
     return dict(ids=ids, w=w, S=S, GS=GS, counts=counts, offsets=offsets, slots=slots, out=out)
 
 
-def route_only(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling):
+def route_only(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling, select_bias=None):
     """Router, selection and dispatch, without the experts."""
-    ids, w, S, GS = route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling)
+    ids, w, S, GS = route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling, select_bias)
     counts, offsets, slots = dispatch(ids, w_router.shape[0])
     return dict(ids=ids, w=w, S=S, GS=GS, counts=counts, offsets=offsets, slots=slots)

@@ -121,6 +121,86 @@ def test_sigmoid_closed_forms():
 
 
 # --------------------------------------------------------------------------
+# selection-only bias (DeepSeek-V3 scheme): moves the choice, not the weights
+# --------------------------------------------------------------------------
+def _bias_example():
+    h = _golden("routing_selection_bias_example.json")
+    return h, np.array(h["scores"]), np.array(h["selection_bias"])
+
+
+def test_selection_bias_hand_example():
+    h, s, b = _bias_example()
+    E = h["num_experts"]
+    x = np.array([[1.0, 0.0]])
+    w_r = np.zeros((E, 2))
+    w_r[:, 0] = [_logit(a) for a in s]
+    ids, w, S, GS = orc.route(x, w_r, None, h["num_groups"], h["topk_groups"], h["topk"], h["routed_scaling"],
+                              select_bias=b)
+    np.testing.assert_allclose(S[0], s, rtol=0, atol=1e-14)   # scores stay unbiased
+    np.testing.assert_allclose(GS[0], h["expected_group_scores"], rtol=0, atol=1e-14)
+    assert ids[0].tolist() == h["expected_ids"]
+    np.testing.assert_allclose(w[0], h["expected_weights"], rtol=0, atol=1e-14)
+    # without the bias: the plain hand example's answer
+    ids0, _, _, _ = orc.route(x, w_r, None, h["num_groups"], h["topk_groups"], h["topk"], h["routed_scaling"])
+    assert ids0[0].tolist() == _golden("routing_hand_example.json")["expected_ids"]
+
+
+def test_selection_bias_hand_example_fp32_mode():
+    h, s, b = _bias_example()
+    ids, w = orc.select_fp32(s.astype(np.float32)[None, :], h["num_groups"], h["topk_groups"], h["topk"],
+                             h["routed_scaling"], select_bias=b.astype(np.float32))
+    assert ids[0].tolist() == h["expected_ids"]
+    np.testing.assert_allclose(w[0], h["expected_weights"], rtol=0, atol=3e-7)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_selection_bias_matches_enumeration(seed):
+    # the choice is the dominant one under the biased values; the weights keep the
+    # ratios of the unbiased scores and sum to the scale
+    rng = np.random.default_rng(1000 + seed)
+    G, TG, K, E = 4, 2, 4, 16
+    S = rng.random((1, E))
+    b = rng.normal(0.0, 0.3, E)
+    if seed % 4 == 1:
+        b = np.round(b * 4) / 4  # coarse: ties among the biased values
+        S = np.round(S * 4) / 4
+    ids, w, _, _ = orc.route(np.array([[1.0]]), np.array([[_logit(a)] for a in np.clip(S[0], 1e-9, 1 - 1e-9)]),
+                             None, G, TG, K, 2.5, select_bias=b)
+    Sx = np.clip(S[0], 1e-9, 1 - 1e-9)
+    want, _ = _brute_select(Sx + b, G, TG, K)
+    assert sorted(ids[0].tolist()) == want
+    assert abs(w[0].sum() - 2.5) < 1e-12
+    for k in range(1, K):
+        assert abs(w[0, k] / w[0, 0] - Sx[ids[0, k]] / Sx[ids[0, 0]]) < 1e-12
+    ids32, w32 = orc.select_fp32(Sx.astype(np.float32)[None, :], G, TG, K, 2.5, select_bias=b.astype(np.float32))
+    want32, _ = _brute_select((Sx.astype(np.float32) + b.astype(np.float32)).astype(np.float32), G, TG, K)
+    assert sorted(ids32[0].tolist()) == want32
+
+
+def test_selection_bias_closed_forms():
+    G, TG, K, E = 4, 2, 4, 16
+    # equal scores: the bias alone decides the choice, and every weight is scale / K
+    S = np.full((1, E), 0.3)
+    b = np.zeros(E)
+    b[[13, 2, 14, 3]] = [0.4, 0.3, 0.2, 0.1]  # groups 0 and 3 win; experts by bias
+    ids, w = orc.select_fp32(S.astype(np.float32), G, TG, K, 2.5, select_bias=b.astype(np.float32))
+    assert ids[0].tolist() == [13, 2, 14, 3]
+    np.testing.assert_allclose(w[0], [2.5 / K] * K, rtol=0, atol=1e-7)
+    # a zero bias changes nothing; a bias constant over all experts changes no choice
+    rng = np.random.default_rng(7)
+    S = rng.random((5, E))
+    x = np.eye(5)
+    w_r = np.array([[_logit(a) for a in S[:, e]] for e in range(E)])
+    base = orc.route(x, w_r, None, G, TG, K, 2.5)
+    for bb in (np.zeros(E), np.full(E, 0.7)):
+        r = orc.route(x, w_r, None, G, TG, K, 2.5, select_bias=bb)
+        assert np.array_equal(r[0], base[0])
+        np.testing.assert_allclose(r[1], base[1], rtol=0, atol=1e-12)
+    m = orc.route_margins(S, G, TG, K, select_bias=np.full(E, 0.7))
+    np.testing.assert_allclose(m, orc.route_margins(S, G, TG, K), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # routing: exhaustive enumeration on tiny inputs
 # --------------------------------------------------------------------------
 def _brute_select(S, G, TG, K):
