@@ -60,13 +60,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.beam_moe_workspace_bytes.restype = sz
     lib.beam_moe_status_str.argtypes = [ctypes.c_int]
     lib.beam_moe_status_str.restype = ctypes.c_char_p
-    lib.beam_moe_route.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.beam_moe_route.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.beam_moe_route.restype = ctypes.c_int
-    lib.beam_moe_select.argtypes = [pd, i32, vp, vp, vp, vp]
+    lib.beam_moe_select.argtypes = [pd, i32, vp, vp, vp, vp, vp]
     lib.beam_moe_select.restype = ctypes.c_int
     lib.beam_moe_dispatch.argtypes = [pd, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.beam_moe_dispatch.restype = ctypes.c_int
-    lib.beam_moe_forward.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.beam_moe_forward.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.beam_moe_forward.restype = ctypes.c_int
     lib.beam_moe_timing_enable.argtypes = [ctypes.c_int]
     lib.beam_moe_timing_enable.restype = ctypes.c_int
@@ -138,7 +138,8 @@ def workspace(dims: Dims, T: int, device="cuda") -> torch.Tensor:
 
 
 def beam_moe_route(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor] = None,
-                   *, want_scores: bool = False, ws: Optional[torch.Tensor] = None, stream=None):
+                   *, select_bias: Optional[torch.Tensor] = None, want_scores: bool = False,
+                   ws: Optional[torch.Tensor] = None, stream=None):
     """Router + group-limited top-k. Returns (ids [T,K] int32, w [T,K] f32, scores [T,E] f32 or None)."""
     T = x.shape[0]
     H, E, K = dims.hidden, dims.num_experts, dims.topk
@@ -146,6 +147,8 @@ def beam_moe_route(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_bi
     _req(w_router, "w_router", torch.float32, (E, H))
     if logit_bias is not None:
         _req(logit_bias, "logit_bias", torch.float32, (E,))
+    if select_bias is not None:
+        _req(select_bias, "select_bias", torch.float32, (E,))
     dev = x.device
     ids = torch.empty((T, K), dtype=torch.int32, device=dev)
     w = torch.empty((T, K), dtype=torch.float32, device=dev)
@@ -153,20 +156,24 @@ def beam_moe_route(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_bi
     if ws is None:
         ws = workspace(dims, T, dev)
     cd = _cdims(dims)
-    st = load_library().beam_moe_route(ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(ids),
-                                       _ptr(w), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream))
+    st = load_library().beam_moe_route(ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                                       _ptr(select_bias), _ptr(ids), _ptr(w), _ptr(scores), _ptr(ws), ws.numel(),
+                                       _stream(stream))
     _check(st, "beam_moe_route")
     return ids, w, scores
 
 
-def beam_moe_select(dims: Dims, scores: torch.Tensor, *, stream=None):
+def beam_moe_select(dims: Dims, scores: torch.Tensor, *, select_bias: Optional[torch.Tensor] = None, stream=None):
     """Selection on supplied post-sigmoid FP32 scores [T,E]. Returns (ids, w)."""
     T = scores.shape[0]
     _req(scores, "scores", torch.float32, (T, dims.num_experts))
+    if select_bias is not None:
+        _req(select_bias, "select_bias", torch.float32, (dims.num_experts,))
     ids = torch.empty((T, dims.topk), dtype=torch.int32, device=scores.device)
     w = torch.empty((T, dims.topk), dtype=torch.float32, device=scores.device)
     cd = _cdims(dims)
-    st = load_library().beam_moe_select(ctypes.byref(cd), T, _ptr(scores), _ptr(ids), _ptr(w), _stream(stream))
+    st = load_library().beam_moe_select(ctypes.byref(cd), T, _ptr(scores), _ptr(select_bias), _ptr(ids), _ptr(w),
+                                        _stream(stream))
     _check(st, "beam_moe_select")
     return ids, w
 
@@ -206,7 +213,8 @@ class ForwardBuffers:
 
 def beam_moe_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],
                      w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, *,
-                     bufs: Optional[ForwardBuffers] = None, stream=None) -> ForwardBuffers:
+                     select_bias: Optional[torch.Tensor] = None, bufs: Optional[ForwardBuffers] = None,
+                     stream=None) -> ForwardBuffers:
     """The whole block. Returns the ForwardBuffers holding out and the routing by-products."""
     T = x.shape[0]
     H, I, E = dims.hidden, dims.intermediate, dims.num_experts
@@ -214,6 +222,8 @@ def beam_moe_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_
     _req(w_router, "w_router", torch.float32, (E, H))
     if logit_bias is not None:
         _req(logit_bias, "logit_bias", torch.float32, (E,))
+    if select_bias is not None:
+        _req(select_bias, "select_bias", torch.float32, (E,))
     _req(w_gate, "w_gate", torch.bfloat16, (E, I, H))
     _req(w_up, "w_up", torch.bfloat16, (E, I, H))
     _req(w_down, "w_down", torch.bfloat16, (E, H, I))
@@ -223,7 +233,8 @@ def beam_moe_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_
         raise ValueError("buffers were sized for another T")
     cd = _cdims(dims)
     st = load_library().beam_moe_forward(
-        ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down),
         _ptr(bufs.out), _ptr(bufs.ids), _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets), _ptr(bufs.slots),
         _ptr(bufs.ws), bufs.ws.numel(), _stream(stream))
     _check(st, "beam_moe_forward")

@@ -16,8 +16,9 @@ namespace beam {
 struct Tile;
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part, int T, int H, int E, int splits,
                                 int k_per_split, hipStream_t st);
-hipError_t launch_select(const float* src, int splits, bool from_partials, const float* bias, float* scores_out,
-                         int T, int E, int G, int TG, int K, float scale, int32_t* ids, float* w, hipStream_t st);
+hipError_t launch_select(const float* src, int splits, bool from_partials, const float* bias,
+                         const float* select_bias, float* scores_out, int T, int E, int G, int TG, int K, float scale,
+                         int32_t* ids, float* w, hipStream_t st);
 int dispatch_units(int n);
 hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_slots, Tile* tiles, int mt, int32_t* ntiles, hipStream_t st);
@@ -219,12 +220,13 @@ const char* beam_moe_status_str(int status) {
 }
 
 int beam_moe_route(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
-                   const float* logit_bias, int32_t* topk_ids, float* topk_w, float* scores_out, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   const float* logit_bias, const float* select_bias, int32_t* topk_ids, float* topk_w,
+                   float* scores_out, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(d, T);
   if (rc != BEAM_MOE_OK || T == 0) return rc;
   if ((rc = check_ptrs({x_bf16, w_router, topk_ids, topk_w})) != BEAM_MOE_OK) return rc;
-  if ((logit_bias && !aligned16(logit_bias)) || (scores_out && !aligned16(scores_out)))
+  if ((logit_bias && !aligned16(logit_bias)) || (select_bias && !aligned16(select_bias)) ||
+      (scores_out && !aligned16(scores_out)))
     return BEAM_MOE_ERR_INVALID_ARG;
   Plan p;
   make_plan(d, T, &p);
@@ -234,17 +236,19 @@ int beam_moe_route(const beam_moe_dims* d, int32_t T, const void* x_bf16, const 
   rc = hip_status(beam::launch_router_logits(static_cast<const uint16_t*>(x_bf16), w_router, part, T, p.H, p.E,
                                              p.splits, p.k_per_split, st));
   if (rc != BEAM_MOE_OK) return rc;
-  return hip_status(beam::launch_select(part, p.splits, true, logit_bias, scores_out, T, p.E, d->num_groups,
-                                        d->topk_groups, d->topk, d->routed_scaling, topk_ids, topk_w, st));
+  return hip_status(beam::launch_select(part, p.splits, true, logit_bias, select_bias, scores_out, T, p.E,
+                                        d->num_groups, d->topk_groups, d->topk, d->routed_scaling, topk_ids, topk_w,
+                                        st));
 }
 
-int beam_moe_select(const beam_moe_dims* d, int32_t T, const float* scores, int32_t* topk_ids, float* topk_w,
-                    void* stream) {
+int beam_moe_select(const beam_moe_dims* d, int32_t T, const float* scores, const float* select_bias,
+                    int32_t* topk_ids, float* topk_w, void* stream) {
   int rc = check_common(d, T);
   if (rc != BEAM_MOE_OK || T == 0) return rc;
   if ((rc = check_ptrs({scores, topk_ids, topk_w})) != BEAM_MOE_OK) return rc;
-  return hip_status(beam::launch_select(scores, 1, false, nullptr, nullptr, T, d->num_experts, d->num_groups,
-                                        d->topk_groups, d->topk, d->routed_scaling, topk_ids, topk_w,
+  if (select_bias && !aligned16(select_bias)) return BEAM_MOE_ERR_INVALID_ARG;
+  return hip_status(beam::launch_select(scores, 1, false, nullptr, select_bias, nullptr, T, d->num_experts,
+                                        d->num_groups, d->topk_groups, d->topk, d->routed_scaling, topk_ids, topk_w,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -262,15 +266,16 @@ int beam_moe_dispatch(const beam_moe_dims* d, int32_t T, const int32_t* topk_ids
 }
 
 int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
-                     const float* logit_bias, const void* w_gate, const void* w_up, const void* w_down, float* out,
-                     int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
-                     int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream) {
+                     const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
+                     const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(d, T);
   if (rc != BEAM_MOE_OK || T == 0) return rc;
   if ((rc = check_ptrs({x_bf16, w_router, w_gate, w_up, w_down, out, topk_ids, topk_w, expert_counts,
                         expert_offsets, sorted_slots})) != BEAM_MOE_OK)
     return rc;
-  if (logit_bias && !aligned16(logit_bias)) return BEAM_MOE_ERR_INVALID_ARG;
+  if ((logit_bias && !aligned16(logit_bias)) || (select_bias && !aligned16(select_bias)))
+    return BEAM_MOE_ERR_INVALID_ARG;
   Plan p;
   make_plan(d, T, &p);
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
@@ -295,8 +300,8 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   BEAM_TRY(mark(ev, kStRouter, st));
   BEAM_TRY(beam::launch_router_logits(x, w_router, part, T, p.H, p.E, p.splits, p.k_per_split, st));
   BEAM_TRY(mark(ev, kStSelect, st));
-  BEAM_TRY(beam::launch_select(part, p.splits, true, logit_bias, nullptr, T, p.E, d->num_groups, d->topk_groups,
-                               d->topk, d->routed_scaling, topk_ids, topk_w, st));
+  BEAM_TRY(beam::launch_select(part, p.splits, true, logit_bias, select_bias, nullptr, T, p.E, d->num_groups,
+                               d->topk_groups, d->topk, d->routed_scaling, topk_ids, topk_w, st));
   BEAM_TRY(mark(ev, kStDispatch, st));
   BEAM_TRY(beam::launch_dispatch(topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), expert_counts, expert_offsets,
                                  sorted_slots, tiles, p.mt, ntiles, st));

@@ -17,7 +17,9 @@
 //       The K dimension may be split across workgroups; partial sums land in
 //       workspace and are added in a fixed order by the select kernel.
 //   select_kernel  one wave per token: partial sums + bias + sigmoid, then the
-//       group top-2 sums, the kept groups and K rounds of a wave-wide argmax.
+//       group top-2 sums, the kept groups and K rounds of a wave-wide argmax,
+//       on the scores or, with a selection-only bias, on score + bias (the
+//       weights always from the unbiased scores).
 #include "common.h"
 
 namespace beam {
@@ -137,10 +139,14 @@ __device__ __forceinline__ bool beats(float v, int i, float ov, int oi) { return
 
 // grid: ceil(T/4); block 256: one wave per token.
 // src: partial logits [splits][T][E] (from_partials) or post-sigmoid scores [T][E].
+// sel_bias (optional): selection-only bias; groups and experts are ranked by
+// c = fl32(s + sel_bias[e]), the weights use the unbiased s.
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ src, int splits, bool from_partials,
-                                                     const float* __restrict__ bias, float* __restrict__ scores_out,
-                                                     int T, int E, int G, int TG, int K, float scale,
-                                                     int32_t* __restrict__ ids, float* __restrict__ wout) {
+                                                     const float* __restrict__ bias,
+                                                     const float* __restrict__ sel_bias,
+                                                     float* __restrict__ scores_out, int T, int E, int G, int TG,
+                                                     int K, float scale, int32_t* __restrict__ ids,
+                                                     float* __restrict__ wout) {
 #pragma clang fp contract(off)
   __shared__ float s_sc[4][256];
   __shared__ float s_gs[4][64];
@@ -150,12 +156,14 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
   const bool active = t < T;
   const int gsz = E / G;
 
-  float v[4];
+  float v[4];  // unbiased scores
+  float c[4];  // selection values
   bool valid[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
     v[j] = 0.f;
+    c[j] = 0.f;
     if (active && e < E) {
       if (from_partials) {
         // split-K partial logits, added in ascending split order; loads are
@@ -178,12 +186,13 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
       } else {
         v[j] = src[(size_t)t * E + e];
       }
-      s_sc[wave][e] = v[j];
+      c[j] = sel_bias ? v[j] + sel_bias[e] : v[j];
+      s_sc[wave][e] = c[j];
     }
   }
   __syncthreads();
 
-  // group score: sum of the two largest scores of the group (one lane per group)
+  // group score: sum of the two largest selection values of the group (one lane per group)
   if (active && lane < G) {
     float m1 = -INFINITY, m2 = -INFINITY;
     const float* g = &s_sc[wave][lane * gsz];
@@ -216,18 +225,21 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     valid[j] = e < E && ((kept >> (e / gsz)) & 1ull);
   }
 
+  // K rounds of a wave-wide argmax of (c, e); the winner's unbiased score bs
+  // travels with it for the weights
   float total = 0.f;
   float my_v = 0.f;
   int my_e = 0;
   for (int k = 0; k < K; ++k) {
-    float bv = 0.f;
+    float bv = 0.f, bs = 0.f;
     int be = 0x7fffffff;
     bool bok = false;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      if (valid[j] && (!bok || beats(v[j], e, bv, be))) {
-        bv = v[j];
+      if (valid[j] && (!bok || beats(c[j], e, bv, be))) {
+        bv = c[j];
+        bs = v[j];
         be = e;
         bok = true;
       }
@@ -235,10 +247,12 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
+      const float os = __shfl_xor(bs, off);
       const int oe = __shfl_xor(be, off);
       const int ook = __shfl_xor(int(bok), off);
       if (ook && (!bok || beats(ov, oe, bv, be))) {
         bv = ov;
+        bs = os;
         be = oe;
         bok = true;
       }
@@ -249,9 +263,9 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
       for (int j = 0; j < 4; ++j)
         if (be == lane + 64 * j) valid[j] = false;
     }
-    total = total + bv;
+    total = total + bs;
     if (lane == k) {
-      my_v = bv;
+      my_v = bs;
       my_e = be;
     }
   }
@@ -272,11 +286,12 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, float* part,
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* src, int splits, bool from_partials, const float* bias, float* scores_out,
-                         int T, int E, int G, int TG, int K, float scale, int32_t* ids, float* w, hipStream_t st) {
+hipError_t launch_select(const float* src, int splits, bool from_partials, const float* bias,
+                         const float* select_bias, float* scores_out, int T, int E, int G, int TG, int K, float scale,
+                         int32_t* ids, float* w, hipStream_t st) {
   dim3 grid((T + 3) / 4);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, st, src, splits, from_partials, bias, scores_out, T, E, G,
-                     TG, K, scale, ids, w);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, st, src, splits, from_partials, bias, select_bias, scores_out,
+                     T, E, G, TG, K, scale, ids, w);
   return hipGetLastError();
 }
 

@@ -85,24 +85,32 @@ size_t beam_moe_workspace_bytes(const beam_moe_dims* dims, int32_t T);
  *   x_bf16      [T, H]  bf16 hidden states
  *   w_router    [E, H]  fp32 router weight
  *   logit_bias  [E]     fp32, added to the logit before the sigmoid; NULL = none
+ *   select_bias [E]     fp32 selection-only bias, NULL = none: groups and experts
+ *                       are ranked by c = fl32(s + select_bias[e]) while the
+ *                       weights stay the normalised unbiased scores s (the
+ *                       DeepSeek-V3 scheme the post's mixture-of-experts
+ *                       section names; the pages show no such vector in use)
  *   topk_ids    [T, K]  int32 out
  *   topk_w      [T, K]  fp32 out: normalised weights times routed_scaling
  *   scores_out  [T, E]  fp32 out, post-sigmoid scores; NULL = not written
  *   ws, ws_bytes        workspace of at least beam_moe_workspace_bytes(dims, T)
  * The logits are accumulated in FP32 (bf16 x times fp32 W_r, exact products). */
 int beam_moe_route(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
-                   const float* logit_bias, int32_t* topk_ids, float* topk_w, float* scores_out, void* ws,
-                   size_t ws_bytes, void* stream);
+                   const float* logit_bias, const float* select_bias, int32_t* topk_ids, float* topk_w,
+                   float* scores_out, void* ws, size_t ws_bytes, void* stream);
 
-/* Steps 2-3 on caller-supplied post-sigmoid FP32 scores [T, E].
- * Fixed FP32 evaluation order, so results are reproducible bit for bit by any
- * implementation that follows it:
- *   group score      = fl32(s_first + s_second) of the group's two largest;
- *   sum              = fl32 running sum of the K selected scores in output order;
+/* Steps 2-3 on caller-supplied post-sigmoid FP32 scores [T, E] (select_bias as
+ * in beam_moe_route, NULL = none).  Fixed FP32 evaluation order, so results are
+ * reproducible bit for bit by any implementation that follows it:
+ *   selection value  c = fl32(s + select_bias[e]), or c = s;
+ *   group score      = fl32(c_first + c_second) of the group's two largest;
+ *   topk_ids[t,:]    = the K largest c among the kept groups, c descending,
+ *                      ties to the lower id;
+ *   sum              = fl32 running sum of the K selected s in output order;
  *   topk_w[t,k]      = fl32(fl32(s_k / sum) * routed_scaling)   (IEEE division).
  * Needs no workspace. */
-int beam_moe_select(const beam_moe_dims* dims, int32_t T, const float* scores, int32_t* topk_ids, float* topk_w,
-                    void* stream);
+int beam_moe_select(const beam_moe_dims* dims, int32_t T, const float* scores, const float* select_bias,
+                    int32_t* topk_ids, float* topk_w, void* stream);
 
 /* Counting-sort dispatch of the T*K (token, slot) pairs by expert.
  *   topk_ids        [T, K]  int32 in [0, E) (ids outside it are skipped and
@@ -115,6 +123,7 @@ int beam_moe_dispatch(const beam_moe_dims* dims, int32_t T, const int32_t* topk_
                       int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
 /* The whole block (steps 1-5).
+ *   x_bf16, w_router, logit_bias, select_bias: as in beam_moe_route
  *   w_gate, w_up  [E, I, H] bf16;  w_down [E, H, I] bf16
  *   out           [T, H] fp32 out
  *   topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots: as above,
@@ -129,9 +138,9 @@ int beam_moe_dispatch(const beam_moe_dims* dims, int32_t T, const int32_t* topk_
  * weighted sum are FP32, summed over k in ascending k order.
  * Supported intermediate sizes additionally satisfy intermediate <= 32768. */
 int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
-                     const float* logit_bias, const void* w_gate, const void* w_up, const void* w_down, float* out,
-                     int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
-                     int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
+                     const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
+                     const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
 /* Diagnostics: device time of the stages of beam_moe_forward.
  * beam_moe_timing_enable(1) makes later beam_moe_forward calls record HIP

@@ -30,12 +30,13 @@ def f64(t: torch.Tensor) -> np.ndarray:
 class Problem:
     """Inputs of one workload, generated on the device with the shared generator."""
 
-    def __init__(self, wl: synth.Workload, device="cuda", experts=None):
+    def __init__(self, wl: synth.Workload, device="cuda", experts=None, select_bias=None):
         self.wl = wl
         self.dims = wl.dims
         self.x = synth.make_x(wl, device)
         self.wr = synth.make_router(wl, device)
         self.bias = synth.make_bias(wl, device)
+        self.select_bias = select_bias  # fp32 [E] device tensor or None
         if experts is None and not wl.router_only:
             experts = synth.make_experts(wl, device)
         self.wg, self.wu, self.wd = experts if experts is not None else (None, None, None)
@@ -47,12 +48,15 @@ class Problem:
         return self._cache[e]
 
     def route_oracle(self, tokens=None):
+        """(X, ids, w, C, GS, margins) of the oracle; C = the selection values (S, or S + select_bias)."""
         d = self.dims
         X = f64(self.x if tokens is None else self.x[torch.as_tensor(tokens, device=self.x.device)])
         bias = None if self.bias is None else f64(self.bias)
-        ids, w, S, GS = orc.route(X, f64(self.wr), bias, d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
-        m = orc.route_margins(S, d.num_groups, d.topk_groups, d.topk)
-        return X, ids, w, S, GS, m
+        sb = None if self.select_bias is None else f64(self.select_bias)
+        ids, w, S, GS = orc.route(X, f64(self.wr), bias, d.num_groups, d.topk_groups, d.topk, d.routed_scaling,
+                                  select_bias=sb)
+        m = orc.route_margins(S, d.num_groups, d.topk_groups, d.topk, select_bias=sb)
+        return X, ids, w, orc.selection_values(S, sb), GS, m
 
 
 def valid_near_tie(ids_gpu_row, S_row, d: synth.Dims, slack=2 * MARGIN) -> bool:

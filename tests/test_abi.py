@@ -74,35 +74,38 @@ def test_unsupported_dims(bad):
     lib = binding.load_library()
     cd = binding._cdims(bad)
     assert lib.beam_moe_workspace_bytes(ctypes.byref(cd), 64) == binding.SIZE_MAX
-    st = lib.beam_moe_forward(ctypes.byref(cd), 64, *([FAKE] * 13), 1 << 40, None)
+    st = lib.beam_moe_forward(ctypes.byref(cd), 64, *([FAKE] * 14), 1 << 40, None)
     assert st == binding.BEAM_MOE_ERR_UNSUPPORTED
-    st = lib.beam_moe_select(ctypes.byref(cd), 64, FAKE, FAKE, FAKE, None)
+    st = lib.beam_moe_select(ctypes.byref(cd), 64, FAKE, None, FAKE, FAKE, None)
     assert st == binding.BEAM_MOE_ERR_UNSUPPORTED
 
 
 def test_invalid_arguments_rejected_before_launch():
     lib = binding.load_library()
     cd = binding._cdims(BEAM)
-    ok = [FAKE] * 13
+    ok = [FAKE] * 14
     # negative T
     assert lib.beam_moe_forward(ctypes.byref(cd), -1, *ok, 1 << 40, None) == binding.BEAM_MOE_ERR_INVALID_ARG
     # each required pointer of forward: NULL and misaligned
-    required = [0, 1, 3, 4, 5, 6, 7, 8, 9, 10, 11]   # x, w_router, gate, up, down, out, ids, w, counts, offsets, slots
+    required = [0, 1, 4, 5, 6, 7, 8, 9, 10, 11, 12]  # x, w_router, gate, up, down, out, ids, w, counts, offsets, slots
     for i in required:
         args = list(ok)
         args[i] = None
         assert lib.beam_moe_forward(ctypes.byref(cd), 64, *args, 1 << 40, None) == binding.BEAM_MOE_ERR_INVALID_ARG
         args[i] = ctypes.c_void_p((1 << 20) + 8)
         assert lib.beam_moe_forward(ctypes.byref(cd), 64, *args, 1 << 40, None) == binding.BEAM_MOE_ERR_INVALID_ARG
-    # the optional bias may be NULL but not misaligned
-    args = list(ok)
-    args[2] = ctypes.c_void_p((1 << 20) + 4)
-    assert lib.beam_moe_forward(ctypes.byref(cd), 64, *args, 1 << 40, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    # the optional biases may be NULL but not misaligned
+    for i in (2, 3):
+        args = list(ok)
+        args[i] = ctypes.c_void_p((1 << 20) + 4)
+        assert lib.beam_moe_forward(ctypes.byref(cd), 64, *args, 1 << 40, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert lib.beam_moe_select(ctypes.byref(cd), 4, FAKE, ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE, None) == \
+        binding.BEAM_MOE_ERR_INVALID_ARG
     # select / dispatch / route null pointers
-    assert lib.beam_moe_select(ctypes.byref(cd), 4, None, FAKE, FAKE, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert lib.beam_moe_select(ctypes.byref(cd), 4, None, None, FAKE, FAKE, None) == binding.BEAM_MOE_ERR_INVALID_ARG
     assert lib.beam_moe_dispatch(ctypes.byref(cd), 4, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == \
         binding.BEAM_MOE_ERR_INVALID_ARG
-    assert lib.beam_moe_route(ctypes.byref(cd), 4, None, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 40, None) == \
+    assert lib.beam_moe_route(ctypes.byref(cd), 4, None, FAKE, None, None, FAKE, FAKE, None, FAKE, 1 << 40, None) == \
         binding.BEAM_MOE_ERR_INVALID_ARG
     assert lib.beam_moe_forward(None, 4, *ok, 1 << 40, None) == binding.BEAM_MOE_ERR_INVALID_ARG
 
@@ -111,21 +114,21 @@ def test_short_or_missing_workspace_rejected():
     lib = binding.load_library()
     cd = binding._cdims(BEAM)
     need = lib.beam_moe_workspace_bytes(ctypes.byref(cd), 64)
-    ok = [FAKE] * 13
+    ok = [FAKE] * 14
     assert lib.beam_moe_forward(ctypes.byref(cd), 64, *ok, need - 1, None) == binding.BEAM_MOE_ERR_WORKSPACE
     args = list(ok)
-    args[12] = None
+    args[13] = None
     assert lib.beam_moe_forward(ctypes.byref(cd), 64, *args, need, None) == binding.BEAM_MOE_ERR_WORKSPACE
     assert lib.beam_moe_dispatch(ctypes.byref(cd), 64, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
         binding.BEAM_MOE_ERR_WORKSPACE
-    assert lib.beam_moe_route(ctypes.byref(cd), 64, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, need - 1, None) == \
-        binding.BEAM_MOE_ERR_WORKSPACE
+    assert lib.beam_moe_route(ctypes.byref(cd), 64, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, need - 1,
+                              None) == binding.BEAM_MOE_ERR_WORKSPACE
 
 
 def test_zero_tokens_is_a_no_op():
     lib = binding.load_library()
     cd = binding._cdims(TINY)
-    assert lib.beam_moe_forward(ctypes.byref(cd), 0, *([None] * 13), 0, None) == binding.BEAM_MOE_OK
-    assert lib.beam_moe_route(ctypes.byref(cd), 0, *([None] * 7), 0, None) == binding.BEAM_MOE_OK
-    assert lib.beam_moe_select(ctypes.byref(cd), 0, None, None, None, None) == binding.BEAM_MOE_OK
+    assert lib.beam_moe_forward(ctypes.byref(cd), 0, *([None] * 14), 0, None) == binding.BEAM_MOE_OK
+    assert lib.beam_moe_route(ctypes.byref(cd), 0, *([None] * 8), 0, None) == binding.BEAM_MOE_OK
+    assert lib.beam_moe_select(ctypes.byref(cd), 0, None, None, None, None, None) == binding.BEAM_MOE_OK
     assert lib.beam_moe_dispatch(ctypes.byref(cd), 0, *([None] * 5), 0, None) == binding.BEAM_MOE_OK

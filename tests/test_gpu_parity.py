@@ -275,3 +275,74 @@ def test_forward_beam_sizes(beam_experts, T):
     _announce(f"forward Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
     _beam_forward_wl(wl, beam_experts, sorted({0, T // 2, T - 1}))
+
+
+# --------------------------------------------------------------------------
+# selection-only bias: ranks groups and experts, never forms the weights
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["normal", "coarse"])
+@pytest.mark.parametrize("dims", [TINY, synth.BEAM, synth.Dims(256, 128, 64, 8, 3, 6)])
+def test_select_with_selection_bias_bit_exact(dims, kind):
+    _announce(f"select with selection bias {kind} {dims}")
+    E = dims.num_experts
+    rng = np.random.default_rng(E + (7 if kind == "coarse" else 0))
+    s = rng.random((129, E)).astype(np.float32)
+    b = rng.normal(0.0, 0.05, E).astype(np.float32)
+    if kind == "coarse":   # exact ties among the biased values
+        s = (np.round(s * 8) / 8).astype(np.float32)
+        b = (np.round(b * 16) / 16).astype(np.float32)
+    ids, w = binding.beam_moe_select(dims, torch.from_numpy(s).to(DEV), select_bias=torch.from_numpy(b).to(DEV))
+    ids_o, w_o = orc.select_fp32(s, dims.num_groups, dims.topk_groups, dims.topk, dims.routed_scaling,
+                                 select_bias=b)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.array_equal(w.cpu().numpy().view(np.int32), w_o.view(np.int32))
+
+
+def test_hand_example_selection_bias_on_gpu():
+    _announce("hand-worked selection-bias example")
+    import json
+    import os
+    h = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "routing_selection_bias_example.json")))
+    d = synth.Dims(256, 128, h["num_experts"], h["num_groups"], h["topk_groups"], h["topk"], h["routed_scaling"])
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device=DEV)
+    x[0, 0] = 1.0
+    wr = torch.zeros((16, 256), dtype=torch.float32, device=DEV)
+    wr[:, 0] = torch.tensor([math.log(a / (1 - a)) for a in h["scores"]], dtype=torch.float32)
+    sb = torch.tensor(h["selection_bias"], dtype=torch.float32, device=DEV)
+    ids, w, s = binding.beam_moe_route(d, x, wr, select_bias=sb, want_scores=True)
+    assert ids.cpu().tolist()[0] == h["expected_ids"]
+    np.testing.assert_allclose(w.cpu().numpy()[0], h["expected_weights"], rtol=0, atol=2e-6)
+    np.testing.assert_allclose(s.cpu().numpy()[0], h["scores"], rtol=0, atol=2e-7)  # scores stay unbiased
+
+
+def test_route_with_selection_bias_e2e():
+    _announce("route with selection bias, T=4096 at Beam scale")
+    wl = synth.WORKLOADS["router_dispatch"]
+    d = wl.dims
+    sb = torch.from_numpy(np.random.default_rng(5).normal(0.0, 0.05, d.num_experts).astype(np.float32)).to(DEV)
+    p = Problem(wl, DEV, select_bias=sb)
+    ids, w, _ = binding.beam_moe_route(d, p.x, p.wr, p.bias, select_bias=sb)
+    X, ids_o, w_o, C_o, GS_o, m = p.route_oracle()
+    excluded = compare_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_o, w_o, C_o, m, d)
+    print(f"  excluded near-tie tokens: {excluded} of {wl.tokens}")
+    assert excluded <= max(2, wl.tokens // 200)
+    # the bias moved the choice of a good share of tokens
+    ids0, _, _ = binding.beam_moe_route(d, p.x, p.wr, p.bias)
+    moved = (np.sort(ids.cpu().numpy(), 1) != np.sort(ids0.cpu().numpy(), 1)).any(1).mean()
+    print(f"  tokens whose experts the bias changed: {moved:.1%}")
+    assert moved > 0.05
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_stream", "mid_tiled_e256"])
+def test_forward_with_selection_bias(name):
+    _announce(f"forward {name} with selection bias")
+    wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else MID[name][0]
+    E = wl.dims.num_experts
+    sb = torch.from_numpy(np.random.default_rng(E).normal(0.0, 0.05, E).astype(np.float32)).to(DEV)
+    p = Problem(wl, DEV, select_bias=sb)
+    bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd, select_bias=sb)
+    excluded, worst = forward_parity(p, bufs)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+    out1 = bufs.out.clone()
+    binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd, select_bias=sb, bufs=bufs)
+    assert torch.equal(out1, bufs.out)
