@@ -44,6 +44,8 @@ evaluation order on purpose (see there).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 
@@ -300,3 +302,55 @@ def route_only(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_sc
     ids, w, S, GS = route(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_scaling, select_bias)
     counts, offsets, slots = dispatch(ids, w_router.shape[0])
     return dict(ids=ids, w=w, S=S, GS=GS, counts=counts, offsets=offsets, slots=slots)
+
+
+# --------------------------------------------------------------------------
+# the block as a residual sublayer (pre-norm, post-norm, scaled update)
+# --------------------------------------------------------------------------
+# Blog, section 残差流 (residual stream): the input embedding is step 1; at
+# step k a sublayer's output is added with weight 1/sqrt(k) while the stream
+# is kept with weight sqrt((k-1)/k); every sublayer is normalised before and
+# after; normalisation runs in FP32.  The pages name neither the norm's form
+# nor its weights or epsilon: read as RMSNorm, unit weights unless given,
+# eps = 1e-6.
+NORM_EPS = 1e-6
+
+
+def rms_norm(v, weight=None, eps=NORM_EPS):
+    """v / sqrt(mean(v^2) + eps) * weight, per row, FP64."""
+    v = np.asarray(v, dtype=np.float64)
+    r = v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+    return r if weight is None else r * np.asarray(weight, dtype=np.float64)
+
+
+def residual_weights(k):
+    """(stream weight, sublayer weight) of step k >= 2: (sqrt((k-1)/k), 1/sqrt(k))."""
+    return math.sqrt((k - 1) / k), 1.0 / math.sqrt(k)
+
+
+def bf16_round(v):
+    """Round to the nearest bf16 value (ties to even), returned as float64."""
+    f = np.asarray(v, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def moe_residual_step(stream, k, w_router, logit_bias, expert_weights, num_groups, topk_groups, topk,
+                      routed_scaling, select_bias=None, norm_in_weight=None, norm_out_weight=None, eps=NORM_EPS):
+    """stream' = sqrt((k-1)/k) * stream + 1/sqrt(k) * norm(MoE(bf16(norm(stream)))).
+
+    The block's input is the pre-norm of the stream rounded to bf16 (the
+    precision the block takes its hidden states in); everything else FP64.
+    Returns dict(x=bf16 input, moe=block output, out=new stream, plus the
+    routing by-products of moe_forward).
+    """
+    stream = np.asarray(stream, dtype=np.float64)
+    x = bf16_round(rms_norm(stream, norm_in_weight, eps))
+    r = moe_forward(x, w_router, logit_bias, expert_weights, num_groups, topk_groups, topk, routed_scaling,
+                    select_bias)
+    a, b = residual_weights(k)
+    r["x"] = x
+    r["moe"] = r["out"]
+    r["out"] = a * stream + b * rms_norm(r["moe"], norm_out_weight, eps)
+    return r

@@ -431,3 +431,65 @@ def test_linear_in_down_projection_and_token_permutation():
     rp = orc.moe_forward(x[perm], w_r, None, lambda e: ws[e], G, TG, K, 2.5)
     np.testing.assert_allclose(rp["out"], r["out"][perm], rtol=1e-12, atol=1e-12)
     assert np.array_equal(rp["ids"], r["ids"][perm])
+
+
+# --------------------------------------------------------------------------
+# residual sublayer: what the blog's residual-stream section fixes
+# --------------------------------------------------------------------------
+def test_residual_weights_keep_the_stream_scale():
+    # the two weights of every step have squares summing to one
+    for k in range(2, 200):
+        a, b = orc.residual_weights(k)
+        assert abs(a * a + b * b - 1.0) < 1e-15
+
+
+def test_residual_weights_equalise_after_104_additions():
+    # embedding = step 1; 104 further additions (52 layers x 2 sublayers): the embedding and
+    # every sublayer output end with the same weight, 1/sqrt(105)
+    n = 105
+    coef = np.zeros(n)        # coef[j]: weight of the term added at step j + 1 (j = 0: embedding)
+    coef[0] = 1.0
+    for k in range(2, n + 1):
+        a, b = orc.residual_weights(k)
+        coef[:k - 1] *= a
+        coef[k - 1] = b
+    np.testing.assert_allclose(coef, np.full(n, 1.0 / math.sqrt(n)), rtol=0, atol=1e-14)
+
+
+def test_rms_norm_closed_forms():
+    v = np.array([[3.0, -3.0, 3.0, -3.0], [1.0, 2.0, 2.0, 4.0]])
+    r = orc.rms_norm(v, eps=0.0)
+    np.testing.assert_allclose(r[0], [1.0, -1.0, 1.0, -1.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r[1], np.array([1.0, 2.0, 2.0, 4.0]) / math.sqrt(25.0 / 4.0), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(np.mean(orc.rms_norm(v * 7.5, eps=0.0) ** 2, axis=1), [1.0, 1.0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(orc.rms_norm(v, [2.0, 1.0, 0.5, 0.0], eps=0.0)[0], [2.0, -1.0, 0.5, 0.0], atol=1e-15)
+    # eps: a zero row stays zero; a tiny row is damped
+    np.testing.assert_allclose(orc.rms_norm(np.zeros((1, 4))), 0.0)
+    assert abs(orc.rms_norm(np.full((1, 4), 1e-3))[0, 0] - 1e-3 / math.sqrt(1e-6 + 1e-6)) < 1e-12
+
+
+def test_bf16_rounding():
+    # exact values pass; halfway cases go to the even neighbour; others to the nearest
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 1.0 + 2 ** -7 + 2 ** -10])
+    want = np.array([1.0, 1.0, 1.0 + 4 * 2 ** -8, 1.0, -2.5, 1.0 + 2 ** -7])
+    np.testing.assert_array_equal(orc.bf16_round(vals), want)
+
+
+def test_residual_step_special_cases():
+    # identical experts: the block is 2.5 * SwiGLU(x) whatever the routing, so the step is
+    # a * stream + b * norm(2.5 * SwiGLU(bf16(norm(stream))))
+    rng = np.random.default_rng(3)
+    E, G, TG, K, H, I = 16, 4, 2, 4, 8, 6
+    wg, wu, wd = rng.standard_normal((I, H)), rng.standard_normal((I, H)), rng.standard_normal((H, I))
+    stream = rng.standard_normal((5, H)) * 3.0
+    w_r = rng.standard_normal((E, H))
+    k = 7
+    r = orc.moe_residual_step(stream, k, w_r, None, lambda e: (wg, wu, wd), G, TG, K, 2.5)
+    x = orc.bf16_round(orc.rms_norm(stream))
+    dense = orc.swiglu_expert(x, wg, wu, wd)
+    a, b = math.sqrt(6 / 7), 1 / math.sqrt(7)
+    np.testing.assert_allclose(r["moe"], 2.5 * dense, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["out"], a * stream + b * orc.rms_norm(2.5 * dense), rtol=0, atol=1e-12)
+    # the block's input is the normalised stream: scaling the stream changes only the kept part
+    r2 = orc.moe_residual_step(stream * 4.0, k, w_r, None, lambda e: (wg, wu, wd), G, TG, K, 2.5)
+    np.testing.assert_allclose(r2["out"] - a * stream * 4.0, r["out"] - a * stream, rtol=0, atol=1e-12)
