@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="decode,prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-residual", action="store_true",
+                    help="skip timing the residual-sublayer entry point on the same batches")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (counter calibration)")
@@ -273,6 +275,40 @@ def time_wl(wl, experts, steps, warmup):
                 n_touched=int((counts > 0).sum()), max_count=int(counts.max()), x=x, wr=wr, bias=bias, bufs=bufs)
 
 
+def time_residual(r, steps, warmup):
+    """The same batch through the residual-sublayer entry point (pre-norm, block, post-norm, scaled
+    update at step 2, unit norm weights), out of place so every step sees the same stream."""
+    import torch
+    from grouped_top_routing_fp32_amd import binding, synth
+
+    wl = r["wl"]
+    d = wl.dims
+    stream_in = synth.make_stream(wl, "cuda")
+    wg, wu, wd = r["experts"]
+    bufs = binding.ForwardBuffers(d, wl.tokens, "cuda")
+    st = torch.cuda.current_stream()
+    call = lambda: binding.beam_moe_residual_forward(d, stream_in, 2, r["wr"], r["bias"], wg, wu, wd,  # noqa: E731
+                                                     bufs=bufs, stream=st)
+    for _ in range(warmup):
+        call()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(st)
+    for _ in range(steps):
+        call()
+    end.record(st)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    T, H = wl.tokens, d.hidden
+    # over the plain block: the pre-norm reads the fp32 stream and writes bf16 x (6 bytes per
+    # element), the fused combine also reads the stream (4)
+    extra_bytes = T * H * 10
+    return {"ms_per_step": round(ms, 4), "value": round(T / (ms / 1e3), 1), "unit": "tokens/s",
+            "overhead_ms_vs_block": round(ms - r["ms_per_step"], 4),
+            "extra_algorithmic_bytes": extra_bytes, "step": 2, "norm": "RMSNorm, eps 1e-6, unit weights"}
+
+
 def accounting(r):
     """Algorithmic bytes and FLOPs of each kernel of one step (no cache effects, no re-reads)."""
     wl = r["wl"]
@@ -283,8 +319,8 @@ def accounting(r):
     b = {
         "router_logits": T * H * 2 + E * H * 4,
         "gate_up": nt * 2 * I * H * 2 + T * H * 2 + n * I * 2,
-        "down": nt * H * I * 2 + n * I * 2 + n * H * 4,
-        "combine": n * H * 4 + n * 4 + T * H * 4,
+        "down": nt * H * I * 2 + n * I * 2 + n * H * 2 + n * (H // 64),
+        "combine": n * H * 2 + n * (H // 64) + n * 4 + T * H * 4,
     }
     f = {
         "router_logits": 2 * T * H * E,
@@ -449,6 +485,10 @@ def main():
         r["experts"] = experts
         results[name] = r
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step; stages {r['stage_ms']}", file=sys.stderr, flush=True)
+        if not args.no_residual:
+            r["residual"] = time_residual(r, args.steps, args.warmup)
+            print(f"[bench] {name} as a residual sublayer: {r['residual']['ms_per_step']:.4f} ms/step",
+                  file=sys.stderr, flush=True)
 
     def record(name):
         r = results[name]
@@ -462,6 +502,8 @@ def main():
         out = {"value": round(wl.tokens / (r["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
                "ms_per_step": round(r["ms_per_step"], 4), "config": cfg, "roofline": roofline(r, bound)}
         out.update(layer_summary(r))
+        if "residual" in r:
+            out["residual_sublayer"] = r["residual"]
         return out
 
     head = names[0]
@@ -472,7 +514,9 @@ def main():
                  "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                  "config": main_rec["config"], "roofline": main_rec["roofline"]})
     for k in ("layer_hbm_gbs", "layer_hbm_frac", "layer_expert_tflops", "layer_mfma_frac", "stage_ms",
-              "experts_touched", "max_rows_per_expert"):
+              "experts_touched", "max_rows_per_expert", "residual_sublayer"):
+        if k not in main_rec:
+            continue
         line[k] = main_rec[k]
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (oracle) on {head}", file=sys.stderr, flush=True)

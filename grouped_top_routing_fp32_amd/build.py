@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "dispatch.hip", "experts.hip", "grouped_gemm.hip", "abi.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "experts.hip", "grouped_gemm.hip", "residual.hip", "abi.cpp"]
 
 # Packed FP32 instructions (v_pk_*_f32) are kept out of every kernel.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -33,6 +33,12 @@ hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const in
 hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
                           hipStream_t st);
 int grouped_gemm_rows();
+bool residual_fits(int H);
+hipError_t launch_prenorm(const float* stream, const float* g_in, uint16_t* x, int T, int H, float eps,
+                          hipStream_t st);
+hipError_t launch_combine_residual(const uint16_t* y16, const uint8_t* yscale, const float* w, const float* stream_in,
+                                   const float* g_out, float* stream_out, int T, int H, int K, int step, float eps,
+                                   hipStream_t st);
 hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
                                  int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
                                  int H, int I, int K, hipStream_t st);
@@ -90,6 +96,7 @@ struct Plan {
   size_t off_tiles, off_ntiles;
   // activations
   size_t off_h, off_hscale, off_y, off_yscale;
+  size_t off_x;  // bf16 [T, H]: the block's input, written by beam_moe_residual_forward
   size_t total;
 };
 
@@ -137,6 +144,8 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
   off = align_up(off + (size_t)p->n * p->H * 2);
   p->off_yscale = off;
   off = align_up(off + (size_t)p->n * (p->H / beam::scale_cols()));
+  p->off_x = off;
+  off = align_up(off + (size_t)T * p->H * 2);
   p->total = off;
 }
 
@@ -196,6 +205,70 @@ hipEvent_t* timing_slot() {
 
 hipError_t mark(hipEvent_t* ev, int i, hipStream_t st) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; }
 
+
+// Inputs and by-product outputs of one pass of the block.
+struct BlockArgs {
+  const uint16_t* x;
+  const float* w_router;
+  const float* logit_bias;
+  const float* select_bias;
+  const uint16_t* wg;
+  const uint16_t* wu;
+  const uint16_t* wd;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* sorted_slots;
+};
+
+// Router, selection, dispatch and the expert projections on the caller's
+// stream, then `combine(y16, yscale)` (the final step of the entry point).
+template <typename CombineFn>
+int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* ws, hipStream_t st,
+              CombineFn combine) {
+  const int T = p.T;
+  float* part = at<float>(ws, p.off_part);
+  beam::Tile* tiles = at<beam::Tile>(ws, p.off_tiles);
+  int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
+  uint16_t* h = at<uint16_t>(ws, p.off_h);
+  uint8_t* hscale = at<uint8_t>(ws, p.off_hscale);
+  uint16_t* y16 = at<uint16_t>(ws, p.off_y);
+  uint8_t* yscale = at<uint8_t>(ws, p.off_yscale);
+  hipEvent_t* ev = timing_slot();
+  int rc = BEAM_MOE_OK;
+#define BEAM_TRY(expr)                                     \
+  do {                                                     \
+    if ((rc = hip_status(expr)) != BEAM_MOE_OK) return rc; \
+  } while (0)
+  BEAM_TRY(mark(ev, kStRouter, st));
+  BEAM_TRY(beam::launch_router_logits(a.x, a.w_router, part, T, p.H, p.E, p.splits, p.k_per_split, st));
+  BEAM_TRY(mark(ev, kStSelect, st));
+  BEAM_TRY(beam::launch_select(part, p.splits, true, a.logit_bias, a.select_bias, nullptr, T, p.E, d->num_groups,
+                               d->topk_groups, d->topk, d->routed_scaling, a.topk_ids, a.topk_w, st));
+  BEAM_TRY(mark(ev, kStDispatch, st));
+  BEAM_TRY(beam::launch_dispatch(a.topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), a.expert_counts,
+                                 a.expert_offsets, a.sorted_slots, tiles, p.mt, ntiles, st));
+  BEAM_TRY(mark(ev, kStGateUp, st));
+  if (p.stream)
+    BEAM_TRY(beam::launch_gateup_stream(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wg, a.wu, h, hscale, p.H,
+                                        p.I, p.K, st));
+  else
+    BEAM_TRY(beam::launch_gateup_grouped(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wg, a.wu, h, hscale,
+                                         p.H, p.I, p.K, st));
+  BEAM_TRY(mark(ev, kStDown, st));
+  if (p.stream)
+    BEAM_TRY(beam::launch_down_stream(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wd, y16, yscale, p.H,
+                                      p.I, st));
+  else
+    BEAM_TRY(beam::launch_down_grouped(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wd, y16, yscale,
+                                       p.H, p.I, st));
+  BEAM_TRY(mark(ev, kStCombine, st));
+  BEAM_TRY(combine(y16, yscale));
+  BEAM_TRY(mark(ev, kNumStages, st));
+#undef BEAM_TRY
+  return BEAM_MOE_OK;
+}
 
 }  // namespace
 
@@ -279,51 +352,45 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   Plan p;
   make_plan(d, T, &p);
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  BlockArgs a{static_cast<const uint16_t*>(x_bf16), w_router, logit_bias, select_bias,
+              static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+              static_cast<const uint16_t*>(w_down), topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
-  const uint16_t* wg = static_cast<const uint16_t*>(w_gate);
-  const uint16_t* wu = static_cast<const uint16_t*>(w_up);
-  const uint16_t* wd = static_cast<const uint16_t*>(w_down);
-  float* part = at<float>(ws, p.off_part);
-  beam::Tile* tiles = at<beam::Tile>(ws, p.off_tiles);
-  int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
-  uint16_t* h = at<uint16_t>(ws, p.off_h);
-  uint8_t* hscale = at<uint8_t>(ws, p.off_hscale);
-  uint16_t* y16 = at<uint16_t>(ws, p.off_y);
-  uint8_t* yscale = at<uint8_t>(ws, p.off_yscale);
-  hipEvent_t* ev = timing_slot();
+  return run_block(d, p, a, ws, st, [&](const uint16_t* y16, const uint8_t* yscale) {
+    return beam::launch_combine(y16, yscale, topk_w, out, T, p.H, p.K, st);
+  });
+}
 
-#define BEAM_TRY(expr)                                  \
-  do {                                                  \
-    if ((rc = hip_status(expr)) != BEAM_MOE_OK) return rc; \
-  } while (0)
-  BEAM_TRY(mark(ev, kStRouter, st));
-  BEAM_TRY(beam::launch_router_logits(x, w_router, part, T, p.H, p.E, p.splits, p.k_per_split, st));
-  BEAM_TRY(mark(ev, kStSelect, st));
-  BEAM_TRY(beam::launch_select(part, p.splits, true, logit_bias, select_bias, nullptr, T, p.E, d->num_groups,
-                               d->topk_groups, d->topk, d->routed_scaling, topk_ids, topk_w, st));
-  BEAM_TRY(mark(ev, kStDispatch, st));
-  BEAM_TRY(beam::launch_dispatch(topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), expert_counts, expert_offsets,
-                                 sorted_slots, tiles, p.mt, ntiles, st));
-  BEAM_TRY(mark(ev, kStGateUp, st));
-  if (p.stream)
-    BEAM_TRY(beam::launch_gateup_stream(x, sorted_slots, tiles, ntiles, p.max_tiles, wg, wu, h, hscale, p.H, p.I,
-                                        p.K, st));
-  else
-    BEAM_TRY(beam::launch_gateup_grouped(x, sorted_slots, tiles, ntiles, p.max_tiles, wg, wu, h, hscale, p.H, p.I,
-                                         p.K, st));
-  BEAM_TRY(mark(ev, kStDown, st));
-  if (p.stream)
-    BEAM_TRY(beam::launch_down_stream(h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y16, yscale, p.H, p.I,
-                                      st));
-  else
-    BEAM_TRY(beam::launch_down_grouped(h, hscale, sorted_slots, tiles, ntiles, p.max_tiles, wd, y16, yscale, p.H, p.I,
-                                       st));
-  BEAM_TRY(mark(ev, kStCombine, st));
-  BEAM_TRY(beam::launch_combine(y16, yscale, topk_w, out, T, p.H, p.K, st));
-  BEAM_TRY(mark(ev, kNumStages, st));
-#undef BEAM_TRY
-  return BEAM_MOE_OK;
+int beam_moe_residual_forward(const beam_moe_dims* d, int32_t T, const float* stream_in, int32_t step,
+                              const float* norm_in_weight, const float* norm_out_weight, float norm_eps,
+                              const float* w_router, const float* logit_bias, const float* select_bias,
+                              const void* w_gate, const void* w_up, const void* w_down, float* stream_out,
+                              int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK) return rc;
+  if (!beam::residual_fits(d->hidden)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (step < 2 || !std::isfinite(norm_eps) || norm_eps < 0.f) return BEAM_MOE_ERR_INVALID_ARG;
+  if (T == 0) return BEAM_MOE_OK;
+  if ((rc = check_ptrs({stream_in, w_router, w_gate, w_up, w_down, stream_out, topk_ids, topk_w, expert_counts,
+                        expert_offsets, sorted_slots})) != BEAM_MOE_OK)
+    return rc;
+  for (const float* opt : {logit_bias, select_bias, norm_in_weight, norm_out_weight})
+    if (opt && !aligned16(opt)) return BEAM_MOE_ERR_INVALID_ARG;
+  Plan p;
+  make_plan(d, T, &p);
+  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* x = at<uint16_t>(ws, p.off_x);
+  if ((rc = hip_status(beam::launch_prenorm(stream_in, norm_in_weight, x, T, p.H, norm_eps, st))) != BEAM_MOE_OK)
+    return rc;
+  BlockArgs a{x, w_router, logit_bias, select_bias, static_cast<const uint16_t*>(w_gate),
+              static_cast<const uint16_t*>(w_up), static_cast<const uint16_t*>(w_down), topk_ids, topk_w,
+              expert_counts, expert_offsets, sorted_slots};
+  return run_block(d, p, a, ws, st, [&](const uint16_t* y16, const uint8_t* yscale) {
+    return beam::launch_combine_residual(y16, yscale, topk_w, stream_in, norm_out_weight, stream_out, T, p.H, p.K,
+                                         step, norm_eps, st);
+  });
 }
 
 int beam_moe_timing_enable(int enable) {

@@ -41,7 +41,7 @@ import torch
 
 M32 = 0xFFFFFFFF
 
-TENSOR_X, TENSOR_ROUTER, TENSOR_GATE, TENSOR_UP, TENSOR_DOWN, TENSOR_PERM = range(6)
+TENSOR_X, TENSOR_ROUTER, TENSOR_GATE, TENSOR_UP, TENSOR_DOWN, TENSOR_PERM, TENSOR_STREAM, TENSOR_NORM = range(8)
 
 
 # --------------------------------------------------------------------------
@@ -193,6 +193,22 @@ def x_rows(wl: Workload, rows, device="cpu") -> torch.Tensor:
 
 def make_x(wl: Workload, device="cpu") -> torch.Tensor:
     return normal((wl.tokens, wl.dims.hidden), wl.x_sigma, wl.seed, TENSOR_X, dtype=torch.bfloat16, device=device)
+
+
+def make_stream(wl: Workload, device="cpu") -> torch.Tensor:
+    """fp32 residual stream [T, H]: unit normals, token t scaled by 2^((t mod 7) - 3) so
+    that the token RMS spans 1/8 .. 8 (exact scaling, powers of two)."""
+    T, H = wl.tokens, wl.dims.hidden
+    z = normal((T, H), 1.0, wl.seed, TENSOR_STREAM, dtype=torch.float32, device=device)
+    e = (torch.arange(T, dtype=torch.int64, device=device) % 7 - 3).to(torch.float32)
+    return z * torch.exp2(e)[:, None]
+
+
+def make_norm_weights(wl: Workload, device="cpu") -> tuple[torch.Tensor, torch.Tensor]:
+    """fp32 norm weights (g_in, g_out) [H] each: 1 + N(0, 0.1^2)."""
+    H = wl.dims.hidden
+    g = normal((2, H), 0.1, wl.seed, TENSOR_NORM, dtype=torch.float32, device=device) + 1.0
+    return g[0].contiguous(), g[1].contiguous()
 
 
 def make_router(wl: Workload, device="cpu") -> torch.Tensor:

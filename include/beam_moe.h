@@ -75,7 +75,7 @@ enum {
 
 /* Bytes of workspace that beam_moe_route, beam_moe_dispatch and
  * beam_moe_forward need for T tokens (one size serves all three; it grows
- * linearly in T: at Beam dims about 122 KB per token, mostly the fp16 SwiGLU
+ * linearly in T: at Beam dims about 132 KB per token, mostly the fp16 SwiGLU
  * activations [T*K, I] and the fp16 expert outputs [T*K, H], each with a
  * power-of-two scale per 64 columns).
  * Returns SIZE_MAX for invalid or unsupported dims. */
@@ -141,6 +141,31 @@ int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, c
                      const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
                      const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
                      int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* The block as a residual sublayer at step `step` of the stream
+ * (「Reflection 发布 Beam 501B 开源模型，支持 1M tokens 上下文」, section 残差流:
+ * the input embedding is step 1; at step k a sublayer's output enters with
+ * weight 1/sqrt(k) and the stream is kept with weight sqrt((k-1)/k); every
+ * sublayer is normalised before and after, in FP32):
+ *   x          = bf16(norm(stream_in) * norm_in_weight)          (RNE)
+ *   out        = the block on x, as beam_moe_forward
+ *   stream_out = sqrt((step-1)/step) * stream_in + 1/sqrt(step) * norm(out) * norm_out_weight
+ * norm(v) = v / sqrt(mean(v^2) + norm_eps) over the H columns of a token (RMSNorm;
+ * the pages name neither form, weights nor eps).  The norm statistics are taken in
+ * FP64, the rest in FP32.
+ *   stream_in        [T, H] fp32
+ *   step             >= 2
+ *   norm_in_weight, norm_out_weight   [H] fp32, NULL = ones
+ *   norm_eps         >= 0, finite
+ *   stream_out       [T, H] fp32 out; may be stream_in itself (in-place update)
+ *   other arguments as in beam_moe_forward.  The workspace also holds x.
+ * Supported hidden sizes additionally satisfy hidden <= 8192. */
+int beam_moe_residual_forward(const beam_moe_dims* dims, int32_t T, const float* stream_in, int32_t step,
+                              const float* norm_in_weight, const float* norm_out_weight, float norm_eps,
+                              const float* w_router, const float* logit_bias, const float* select_bias,
+                              const void* w_gate, const void* w_up, const void* w_down, float* stream_out,
+                              int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
 /* Diagnostics: device time of the stages of beam_moe_forward.
  * beam_moe_timing_enable(1) makes later beam_moe_forward calls record HIP

@@ -137,3 +137,38 @@ def forward_parity(p: Problem, bufs, tokens=None):
     out_g = bufs.out.cpu().numpy().astype(np.float64)[tokens]
     worst = compare_outputs(out_g, out_o, keep)
     return excluded, worst
+
+
+def residual_parity(p: Problem, stream: torch.Tensor, step: int, bufs, tokens=None, g_in=None, g_out=None,
+                    eps=orc.NORM_EPS):
+    """Compare one beam_moe_residual_forward result (new stream in bufs.out) with the oracle.
+
+    Two output checks per kept token: the new stream within 1e-2 x its RMS, and
+    the sublayer's contribution recovered from it, (new - a * stream) / b, within
+    1e-2 x the RMS of the oracle's norm(out) * g_out, which the stream term
+    would otherwise mask at large stream scales.  Returns (excluded, worst ratio)."""
+    d = p.dims
+    T = stream.shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    S = f64(stream)[tokens]
+    sb = None if p.select_bias is None else f64(p.select_bias)
+    bias = None if p.bias is None else f64(p.bias)
+    r = orc.moe_residual_step(S, step, f64(p.wr), bias, p.expert_f64, d.num_groups, d.topk_groups, d.topk,
+                              d.routed_scaling, select_bias=sb,
+                              norm_in_weight=None if g_in is None else f64(g_in),
+                              norm_out_weight=None if g_out is None else f64(g_out), eps=eps)
+    m = orc.route_margins(r["S"], d.num_groups, d.topk_groups, d.topk, select_bias=sb)
+    ids_g = bufs.ids.cpu().numpy()
+    w_g = bufs.w.cpu().numpy()
+    excluded = compare_routing(ids_g[tokens], w_g[tokens], r["ids"], r["w"], orc.selection_values(r["S"], sb), m,
+                               d)
+    check_dispatch_valid(ids_g, bufs.counts.cpu().numpy(), bufs.offsets.cpu().numpy(), bufs.slots.cpu().numpy(),
+                         d.num_experts)
+    keep = m >= MARGIN
+    new_g = bufs.out.cpu().numpy().astype(np.float64)[tokens]
+    worst = compare_outputs(new_g, r["out"], keep)
+    a, b = orc.residual_weights(step)
+    term_o = orc.rms_norm(r["moe"], None if g_out is None else f64(g_out), eps)
+    term_g = (new_g - a * S) / b
+    worst = max(worst, compare_outputs(term_g, term_o, keep))
+    return excluded, worst

@@ -53,9 +53,10 @@ def test_workspace_bytes():
     n64 = binding.beam_moe_workspace_bytes(BEAM, 64)
     n16k = binding.beam_moe_workspace_bytes(BEAM, 16384)
     assert 0 < n64 < n16k
-    # dominated by the fp16 activations h [T*K, I] and expert outputs y [T*K, H]
-    assert n16k >= 16384 * 8 * (2560 * 2 + 5120 * 2)
-    assert n16k < 16384 * 8 * (2560 * 2 + 5120 * 2) * 1.1
+    # dominated by the fp16 activations h [T*K, I] and expert outputs y [T*K, H], plus the bf16 input x [T, H]
+    per_token = 8 * (2560 * 2 + 5120 * 2) + 5120 * 2
+    assert n16k >= 16384 * per_token
+    assert n16k < 16384 * per_token * 1.1
     assert binding.beam_moe_workspace_bytes(TINY, 0) >= 0
 
 
@@ -132,3 +133,36 @@ def test_zero_tokens_is_a_no_op():
     assert lib.beam_moe_route(ctypes.byref(cd), 0, *([None] * 8), 0, None) == binding.BEAM_MOE_OK
     assert lib.beam_moe_select(ctypes.byref(cd), 0, None, None, None, None, None) == binding.BEAM_MOE_OK
     assert lib.beam_moe_dispatch(ctypes.byref(cd), 0, *([None] * 5), 0, None) == binding.BEAM_MOE_OK
+
+
+def _residual(lib, cd, T, step=2, eps=1e-6, ptrs=None, ws_bytes=1 << 40):
+    # dims, T, stream_in, step, g_in, g_out, eps, w_router, logit_bias, select_bias, gate, up, down,
+    # stream_out, ids, w, counts, offsets, slots, ws, ws_bytes, stream
+    p = ptrs if ptrs is not None else {}
+    g = lambda k, dflt=FAKE: p.get(k, dflt)  # noqa: E731
+    return lib.beam_moe_residual_forward(ctypes.byref(cd), T, g("stream_in"), step, g("g_in", None),
+                                         g("g_out", None), eps, g("w_router"), g("logit_bias", None),
+                                         g("select_bias", None), g("gate"), g("up"), g("down"), g("stream_out"),
+                                         g("ids"), g("w"), g("counts"), g("offsets"), g("slots"), g("ws"), ws_bytes,
+                                         None)
+
+
+def test_residual_forward_validation():
+    lib = binding.load_library()
+    cd = binding._cdims(BEAM)
+    assert _residual(lib, cd, 64, step=1) == binding.BEAM_MOE_ERR_INVALID_ARG       # step 1 is the embedding
+    assert _residual(lib, cd, 64, eps=-1.0) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert _residual(lib, cd, 64, eps=float("nan")) == binding.BEAM_MOE_ERR_INVALID_ARG
+    for name in ("stream_in", "w_router", "gate", "up", "down", "stream_out", "ids", "w", "counts", "offsets",
+                 "slots"):
+        assert _residual(lib, cd, 64, ptrs={name: None}) == binding.BEAM_MOE_ERR_INVALID_ARG, name
+    for name in ("g_in", "g_out", "logit_bias", "select_bias"):
+        assert _residual(lib, cd, 64, ptrs={name: ctypes.c_void_p((1 << 20) + 4)}) == \
+            binding.BEAM_MOE_ERR_INVALID_ARG, name
+    need = lib.beam_moe_workspace_bytes(ctypes.byref(cd), 64)
+    assert _residual(lib, cd, 64, ws_bytes=need - 1) == binding.BEAM_MOE_ERR_WORKSPACE
+    wide = binding._cdims(Dims(8448, 2560, 256, 8, 4, 8))   # H > 8192
+    assert _residual(lib, wide, 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert _residual(lib, binding._cdims(TINY), 0, ptrs={k: None for k in ("stream_in", "w_router", "gate", "up",
+                     "down", "stream_out", "ids", "w", "counts", "offsets", "slots", "ws")}, ws_bytes=0) == \
+        binding.BEAM_MOE_OK

@@ -15,7 +15,7 @@ import torch
 
 from grouped_top_routing_fp32_amd import binding, synth
 from oracle import beam_moe_oracle as orc
-from parity_helpers import Problem, check_dispatch_valid, compare_routing, f64, forward_parity
+from parity_helpers import Problem, check_dispatch_valid, compare_routing, f64, forward_parity, residual_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -346,3 +346,61 @@ def test_forward_with_selection_bias(name):
     out1 = bufs.out.clone()
     binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd, select_bias=sb, bufs=bufs)
     assert torch.equal(out1, bufs.out)
+
+
+# --------------------------------------------------------------------------
+# the block as a residual sublayer: pre-norm, block, post-norm, scaled update
+# --------------------------------------------------------------------------
+def _residual_case(wl, step, weights, experts=None, select_bias=None):
+    p = Problem(wl, DEV, experts=experts, select_bias=select_bias)
+    stream = synth.make_stream(wl, DEV)
+    g_in, g_out = synth.make_norm_weights(wl, DEV) if weights else (None, None)
+    bufs = binding.beam_moe_residual_forward(p.dims, stream, step, p.wr, p.bias, p.wg, p.wu, p.wd,
+                                             select_bias=select_bias, norm_in_weight=g_in, norm_out_weight=g_out)
+    torch.cuda.synchronize()
+    return p, stream, g_in, g_out, bufs
+
+
+@pytest.mark.parametrize("step,weights", [(2, False), (3, True), (105, True)])
+def test_residual_tiny(step, weights):
+    _announce(f"residual tiny step={step} weights={weights}")
+    p, stream, g_in, g_out, bufs = _residual_case(synth.WORKLOADS["tiny"], step, weights)
+    excluded, worst = residual_parity(p, stream, step, bufs, g_in=g_in, g_out=g_out)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+
+
+@pytest.mark.parametrize("name", ["mid_stream", "mid_tiled", "mid_stream_skew"])
+def test_residual_mid(name):
+    _announce(f"residual {name} (all tokens)")
+    wl, _ = MID[name]
+    p, stream, g_in, g_out, bufs = _residual_case(wl, 4, True)
+    excluded, worst = residual_parity(p, stream, 4, bufs, g_in=g_in, g_out=g_out)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+    # in place (stream_out is stream_in) gives the same bits, and so does a second call
+    new1 = bufs.out.clone()
+    inplace = stream.clone()
+    binding.beam_moe_residual_forward(p.dims, inplace, 4, p.wr, p.bias, p.wg, p.wu, p.wd, norm_in_weight=g_in,
+                                      norm_out_weight=g_out, stream_out=inplace)
+    assert torch.equal(inplace, new1)
+    binding.beam_moe_residual_forward(p.dims, stream, 4, p.wr, p.bias, p.wg, p.wu, p.wd, norm_in_weight=g_in,
+                                      norm_out_weight=g_out, bufs=bufs)
+    assert torch.equal(bufs.out, new1)
+
+
+def test_residual_selection_bias():
+    _announce("residual mid_tiled with selection bias")
+    wl, _ = MID["mid_tiled"]
+    sb = synth.normal((wl.dims.num_experts,), 0.05, 11, 0, device=DEV)
+    p, stream, g_in, g_out, bufs = _residual_case(wl, 6, True, select_bias=sb)
+    excluded, worst = residual_parity(p, stream, 6, bufs, g_in=g_in, g_out=g_out)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+
+
+@pytest.mark.parametrize("T", [64, 1024])
+def test_residual_beam(beam_experts, T):
+    _announce(f"residual Beam T={T}")
+    wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
+    p, stream, g_in, g_out, bufs = _residual_case(wl, 3, True, experts=beam_experts)
+    sample = sorted({0, 1, 2, 3, T // 2, T - 1})
+    excluded, worst = residual_parity(p, stream, 3, bufs, sample, g_in=g_in, g_out=g_out)
+    print(f"  sampled {len(sample)} tokens, excluded {excluded}, worst error / tolerance {worst:.3f}")
