@@ -241,6 +241,35 @@ def time_workload(name, experts, steps, warmup):
     return time_wl(synth.WORKLOADS[name], experts, steps, warmup)
 
 
+def timed_loops(call, steps, warmup, stream):
+    """Milliseconds of `steps` back-to-back calls (stage markers off), then the per-stage
+    device times summed over a second loop of `steps` calls with the markers on (each
+    marker costs a few microseconds of its own, so the first loop gives the step time)."""
+    import torch
+    from grouped_top_routing_fp32_amd import binding
+
+    for _ in range(warmup):
+        call()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    binding.beam_moe_timing_read()                 # drop anything recorded before
+    binding.beam_moe_timing_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    binding.beam_moe_timing_enable(False)
+    stage_ms, calls = binding.beam_moe_timing_read()
+    assert calls == steps, (calls, steps)
+    return total_ms, stage_ms
+
+
 def time_wl(wl, experts, steps, warmup):
     import torch
     from grouped_top_routing_fp32_amd import binding, synth
@@ -252,23 +281,8 @@ def time_wl(wl, experts, steps, warmup):
     wg, wu, wd = experts
     bufs = binding.ForwardBuffers(d, wl.tokens, "cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        binding.beam_moe_forward(d, x, wr, bias, wg, wu, wd, bufs=bufs, stream=stream)
-    torch.cuda.synchronize()
-    binding.beam_moe_timing_read()                 # drop anything recorded before
-    binding.beam_moe_timing_enable(True)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(steps):
-        binding.beam_moe_forward(d, x, wr, bias, wg, wu, wd, bufs=bufs, stream=stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    binding.beam_moe_timing_enable(False)
-    stage_ms, calls = binding.beam_moe_timing_read()
-    total_ms = start.elapsed_time(end)
-    assert calls == steps, (calls, steps)
+    call = lambda: binding.beam_moe_forward(d, x, wr, bias, wg, wu, wd, bufs=bufs, stream=stream)  # noqa: E731
+    total_ms, stage_ms = timed_loops(call, steps, warmup, stream)
     counts = bufs.counts.cpu()
     return dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps,
                 stage_ms={k: v / steps for k, v in stage_ms.items()},
@@ -289,23 +303,21 @@ def time_residual(r, steps, warmup):
     st = torch.cuda.current_stream()
     call = lambda: binding.beam_moe_residual_forward(d, stream_in, 2, r["wr"], r["bias"], wg, wu, wd,  # noqa: E731
                                                      bufs=bufs, stream=st)
-    for _ in range(warmup):
-        call()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(st)
-    for _ in range(steps):
-        call()
-    end.record(st)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    total_ms, stage_ms = timed_loops(call, steps, warmup, st)
+    ms = total_ms / steps
+    stage = {k: round(v / steps, 4) for k, v in stage_ms.items()}
+    touched = int((bufs.counts > 0).sum())
     T, H = wl.tokens, d.hidden
     # over the plain block: the pre-norm reads the fp32 stream and writes bf16 x (6 bytes per
     # element), the fused combine also reads the stream (4)
     extra_bytes = T * H * 10
+    # the cost of the sublayer's own work, free of the routing difference (the normalised stream
+    # routes to a different set of experts than the block's own x): pre-norm plus the fused
+    # combine's time above the plain combine's
+    own_ms = stage["prenorm"] + stage["combine"] - r["stage_ms"]["combine"]
     return {"ms_per_step": round(ms, 4), "value": round(T / (ms / 1e3), 1), "unit": "tokens/s",
-            "overhead_ms_vs_block": round(ms - r["ms_per_step"], 4),
+            "stage_ms": stage, "experts_touched": touched,
+            "norm_and_update_ms": round(own_ms, 4),
             "extra_algorithmic_bytes": extra_bytes, "step": 2, "norm": "RMSNorm, eps 1e-6, unit weights"}
 
 

@@ -175,8 +175,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BEAM_MOE_OK : BEAM_MOE_E
 // ---------------------------------------------------------------------------
 // stage timing (diagnostics)
 // ---------------------------------------------------------------------------
-enum Stage { kStRouter = 0, kStSelect, kStDispatch, kStGateUp, kStDown, kStCombine, kNumStages };
-const char* const kStageNames[kNumStages] = {"router_logits", "select", "dispatch", "gate_up", "down", "combine"};
+enum Stage { kStPrenorm = 0, kStRouter, kStSelect, kStDispatch, kStGateUp, kStDown, kStCombine, kNumStages };
+const char* const kStageNames[kNumStages] = {"prenorm", "router_logits", "select", "dispatch",
+                                             "gate_up", "down", "combine"};
 
 struct Timing {
   std::mutex mu;
@@ -222,10 +223,11 @@ struct BlockArgs {
   int32_t* sorted_slots;
 };
 
-// Router, selection, dispatch and the expert projections on the caller's
+// `pre()` (whatever produces the block's input; nothing for beam_moe_forward),
+// then router, selection, dispatch and the expert projections on the caller's
 // stream, then `combine(y16, yscale)` (the final step of the entry point).
-template <typename CombineFn>
-int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* ws, hipStream_t st,
+template <typename PreFn, typename CombineFn>
+int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* ws, hipStream_t st, PreFn pre,
               CombineFn combine) {
   const int T = p.T;
   float* part = at<float>(ws, p.off_part);
@@ -241,6 +243,8 @@ int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* w
   do {                                                     \
     if ((rc = hip_status(expr)) != BEAM_MOE_OK) return rc; \
   } while (0)
+  BEAM_TRY(mark(ev, kStPrenorm, st));
+  BEAM_TRY(pre());
   BEAM_TRY(mark(ev, kStRouter, st));
   BEAM_TRY(beam::launch_router_logits(a.x, a.w_router, part, T, p.H, p.E, p.splits, p.k_per_split, st));
   BEAM_TRY(mark(ev, kStSelect, st));
@@ -356,9 +360,11 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
               static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
               static_cast<const uint16_t*>(w_down), topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return run_block(d, p, a, ws, st, [&](const uint16_t* y16, const uint8_t* yscale) {
-    return beam::launch_combine(y16, yscale, topk_w, out, T, p.H, p.K, st);
-  });
+  return run_block(
+      d, p, a, ws, st, [] { return hipSuccess; },
+      [&](const uint16_t* y16, const uint8_t* yscale) {
+        return beam::launch_combine(y16, yscale, topk_w, out, T, p.H, p.K, st);
+      });
 }
 
 int beam_moe_residual_forward(const beam_moe_dims* d, int32_t T, const float* stream_in, int32_t step,
@@ -382,15 +388,15 @@ int beam_moe_residual_forward(const beam_moe_dims* d, int32_t T, const float* st
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t* x = at<uint16_t>(ws, p.off_x);
-  if ((rc = hip_status(beam::launch_prenorm(stream_in, norm_in_weight, x, T, p.H, norm_eps, st))) != BEAM_MOE_OK)
-    return rc;
   BlockArgs a{x, w_router, logit_bias, select_bias, static_cast<const uint16_t*>(w_gate),
               static_cast<const uint16_t*>(w_up), static_cast<const uint16_t*>(w_down), topk_ids, topk_w,
               expert_counts, expert_offsets, sorted_slots};
-  return run_block(d, p, a, ws, st, [&](const uint16_t* y16, const uint8_t* yscale) {
-    return beam::launch_combine_residual(y16, yscale, topk_w, stream_in, norm_out_weight, stream_out, T, p.H, p.K,
-                                         step, norm_eps, st);
-  });
+  return run_block(
+      d, p, a, ws, st, [&] { return beam::launch_prenorm(stream_in, norm_in_weight, x, T, p.H, norm_eps, st); },
+      [&](const uint16_t* y16, const uint8_t* yscale) {
+        return beam::launch_combine_residual(y16, yscale, topk_w, stream_in, norm_out_weight, stream_out, T, p.H,
+                                             p.K, step, norm_eps, st);
+      });
 }
 
 int beam_moe_timing_enable(int enable) {

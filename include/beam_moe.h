@@ -167,8 +167,9 @@ int beam_moe_residual_forward(const beam_moe_dims* dims, int32_t T, const float*
                               int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
                               int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
-/* Diagnostics: device time of the stages of beam_moe_forward.
- * beam_moe_timing_enable(1) makes later beam_moe_forward calls record HIP
+/* Diagnostics: device time of the stages of beam_moe_forward and
+ * beam_moe_residual_forward ("prenorm" is zero for the former).
+ * beam_moe_timing_enable(1) makes later calls of either record HIP
  * events between their stages on the caller's stream (a marker per stage,
  * no synchronisation; the events are created by the library on first use and
  * kept for reuse). beam_moe_timing_read waits for the last recorded call,
