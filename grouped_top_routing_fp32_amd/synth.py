@@ -41,7 +41,8 @@ import torch
 
 M32 = 0xFFFFFFFF
 
-TENSOR_X, TENSOR_ROUTER, TENSOR_GATE, TENSOR_UP, TENSOR_DOWN, TENSOR_PERM, TENSOR_STREAM, TENSOR_NORM = range(8)
+(TENSOR_X, TENSOR_ROUTER, TENSOR_GATE, TENSOR_UP, TENSOR_DOWN, TENSOR_PERM, TENSOR_STREAM, TENSOR_NORM,
+ TENSOR_GATE_SCALE, TENSOR_UP_SCALE, TENSOR_DOWN_SCALE) = range(11)
 
 
 # --------------------------------------------------------------------------
@@ -261,3 +262,57 @@ def make_experts(wl: Workload, device="cpu", experts=None):
         normal((H, I), s, wl.seed, TENSOR_DOWN, e, torch.bfloat16, out=wd[e])
     return wg, wu, wd
 
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) expert weights: codes and one fp32 scale per output row
+# --------------------------------------------------------------------------
+FP8_CODE_SIGMA = 100.0  # codes ~ N(0, 100^2) rounded to E4M3; the table's tails (|z| < 4.4) stay below 448
+
+
+def fp8_codes(shape, seed: int, tensor_id: int, expert: int, device="cpu", out=None) -> torch.Tensor:
+    """uint8 E4M3 codes: unit normals times FP8_CODE_SIGMA (fp32), rounded by torch's float8_e4m3fn cast."""
+    z = normal(shape, FP8_CODE_SIGMA, seed, tensor_id, expert, torch.float32, device)
+    q = z.to(torch.float8_e4m3fn).view(torch.uint8)
+    if out is None:
+        return q
+    out.copy_(q)
+    return out
+
+
+def fp8_scales(n: int, sigma: float, seed: int, tensor_id: int, expert: int, device="cpu") -> torch.Tensor:
+    """fp32 per-row scales (sigma / FP8_CODE_SIGMA) * (1 + 0.2 z), z a unit normal (|z| < 4.4: positive)."""
+    z = normal((n,), 1.0, seed, tensor_id, expert, torch.float32, device)
+    f32 = lambda v: torch.tensor(v, dtype=torch.float32, device=z.device)  # noqa: E731
+    return (z * f32(0.2) + f32(1.0)) * f32(sigma / FP8_CODE_SIGMA)
+
+
+def expert_weights_fp8(wl: Workload, e: int, device="cpu"):
+    """(q_gate [I,H], s_gate [I], q_up [I,H], s_up [I], q_down [H,I], s_down [H]) of expert e;
+    dequantised rows have standard deviation about expert_sigma."""
+    d = wl.dims
+    s = wl.expert_sigma
+    I, H = d.intermediate, d.hidden
+    return (fp8_codes((I, H), wl.seed, TENSOR_GATE, e, device), fp8_scales(I, s, wl.seed, TENSOR_GATE_SCALE, e, device),
+            fp8_codes((I, H), wl.seed, TENSOR_UP, e, device), fp8_scales(I, s, wl.seed, TENSOR_UP_SCALE, e, device),
+            fp8_codes((H, I), wl.seed, TENSOR_DOWN, e, device), fp8_scales(H, s, wl.seed, TENSOR_DOWN_SCALE, e, device))
+
+
+def make_experts_fp8(wl: Workload, device="cpu"):
+    """Stacked FP8 experts: codes [E,I,H], [E,I,H], [E,H,I] (uint8) and scales [E,I], [E,I], [E,H] (fp32)."""
+    d = wl.dims
+    E, I, H = d.num_experts, d.intermediate, d.hidden
+    qg = torch.empty((E, I, H), dtype=torch.uint8, device=device)
+    qu = torch.empty((E, I, H), dtype=torch.uint8, device=device)
+    qd = torch.empty((E, H, I), dtype=torch.uint8, device=device)
+    sg = torch.empty((E, I), dtype=torch.float32, device=device)
+    su = torch.empty((E, I), dtype=torch.float32, device=device)
+    sd = torch.empty((E, H), dtype=torch.float32, device=device)
+    s = wl.expert_sigma
+    for e in range(E):
+        fp8_codes((I, H), wl.seed, TENSOR_GATE, e, device, out=qg[e])
+        fp8_codes((I, H), wl.seed, TENSOR_UP, e, device, out=qu[e])
+        fp8_codes((H, I), wl.seed, TENSOR_DOWN, e, device, out=qd[e])
+        sg[e] = fp8_scales(I, s, wl.seed, TENSOR_GATE_SCALE, e, device)
+        su[e] = fp8_scales(I, s, wl.seed, TENSOR_UP_SCALE, e, device)
+        sd[e] = fp8_scales(H, s, wl.seed, TENSOR_DOWN_SCALE, e, device)
+    return qg, sg, qu, su, qd, sd

@@ -305,6 +305,46 @@ def route_only(x, w_router, logit_bias, num_groups, topk_groups, topk, routed_sc
 
 
 # --------------------------------------------------------------------------
+# FP8 (E4M3) expert weights
+# --------------------------------------------------------------------------
+# 「Reflection 放出 501B 的 Beam 权重：四套精度、滑动窗口和一场榜单落差」, the
+# parameter-precision listing of the FP8 repository and the remarks under it:
+# every expert weight is stored as F8_E4M3 (the router, embedding and LM head
+# are kept out of the quantisation), a plain dynamic FP8 quantisation of the
+# BF16 weights.  The pages give no scale granularity; read here as one FP32
+# scale per output row (per channel): W[r, :] = decode(q[r, :]) * scale[r].
+def e4m3_decode(codes):
+    """Values of OCP FP8 E4M3 codes (the "fn" variant: no infinities, S.1111.111 is NaN).
+
+    Sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0:
+    normal (e > 0):  (-1)^s * 2^(e - 7) * (1 + m / 8);
+    subnormal (e = 0): (-1)^s * 2^-6 * (m / 8).
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def dequantize_rows(codes, scales):
+    """W[r, :] = e4m3_decode(codes[r, :]) * scales[r] (FP64; one scale per output row)."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[:, None]
+
+
+def fp8_expert(q_gate, s_gate, q_up, s_up, q_down, s_down):
+    """(W_gate, W_up, W_down) in FP64 from E4M3 codes and per-row scales.
+
+    q_gate, q_up [I, H] with s_gate, s_up [I]; q_down [H, I] with s_down [H].
+    Any function returning these can serve as ``expert_weights`` of
+    :func:`moe_forward`: the block itself is unchanged.
+    """
+    return dequantize_rows(q_gate, s_gate), dequantize_rows(q_up, s_up), dequantize_rows(q_down, s_down)
+
+
+# --------------------------------------------------------------------------
 # the block as a residual sublayer (pre-norm, post-norm, scaled update)
 # --------------------------------------------------------------------------
 # Blog, section 残差流 (residual stream): the input embedding is step 1; at

@@ -11,7 +11,9 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
+from grouped_top_routing_fp32_amd import synth
 from oracle import beam_moe_oracle as orc
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -493,3 +495,70 @@ def test_residual_step_special_cases():
     # the block's input is the normalised stream: scaling the stream changes only the kept part
     r2 = orc.moe_residual_step(stream * 4.0, k, w_r, None, lambda e: (wg, wu, wd), G, TG, K, 2.5)
     np.testing.assert_allclose(r2["out"] - a * stream * 4.0, r["out"] - a * stream, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) expert weights
+# --------------------------------------------------------------------------
+def test_e4m3_decode_known_values():
+    # values fixed by the OCP 8-bit floating point specification (E4M3, bias 7, no infinities)
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5,
+             0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in known.items():
+        assert orc.e4m3_decode(np.array([c]))[0] == v, hex(c)
+    assert np.isnan(orc.e4m3_decode(np.array([0x7F, 0xFF]))).all()
+    z = orc.e4m3_decode(np.array([0x80]))[0]
+    assert z == 0.0 and math.copysign(1.0, z) == -1.0
+
+
+def test_e4m3_decode_matches_torch_float8():
+    # an independent implementation: torch's float8_e4m3fn dtype
+    codes = np.arange(256)
+    mine = orc.e4m3_decode(codes)
+    lib = torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(lib))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(mine[ok], lib[ok])
+
+
+def test_e4m3_decode_order_and_symmetry():
+    pos = orc.e4m3_decode(np.arange(0, 127))
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(orc.e4m3_decode(np.arange(128, 255)), -pos)
+    # relative spacing of the normal range is 2^-3 (three mantissa bits)
+    normal = pos[8:]
+    assert np.max(np.diff(normal) / normal[:-1]) == 0.125
+
+
+def test_dequantize_rows_scales_each_row():
+    codes = np.array([[0x38, 0x40], [0xB8, 0x30]])
+    w = orc.dequantize_rows(codes, [2.0, 0.5])
+    assert np.array_equal(w, [[2.0, 4.0], [-0.5, 0.25]])
+
+
+def test_fp8_expert_hand_example():
+    # H = 2, I = 1; W_gate = [[2, 2]], W_up = [[1, 0]], W_down = [[1], [-3]]; x = [1, 1]:
+    # g = 4, u = 1, h = silu(4), y = [h, -3h].  Pairing a scale with the wrong matrix
+    # (gate <-> up) gives g = 1, u = 4, another value.
+    qg, sg = np.array([[0x38, 0x38]]), [2.0]
+    qu, su = np.array([[0x40, 0x00]]), [0.5]
+    qd, sd = np.array([[0x38], [0xB8]]), [1.0, 3.0]
+    wg, wu, wd = orc.fp8_expert(qg, sg, qu, su, qd, sd)
+    y = orc.swiglu_expert(np.array([[1.0, 1.0]]), wg, wu, wd)
+    h = 4.0 / (1.0 + math.exp(-4.0))
+    np.testing.assert_allclose(y[0], [h, -3.0 * h], rtol=1e-15)
+    wg2, wu2, wd2 = orc.fp8_expert(qg, su, qu, sg, qd, sd)
+    y2 = orc.swiglu_expert(np.array([[1.0, 1.0]]), wg2, wu2, wd2)
+    assert abs(y2[0, 0] - h) > 0.1
+
+
+def test_fp8_generator_codes_are_finite_and_scaled():
+    wl = synth.WORKLOADS["tiny"]
+    qg, sg, qu, su, qd, sd = synth.expert_weights_fp8(wl, 0)
+    for q in (qg, qu, qd):
+        v = orc.e4m3_decode(q.numpy())
+        assert not np.isnan(v).any() and np.abs(v).max() <= 448.0
+    for s in (sg, su, sd):
+        assert (s > 0).all()
+    w = orc.dequantize_rows(qd.numpy(), sd.numpy())
+    assert 0.015 < w.std() < 0.025
