@@ -45,7 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_hbm_traffic_decode_prefil
 KERNEL_SOURCES = ["grouped_top_routing_fp32_amd/csrc/" + f
                   for f in ("common.h", "experts.hip", "grouped_gemm.hip", "dispatch.hip", "abi.cpp")]
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
-GATE_UP_KERNELS = {"decode": "gateup_stream", "prefill": "grouped_gemm_kernel<true>"}
+GATE_UP_KERNELS = {"decode": "gateup_stream_lds_kernel", "prefill": "grouped_gemm_kernel<true>",
+                   "decode_fp8": "gateup_stream_fp8_kernel"}
 
 
 def parse():
@@ -53,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode,prefill")
+    ap.add_argument("--workloads", default="decode,prefill,decode_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-residual", action="store_true",
                     help="skip timing the residual-sublayer entry point on the same batches")
@@ -236,8 +237,12 @@ def measured_traffic(workload):
     return None
 
 
-def time_workload(name, experts, steps, warmup):
+def time_workload(name, experts, steps, warmup, experts_fp8=None):
+    """`name` is a workload of synth.WORKLOADS, or one with the suffix "_fp8": the same batch
+    through the FP8-weight entry point."""
     from grouped_top_routing_fp32_amd import synth
+    if name.endswith("_fp8"):
+        return time_wl(synth.WORKLOADS[name[:-4]], experts, steps, warmup, fp8=experts_fp8)
     return time_wl(synth.WORKLOADS[name], experts, steps, warmup)
 
 
@@ -270,7 +275,7 @@ def timed_loops(call, steps, warmup, stream):
     return total_ms, stage_ms
 
 
-def time_wl(wl, experts, steps, warmup):
+def time_wl(wl, experts, steps, warmup, fp8=None):
     import torch
     from grouped_top_routing_fp32_amd import binding, synth
 
@@ -281,7 +286,10 @@ def time_wl(wl, experts, steps, warmup):
     wg, wu, wd = experts
     bufs = binding.ForwardBuffers(d, wl.tokens, "cuda")
     stream = torch.cuda.current_stream()
-    call = lambda: binding.beam_moe_forward(d, x, wr, bias, wg, wu, wd, bufs=bufs, stream=stream)  # noqa: E731
+    if fp8 is not None:
+        call = lambda: binding.beam_moe_forward_fp8(d, x, wr, bias, *fp8, bufs=bufs, stream=stream)  # noqa: E731
+    else:
+        call = lambda: binding.beam_moe_forward(d, x, wr, bias, wg, wu, wd, bufs=bufs, stream=stream)  # noqa: E731
     total_ms, stage_ms = timed_loops(call, steps, warmup, stream)
     counts = bufs.counts.cpu()
     return dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps,
@@ -328,10 +336,13 @@ def accounting(r):
     T, H, I, E, K = wl.tokens, d.hidden, d.intermediate, d.num_experts, d.topk
     n = T * K
     nt = r["n_touched"]
+    # weight bytes per element: bf16, or E4M3 codes plus an fp32 scale per row
+    wb = 1 if r.get("fp8") else 2
+    srow = 4 if r.get("fp8") else 0
     b = {
         "router_logits": T * H * 2 + E * H * 4,
-        "gate_up": nt * 2 * I * H * 2 + T * H * 2 + n * I * 2,
-        "down": nt * H * I * 2 + n * I * 2 + n * H * 2 + n * (H // 64),
+        "gate_up": nt * 2 * I * (H * wb + srow) + T * H * 2 + n * I * 2,
+        "down": nt * H * (I * wb + srow) + n * I * 2 + n * H * 2 + n * (H // 64),
         "combine": n * H * 2 + n * (H // 64) + n * 4 + T * H * 4,
     }
     f = {
@@ -339,16 +350,16 @@ def accounting(r):
         "gate_up": 2 * n * 2 * I * H,
         "down": 2 * n * H * I,
     }
-    layer_bytes = nt * 3 * I * H * 2 + E * H * 4 + T * H * 2 + T * H * 4
+    layer_bytes = nt * 3 * I * H * wb + nt * (2 * I + H) * srow + E * H * 4 + T * H * 2 + T * H * 4
     expert_flops = 2 * n * 3 * I * H
     return b, f, layer_bytes, expert_flops
 
 
-def roofline(r, bound):
+def roofline(r, bound, name):
     b, f, layer_bytes, expert_flops = accounting(r)
     kernel = "gate_up"
     dur_s = r["stage_ms"][kernel] / 1e3
-    traffic = measured_traffic(r["wl"].name)
+    traffic = measured_traffic(name)
     if bound == "hbm":
         achieved = b[kernel] / dur_s / 1e9
         return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -484,6 +495,11 @@ def main():
     names = [w for w in args.workloads.split(",") if w]
     print(f"[bench] generating Beam expert weights (20.1 GB bf16) on the device", file=sys.stderr, flush=True)
     experts = synth.make_experts(synth.WORKLOADS["decode"], "cuda")
+    experts_fp8 = None
+    if any(n.endswith("_fp8") for n in names) and not args.sweep:
+        print(f"[bench] generating Beam FP8 expert weights (10.1 GB E4M3 + row scales) on the device",
+              file=sys.stderr, flush=True)
+        experts_fp8 = synth.make_experts_fp8(synth.WORKLOADS["decode"], "cuda")
     torch.cuda.synchronize()
     if args.copy_calibration:
         copy_calibration()
@@ -493,11 +509,12 @@ def main():
     results = {}
     for name in names:
         print(f"[bench] timing {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-        r = time_workload(name, experts, args.steps, args.warmup)
+        r = time_workload(name, experts, args.steps, args.warmup, experts_fp8)
         r["experts"] = experts
+        r["fp8"] = name.endswith("_fp8")
         results[name] = r
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step; stages {r['stage_ms']}", file=sys.stderr, flush=True)
-        if not args.no_residual:
+        if not args.no_residual and not r["fp8"]:
             r["residual"] = time_residual(r, args.steps, args.warmup)
             print(f"[bench] {name} as a residual sublayer: {r['residual']['ms_per_step']:.4f} ms/step",
                   file=sys.stderr, flush=True)
@@ -507,12 +524,13 @@ def main():
         wl = r["wl"]
         d = wl.dims
         bound = "hbm" if wl.tokens * d.topk / d.num_experts < 32 else "mfma"
-        cfg = {"workload": f"{name}: Beam MoE block forward, T={wl.tokens}", "tokens": wl.tokens,
+        what = "Beam MoE block forward" + (" with FP8 E4M3 expert weights" if r["fp8"] else "")
+        cfg = {"workload": f"{name}: {what}, T={wl.tokens}", "tokens": wl.tokens,
                "hidden": d.hidden, "intermediate": d.intermediate, "experts": d.num_experts,
                "groups": d.num_groups, "topk_groups": d.topk_groups, "topk": d.topk,
                "routed_scaling": d.routed_scaling, "router_bias": "zipf(1.2)" if wl.zipf_s else None}
         out = {"value": round(wl.tokens / (r["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
-               "ms_per_step": round(r["ms_per_step"], 4), "config": cfg, "roofline": roofline(r, bound)}
+               "ms_per_step": round(r["ms_per_step"], 4), "config": cfg, "roofline": roofline(r, bound, name)}
         out.update(layer_summary(r))
         if "residual" in r:
             out["residual_sublayer"] = r["residual"]

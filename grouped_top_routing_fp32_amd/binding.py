@@ -25,8 +25,8 @@ BEAM_MOE_ERR_WORKSPACE = -3
 BEAM_MOE_ERR_HIP = -4
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_select", "beam_moe_dispatch",
-            "beam_moe_forward", "beam_moe_residual_forward", "beam_moe_timing_enable", "beam_moe_timing_read",
-            "beam_moe_stage_name", "beam_moe_status_str")
+            "beam_moe_forward", "beam_moe_forward_fp8", "beam_moe_residual_forward", "beam_moe_timing_enable",
+            "beam_moe_timing_read", "beam_moe_stage_name", "beam_moe_status_str")
 
 SIZE_MAX = 2 ** 64 - 1
 
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.beam_moe_dispatch.restype = ctypes.c_int
     lib.beam_moe_forward.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.beam_moe_forward.restype = ctypes.c_int
+    lib.beam_moe_forward_fp8.argtypes = [pd, i32] + [vp] * 17 + [sz, vp]
+    lib.beam_moe_forward_fp8.restype = ctypes.c_int
     lib.beam_moe_residual_forward.argtypes = [pd, i32, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, vp, vp, sz, vp]
     lib.beam_moe_residual_forward.restype = ctypes.c_int
@@ -241,6 +243,40 @@ def beam_moe_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_
         _ptr(bufs.out), _ptr(bufs.ids), _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets), _ptr(bufs.slots),
         _ptr(bufs.ws), bufs.ws.numel(), _stream(stream))
     _check(st, "beam_moe_forward")
+    return bufs
+
+
+def beam_moe_forward_fp8(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],
+                         w_gate_fp8: torch.Tensor, gate_scale: torch.Tensor, w_up_fp8: torch.Tensor,
+                         up_scale: torch.Tensor, w_down_fp8: torch.Tensor, down_scale: torch.Tensor, *,
+                         select_bias: Optional[torch.Tensor] = None, bufs: Optional[ForwardBuffers] = None,
+                         stream=None) -> ForwardBuffers:
+    """The whole block with E4M3 expert weights (uint8 codes) and fp32 per-row scales."""
+    T = x.shape[0]
+    H, I, E = dims.hidden, dims.intermediate, dims.num_experts
+    _req(x, "x", torch.bfloat16, (T, H))
+    _req(w_router, "w_router", torch.float32, (E, H))
+    if logit_bias is not None:
+        _req(logit_bias, "logit_bias", torch.float32, (E,))
+    if select_bias is not None:
+        _req(select_bias, "select_bias", torch.float32, (E,))
+    _req(w_gate_fp8, "w_gate_fp8", torch.uint8, (E, I, H))
+    _req(w_up_fp8, "w_up_fp8", torch.uint8, (E, I, H))
+    _req(w_down_fp8, "w_down_fp8", torch.uint8, (E, H, I))
+    _req(gate_scale, "gate_scale", torch.float32, (E, I))
+    _req(up_scale, "up_scale", torch.float32, (E, I))
+    _req(down_scale, "down_scale", torch.float32, (E, H))
+    if bufs is None:
+        bufs = ForwardBuffers(dims, T, x.device)
+    if bufs.T != T:
+        raise ValueError("buffers were sized for another T")
+    cd = _cdims(dims)
+    st = load_library().beam_moe_forward_fp8(
+        ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate_fp8),
+        _ptr(gate_scale), _ptr(w_up_fp8), _ptr(up_scale), _ptr(w_down_fp8), _ptr(down_scale),
+        _ptr(bufs.out), _ptr(bufs.ids), _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets), _ptr(bufs.slots),
+        _ptr(bufs.ws), bufs.ws.numel(), _stream(stream))
+    _check(st, "beam_moe_forward_fp8")
     return bufs
 
 

@@ -32,6 +32,14 @@ hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const in
                               uint8_t* yscale, int H, int I, hipStream_t st);
 hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
                           hipStream_t st);
+bool stream_fp8_fits(int H, int I);
+hipError_t launch_gateup_stream_fp8(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                                    int max_tiles, const uint8_t* wg, const uint8_t* wu, const float* sg,
+                                    const float* su, uint16_t* h, uint8_t* hscale, int H, int I, int K,
+                                    hipStream_t st);
+hipError_t launch_down_stream_fp8(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                                  const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd,
+                                  uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st);
 int grouped_gemm_rows();
 bool residual_fits(int H);
 hipError_t launch_prenorm(const float* stream, const float* g_in, uint16_t* x, int T, int H, float eps,
@@ -100,7 +108,8 @@ struct Plan {
   size_t total;
 };
 
-void make_plan(const beam_moe_dims* d, int T, Plan* p) {
+// fp8: the FP8-weight expert kernels, which are stream kernels at every T.
+void make_plan(const beam_moe_dims* d, int T, Plan* p, bool fp8 = false) {
   p->T = T;
   p->H = d->hidden;
   p->I = d->intermediate;
@@ -118,7 +127,7 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p) {
   p->k_per_split = steps_per * 32;
   p->splits = (ksteps + steps_per - 1) / steps_per;
   p->units = beam::dispatch_units(p->n);
-  p->stream = use_stream_path(d, T);
+  p->stream = fp8 || use_stream_path(d, T);
   const int touched = p->E < p->n ? p->E : p->n;  // most experts with rows
   if (p->stream) {
     p->mt = kWholeExpert;
@@ -213,9 +222,15 @@ struct BlockArgs {
   const float* w_router;
   const float* logit_bias;
   const float* select_bias;
-  const uint16_t* wg;
+  const uint16_t* wg;  // bf16 experts (null for FP8 ones)
   const uint16_t* wu;
   const uint16_t* wd;
+  const uint8_t* qg;  // FP8 experts: E4M3 codes and per-row scales (null for bf16 ones)
+  const uint8_t* qu;
+  const uint8_t* qd;
+  const float* sg;
+  const float* su;
+  const float* sd;
   int32_t* topk_ids;
   float* topk_w;
   int32_t* expert_counts;
@@ -254,14 +269,20 @@ int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* w
   BEAM_TRY(beam::launch_dispatch(a.topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), a.expert_counts,
                                  a.expert_offsets, a.sorted_slots, tiles, p.mt, ntiles, st));
   BEAM_TRY(mark(ev, kStGateUp, st));
-  if (p.stream)
+  if (a.qg)
+    BEAM_TRY(beam::launch_gateup_stream_fp8(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qg, a.qu, a.sg, a.su,
+                                            h, hscale, p.H, p.I, p.K, st));
+  else if (p.stream)
     BEAM_TRY(beam::launch_gateup_stream(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wg, a.wu, h, hscale, p.H,
                                         p.I, p.K, st));
   else
     BEAM_TRY(beam::launch_gateup_grouped(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wg, a.wu, h, hscale,
                                          p.H, p.I, p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
-  if (p.stream)
+  if (a.qd)
+    BEAM_TRY(beam::launch_down_stream_fp8(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qd, a.sd, y16,
+                                          yscale, p.H, p.I, st));
+  else if (p.stream)
     BEAM_TRY(beam::launch_down_stream(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wd, y16, yscale, p.H,
                                       p.I, st));
   else
@@ -356,9 +377,68 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   Plan p;
   make_plan(d, T, &p);
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
-  BlockArgs a{static_cast<const uint16_t*>(x_bf16), w_router, logit_bias, select_bias,
-              static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
-              static_cast<const uint16_t*>(w_down), topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots};
+  BlockArgs a{static_cast<const uint16_t*>(x_bf16),
+              w_router,
+              logit_bias,
+              select_bias,
+              static_cast<const uint16_t*>(w_gate),
+              static_cast<const uint16_t*>(w_up),
+              static_cast<const uint16_t*>(w_down),
+              nullptr,
+              nullptr,
+              nullptr,
+              nullptr,
+              nullptr,
+              nullptr,
+              topk_ids,
+              topk_w,
+              expert_counts,
+              expert_offsets,
+              sorted_slots};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return run_block(
+      d, p, a, ws, st, [] { return hipSuccess; },
+      [&](const uint16_t* y16, const uint8_t* yscale) {
+        return beam::launch_combine(y16, yscale, topk_w, out, T, p.H, p.K, st);
+      });
+}
+
+int beam_moe_forward_fp8(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                         const float* logit_bias, const float* select_bias, const uint8_t* w_gate_fp8,
+                         const float* gate_scale, const uint8_t* w_up_fp8, const float* up_scale,
+                         const uint8_t* w_down_fp8, const float* down_scale, float* out, int32_t* topk_ids,
+                         float* topk_w, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK) return rc;
+  if (!beam::stream_fp8_fits(d->hidden, d->intermediate)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (T == 0) return BEAM_MOE_OK;
+  if ((rc = check_ptrs({x_bf16, w_router, w_gate_fp8, gate_scale, w_up_fp8, up_scale, w_down_fp8, down_scale, out,
+                        topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots})) != BEAM_MOE_OK)
+    return rc;
+  if ((logit_bias && !aligned16(logit_bias)) || (select_bias && !aligned16(select_bias)))
+    return BEAM_MOE_ERR_INVALID_ARG;
+  Plan p;
+  make_plan(d, T, &p, true);
+  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  BlockArgs a{static_cast<const uint16_t*>(x_bf16),
+              w_router,
+              logit_bias,
+              select_bias,
+              nullptr,
+              nullptr,
+              nullptr,
+              w_gate_fp8,
+              w_up_fp8,
+              w_down_fp8,
+              gate_scale,
+              up_scale,
+              down_scale,
+              topk_ids,
+              topk_w,
+              expert_counts,
+              expert_offsets,
+              sorted_slots};
   hipStream_t st = static_cast<hipStream_t>(stream);
   return run_block(
       d, p, a, ws, st, [] { return hipSuccess; },
@@ -388,9 +468,24 @@ int beam_moe_residual_forward(const beam_moe_dims* d, int32_t T, const float* st
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t* x = at<uint16_t>(ws, p.off_x);
-  BlockArgs a{x, w_router, logit_bias, select_bias, static_cast<const uint16_t*>(w_gate),
-              static_cast<const uint16_t*>(w_up), static_cast<const uint16_t*>(w_down), topk_ids, topk_w,
-              expert_counts, expert_offsets, sorted_slots};
+  BlockArgs a{x,
+              w_router,
+              logit_bias,
+              select_bias,
+              static_cast<const uint16_t*>(w_gate),
+              static_cast<const uint16_t*>(w_up),
+              static_cast<const uint16_t*>(w_down),
+              nullptr,
+              nullptr,
+              nullptr,
+              nullptr,
+              nullptr,
+              nullptr,
+              topk_ids,
+              topk_w,
+              expert_counts,
+              expert_offsets,
+              sorted_slots};
   return run_block(
       d, p, a, ws, st, [&] { return beam::launch_prenorm(stream_in, norm_in_weight, x, T, p.H, norm_eps, st); },
       [&](const uint16_t* y16, const uint8_t* yscale) {

@@ -300,6 +300,279 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// stream kernels with FP8 (E4M3) expert weights
+// ---------------------------------------------------------------------------
+// 「Reflection 放出 501B 的 Beam 权重：四套精度、滑动窗口和一场榜单落差」, the
+// FP8 repository's parameter-precision listing: every expert weight is E4M3;
+// the granularity of its scales is not given, taken here as one fp32 scale
+// per output row.  W[r, :] = decode(q[r, :]) * scale[r]: the codes are decoded
+// exactly to bf16 (gate/up, against bf16 activations) or fp16 (down, against
+// the fp16 activations, times the activations' 2^s) in registers, the MFMAs
+// accumulate in FP32 and the row scale multiplies the accumulator.  Half the
+// bytes of the bf16 weights for the same arithmetic.
+//
+// Stage of kF8Sk = 256 of K: weight rows of 256 bytes (256 codes) and
+// activation rows of 512 bytes (256 bf16 / fp16 values), both with 16-byte
+// chunk c of row r at position c ^ (r & 15) (activation rows keyed by their
+// index 0..7).  Per 64 of K a lane reads one 16-byte chunk of codes (16 K
+// values) and the two matching 16-byte chunks of its activation row: two
+// MFMAs of K = 32, the first on the chunk's 8 low codes, the second on its
+// 8 high ones.  A and B agree on which K each operand slot holds, which is
+// all a contraction needs.
+constexpr int kF8Sk = 256;     // K per stage
+constexpr int kF8WRow = 256;   // bytes of a staged weight row
+constexpr int kF8ARow = 512;   // bytes of a staged activation row
+constexpr int kF8Slots = 3;    // ring depth
+
+__device__ __forceinline__ int f8_woff(int row, int chunk) { return row * kF8WRow + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int f8_aoff(int row, int chunk) { return row * kF8ARow + ((chunk ^ (row & 15)) << 4); }
+
+// 16 E4M3 codes -> two operands of 8 bf16 (exact: E4M3 values are bf16 values).
+__device__ __forceinline__ void fp8x16_to_bf16(u32x4 q, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[i], 1.0f, false));
+    lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[i], 1.0f, true));
+    hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[i + 2], 1.0f, false));
+    hi[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[i + 2], 1.0f, true));
+  }
+}
+
+// 16 E4M3 codes times sc (a power of two) -> two operands of 8 fp16 (exact
+// while |value * sc| stays within fp16's range).
+__device__ __forceinline__ void fp8x16_to_f16(u32x4 q, float sc, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i], sc, false));
+    lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i], sc, true));
+    hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i + 2], sc, false));
+    hi[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i + 2], sc, true));
+  }
+}
+
+// grid: (max_tiles, I / 64); block 256; dynamic LDS SLOTS * (128 * 256 + 8 * 512) bytes.
+// Slot: 128 weight rows (0..63 gate, 64..127 up, of the workgroup's columns), then
+// the pass's 8 activation rows.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void gateup_stream_fp8_kernel(const uint16_t* __restrict__ x,
+                                                                const int32_t* __restrict__ sorted_slots,
+                                                                const Tile* __restrict__ tiles,
+                                                                const int32_t* __restrict__ ntiles,
+                                                                const uint8_t* __restrict__ wg,
+                                                                const uint8_t* __restrict__ wu,
+                                                                const float* __restrict__ sg,
+                                                                const float* __restrict__ su,
+                                                                uint16_t* __restrict__ h,
+                                                                uint8_t* __restrict__ hscale, int H, int I, int K) {
+  constexpr int kWBytes = 128 * kF8WRow;
+  constexpr int kSlot = kWBytes + kLdsRows * kF8ARow;
+  constexpr int kWCopies = 8;            // 32 weight rows of 256 bytes per wave: 4 rows per copy
+  constexpr int kCopies = kWCopies + 1;  // plus two activation rows of 512 bytes
+  extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
+  __shared__ float smax[4];
+  if ((int)blockIdx.x >= ntiles[0]) return;
+  const Tile tl = tiles[blockIdx.x];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m = lane & 15;
+  const int col = blockIdx.y * 64 + wave * 16 + m;
+  const int nsb = I / kScaleCols;
+  const int nst = H / kF8Sk;
+  const size_t ebase = (size_t)tl.expert * I * H;
+
+  // weight copies: wave w fills slot rows 32w .. 32w+31 (w < 2: gate, else up), 16 lanes a row
+  const uint8_t* wsrc[kWCopies];
+#pragma unroll
+  for (int q = 0; q < kWCopies; ++q) {
+    const int r = 32 * wave + 4 * q + (lane >> 4);
+    const uint8_t* base = (r < 64 ? wg : wu) + ebase + (size_t)(blockIdx.y * 64 + (r & 63)) * H;
+    wsrc[q] = base + (((lane & 15) ^ (r & 15)) << 4);
+  }
+  const float scale_g = sg[(size_t)tl.expert * I + col];
+  const float scale_u = su[(size_t)tl.expert * I + col];
+
+  for (int p = 0; p < tl.rows; p += kLdsRows) {
+    const int nrows = min(kLdsRows, tl.rows - p);
+    // activation copy: wave w fills activation rows 2w, 2w+1, 32 lanes a row
+    const int xr = 2 * wave + (lane >> 5);
+    const int tok = sorted_slots[tl.row_start + p + min(xr, nrows - 1)] / K;
+    const unsigned char* xsrc =
+        reinterpret_cast<const unsigned char*>(x + (size_t)tok * H) + (((lane & 31) ^ (xr & 15)) << 4);
+    auto issue = [&](int st, int slot) {
+      unsigned char* sl = ring + slot * kSlot;
+#pragma unroll
+      for (int q = 0; q < kWCopies; ++q)
+        lds_copy16(wsrc[q] + (size_t)st * kF8Sk, lds_addr(sl + (32 * wave + 4 * q) * kF8WRow));
+      lds_copy16(xsrc + (size_t)st * kF8Sk * 2, lds_addr(sl + kWBytes + 2 * wave * kF8ARow));
+    };
+    f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
+    const bool rv = m < nrows;
+    const int arow = rv ? m : 0;
+    const int grow = wave * 16 + m, urow = 64 + wave * 16 + m;
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < SLOTS - 1; ++s)
+      if (s < nst) issue(s, s);
+    for (int st = 0; st < nst; ++st) {
+      const int later = min(SLOTS - 2, nst - 1 - st);  // stages requested after stage st
+      if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();  // stage st complete for all waves; stage st - 1's slot is free
+      if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+      const unsigned char* sl = ring + (st % SLOTS) * kSlot;
+      const unsigned char* sa = sl + kWBytes;
+#pragma unroll
+      for (int j = 0; j < kF8Sk / 64; ++j) {
+        const int cw = 4 * j + (lane >> 4);
+        const u32x4 gq = *reinterpret_cast<const u32x4*>(sl + f8_woff(grow, cw));
+        const u32x4 uq = *reinterpret_cast<const u32x4*>(sl + f8_woff(urow, cw));
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw + 1));
+        u32x4 g0, g1, u0, u1;
+        fp8x16_to_bf16(gq, g0, g1);
+        fp8x16_to_bf16(uq, u0, u1);
+        const u32x4 az0 = rv ? a0 : zero, az1 = rv ? a1 : zero;
+        ag = mfma16x16x32(az0, g0, ag);
+        au = mfma16x16x32(az0, u0, au);
+        ag = mfma16x16x32(az1, g1, ag);
+        au = mfma16x16x32(az1, u1, au);
+      }
+    }
+    // row scales, then SwiGLU in FP32; one power-of-two scale per (pass, 64 columns)
+    float v[4];
+    float mx = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = (lane >> 4) * 4 + r;
+      v[r] = (row < nrows) ? silu_f32(ag[r] * scale_g) * (au[r] * scale_u) : 0.f;
+      mx = fmaxf(mx, fabsf(v[r]));
+    }
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
+    __syncthreads();  // also: every wave is done with the ring before the next pass refills it
+    const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = (lane >> 4) * 4 + r;
+      if (row < nrows) {
+        const size_t gr = (size_t)(tl.row_start + p + row);
+        h[gr * I + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(v[r], -sexp));
+        if (wave == 0 && m == 0) hscale[gr * nsb + blockIdx.y] = (uint8_t)sexp;
+      }
+    }
+    __syncthreads();  // smax is rewritten by the next pass
+  }
+}
+
+// grid: (max_tiles, H / 64); block 256; dynamic LDS SLOTS * (64 * 256 + 8 * 512) bytes + the
+// pass's scales.  Slot: 64 W_down rows of the workgroup's columns, then the pass's 8 h rows.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void down_stream_fp8_kernel(const uint16_t* __restrict__ h,
+                                                              const uint8_t* __restrict__ hscale,
+                                                              const int32_t* __restrict__ sorted_slots,
+                                                              const Tile* __restrict__ tiles,
+                                                              const int32_t* __restrict__ ntiles,
+                                                              const uint8_t* __restrict__ wd,
+                                                              const float* __restrict__ sd,
+                                                              uint16_t* __restrict__ y16,
+                                                              uint8_t* __restrict__ yscale, int H, int I) {
+  constexpr int kWBytes = 64 * kF8WRow;
+  constexpr int kSlot = kWBytes + kLdsRows * kF8ARow;
+  constexpr int kWCopies = 4;            // 16 weight rows of 256 bytes per wave
+  constexpr int kCopies = kWCopies + 1;  // plus two activation rows of 512 bytes
+  extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
+  __shared__ int sany;
+  __shared__ float smax[4];
+  uint8_t* ssc = ring + SLOTS * kSlot;  // the pass's activation scales
+  if ((int)blockIdx.x >= ntiles[0]) return;
+  const Tile tl = tiles[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m = lane & 15;
+  const int col = blockIdx.y * 64 + wave * 16 + m;
+  const int nsb = I / kScaleCols;
+  const int nst = I / kF8Sk;
+
+  const uint8_t* wsrc[kWCopies];
+#pragma unroll
+  for (int q = 0; q < kWCopies; ++q) {
+    const int r = 16 * wave + 4 * q + (lane >> 4);
+    const uint8_t* base = wd + (size_t)tl.expert * H * I + (size_t)(blockIdx.y * 64 + r) * I;
+    wsrc[q] = base + (((lane & 15) ^ (r & 15)) << 4);
+  }
+  const float scale_d = sd[(size_t)tl.expert * H + col];
+
+  for (int p = 0; p < tl.rows; p += kLdsRows) {
+    const int nrows = min(kLdsRows, tl.rows - p);
+    const int xr = 2 * wave + (lane >> 5);
+    const unsigned char* xsrc =
+        reinterpret_cast<const unsigned char*>(h + (size_t)(tl.row_start + p + min(xr, nrows - 1)) * I) +
+        (((lane & 31) ^ (xr & 15)) << 4);
+    auto issue = [&](int st, int slot) {
+      unsigned char* sl = ring + slot * kSlot;
+#pragma unroll
+      for (int q = 0; q < kWCopies; ++q)
+        lds_copy16(wsrc[q] + (size_t)st * kF8Sk, lds_addr(sl + (16 * wave + 4 * q) * kF8WRow));
+      lds_copy16(xsrc + (size_t)st * kF8Sk * 2, lds_addr(sl + kWBytes + 2 * wave * kF8ARow));
+    };
+#pragma unroll
+    for (int s = 0; s < SLOTS - 1; ++s)
+      if (s < nst) issue(s, s);
+    if (tid == 0) sany = 0;
+    __syncthreads();
+    for (int i = tid; i < nsb; i += 256) {
+      const uint8_t sv = hscale[(size_t)(tl.row_start + p) * nsb + i];
+      ssc[i] = sv;
+      if (sv) sany = 1;
+    }
+    __syncthreads();
+    const bool scaled = sany != 0;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool rv = m < nrows;
+    const int arow = rv ? m : 0;
+    const int brow = wave * 16 + m;
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+    for (int st = 0; st < nst; ++st) {
+      const int later = min(SLOTS - 2, nst - 1 - st);
+      if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+      const unsigned char* sl = ring + (st % SLOTS) * kSlot;
+      const unsigned char* sa = sl + kWBytes;
+#pragma unroll
+      for (int j = 0; j < kF8Sk / 64; ++j) {
+        const int cw = 4 * j + (lane >> 4);
+        const u32x4 bq = *reinterpret_cast<const u32x4*>(sl + f8_woff(brow, cw));
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw + 1));
+        // the 64 K values of step j share one activation scale block
+        const float sc = scaled ? __builtin_amdgcn_ldexpf(1.0f, ssc[(st * kF8Sk) / kScaleCols + j]) : 1.0f;
+        u32x4 b0, b1;
+        fp8x16_to_f16(bq, sc, b0, b1);
+        acc = mfma16x16x32_f16(rv ? a0 : zero, b0, acc);
+        acc = mfma16x16x32_f16(rv ? a1 : zero, b1, acc);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] *= scale_d;
+    store_y_pass(acc, nrows, sorted_slots + tl.row_start + p, y16, yscale, H, col, smax);
+    __syncthreads();  // every wave is done with the ring and the scales before the next pass
+  }
+}
+
 // LDS of one gfx950 compute unit, the most one workgroup can take.
 constexpr size_t kLdsBytesPerCU = 160 * 1024;
 
@@ -313,6 +586,45 @@ size_t down_stream_lds_bytes(int I) {
 bool stream_fits(int H, int I) {
   return H % kSk == 0 && I % kSk == 0 && gateup_stream_lds_bytes() <= kLdsBytesPerCU &&
          down_stream_lds_bytes(I) <= kLdsBytesPerCU;
+}
+
+size_t gateup_stream_fp8_lds_bytes() { return (size_t)kF8Slots * (128 * kF8WRow + kLdsRows * kF8ARow); }
+size_t down_stream_fp8_lds_bytes(int I) {
+  return (size_t)kF8Slots * (64 * kF8WRow + kLdsRows * kF8ARow) + I / kScaleCols;
+}
+
+// Whether the FP8 stream kernels can run at this shape: K of both projections
+// in whole 256-value stages, and the staged rows and scales fit in LDS.
+bool stream_fp8_fits(int H, int I) {
+  return H % kF8Sk == 0 && I % kF8Sk == 0 && gateup_stream_fp8_lds_bytes() <= kLdsBytesPerCU &&
+         down_stream_fp8_lds_bytes(I) <= kLdsBytesPerCU;
+}
+
+hipError_t launch_gateup_stream_fp8(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                                    int max_tiles, const uint8_t* wg, const uint8_t* wu, const float* sg,
+                                    const float* su, uint16_t* h, uint8_t* hscale, int H, int I, int K,
+                                    hipStream_t st) {
+  dim3 grid(max_tiles, I / 64);
+  const size_t bytes = gateup_stream_fp8_lds_bytes();
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<kF8Slots>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gateup_stream_fp8_kernel<kF8Slots>), grid, dim3(256), bytes, st, x, slots, tiles, ntiles, wg,
+                     wu, sg, su, h, hscale, H, I, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_stream_fp8(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                                  const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd,
+                                  uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st) {
+  dim3 grid(max_tiles, H / 64);
+  const size_t bytes = down_stream_fp8_lds_bytes(I);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_stream_fp8_kernel<kF8Slots>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((down_stream_fp8_kernel<kF8Slots>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
+                     ntiles, wd, sd, y16, yscale, H, I);
+  return hipGetLastError();
 }
 
 // Launchers of the stream path (passes of kLdsRows rows; requires stream_fits).

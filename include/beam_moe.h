@@ -73,8 +73,8 @@ enum {
   BEAM_MOE_ERR_HIP = -4          /* a HIP launch failed                          */
 };
 
-/* Bytes of workspace that beam_moe_route, beam_moe_dispatch and
- * beam_moe_forward need for T tokens (one size serves all three; it grows
+/* Bytes of workspace that beam_moe_route, beam_moe_dispatch and the forward
+ * entry points need for T tokens (one size serves all of them; it grows
  * linearly in T: at Beam dims about 132 KB per token, mostly the fp16 SwiGLU
  * activations [T*K, I] and the fp16 expert outputs [T*K, H], each with a
  * power-of-two scale per 64 columns).
@@ -142,6 +142,32 @@ int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, c
                      const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
                      int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole block with FP8 expert weights (steps 1-5 as beam_moe_forward).
+ * The FP8 checkpoint of the model stores every expert weight as E4M3 and keeps
+ * the router out of the quantisation (「Reflection 放出 501B 的 Beam 权重：四套
+ * 精度、滑动窗口和一场榜单落差」, its parameter-precision listing of the FP8
+ * repository); the scale granularity is not given there and is taken as one
+ * fp32 scale per output row:  W[e][r, :] = e4m3(q[e][r, :]) * scale[e][r].
+ *   w_gate_fp8, w_up_fp8  [E, I, H] uint8 E4M3 codes (OCP FP8 E4M3: bias 7,
+ *                         no infinities, 0x7F / 0xFF are NaN and must not occur)
+ *   gate_scale, up_scale  [E, I] fp32
+ *   w_down_fp8            [E, H, I] uint8 E4M3 codes;  down_scale [E, H] fp32
+ *   other arguments as in beam_moe_forward (the router stays FP32).
+ * Precision: the codes are decoded exactly to bf16 (gate/up, against the bf16
+ * x) or fp16 (down, against the fp16 activations) in registers; products
+ * accumulate in FP32 and the row scale multiplies the accumulated sum; the
+ * rest as in beam_moe_forward.  The expert kernels are the few-rows-per-expert
+ * ones at every T: built for decode-sized batches, correct but slower than
+ * the bf16 grouped GEMMs once experts see many rows.
+ * Supported sizes additionally satisfy hidden % 256 == 0 and
+ * intermediate % 256 == 0; the workspace is beam_moe_workspace_bytes(dims, T). */
+int beam_moe_forward_fp8(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                         const float* logit_bias, const float* select_bias, const uint8_t* w_gate_fp8,
+                         const float* gate_scale, const uint8_t* w_up_fp8, const float* up_scale,
+                         const uint8_t* w_down_fp8, const float* down_scale, float* out, int32_t* topk_ids,
+                         float* topk_w, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* The block as a residual sublayer at step `step` of the stream
  * (「Reflection 发布 Beam 501B 开源模型，支持 1M tokens 上下文」, section 残差流:
  * the input embedding is step 1; at step k a sublayer's output enters with
@@ -167,8 +193,9 @@ int beam_moe_residual_forward(const beam_moe_dims* dims, int32_t T, const float*
                               int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
                               int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
-/* Diagnostics: device time of the stages of beam_moe_forward and
- * beam_moe_residual_forward ("prenorm" is zero for the former).
+/* Diagnostics: device time of the stages of beam_moe_forward,
+ * beam_moe_forward_fp8 and beam_moe_residual_forward ("prenorm" is empty
+ * except in the last).
  * beam_moe_timing_enable(1) makes later calls of either record HIP
  * events between their stages on the caller's stream (a marker per stage,
  * no synchronisation; the events are created by the library on first use and

@@ -30,26 +30,40 @@ def f64(t: torch.Tensor) -> np.ndarray:
 class Problem:
     """Inputs of one workload, generated on the device with the shared generator."""
 
-    def __init__(self, wl: synth.Workload, device="cuda", experts=None, select_bias=None):
+    def __init__(self, wl: synth.Workload, device="cuda", experts=None, select_bias=None, fp8=False):
         self.wl = wl
         self.dims = wl.dims
         self.x = synth.make_x(wl, device)
         self.wr = synth.make_router(wl, device)
         self.bias = synth.make_bias(wl, device)
         self.select_bias = select_bias  # fp32 [E] device tensor or None
-        if experts is None and not wl.router_only:
+        self.fp8 = fp8
+        if fp8:
+            # (q_gate, s_gate, q_up, s_up, q_down, s_down) of every expert
+            self.q = experts if experts is not None else synth.make_experts_fp8(wl, device)
+            experts = None
+        elif experts is None and not wl.router_only:
             experts = synth.make_experts(wl, device)
         self.wg, self.wu, self.wd = experts if experts is not None else (None, None, None)
         self._cache = {}
 
     def expert_f64(self, e: int):
         if e not in self._cache:
-            self._cache[e] = (f64(self.wg[e]), f64(self.wu[e]), f64(self.wd[e]))
+            if self.fp8:
+                qg, sg, qu, su, qd, sd = (t[e].cpu().numpy() for t in self.q)
+                self._cache[e] = orc.fp8_expert(qg, sg, qu, su, qd, sd)
+            else:
+                self._cache[e] = (f64(self.wg[e]), f64(self.wu[e]), f64(self.wd[e]))
         return self._cache[e]
 
     def route_oracle(self, tokens=None):
         """(X, ids, w, C, GS, margins) of the oracle; C = the selection values (S, or S + select_bias)."""
         d = self.dims
+        if tokens is not None:
+            # checked on the host: an index past the batch would trip the device-side gather's assert
+            tok = np.asarray(tokens)
+            if tok.size and (tok.min() < 0 or tok.max() >= self.x.shape[0]):
+                raise IndexError(f"token sample {tok.tolist()} outside a batch of {self.x.shape[0]}")
         X = f64(self.x if tokens is None else self.x[torch.as_tensor(tokens, device=self.x.device)])
         bias = None if self.bias is None else f64(self.bias)
         sb = None if self.select_bias is None else f64(self.select_bias)

@@ -20,7 +20,7 @@ FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation f
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(beam_moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(beam_moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_abi():
@@ -166,3 +166,34 @@ def test_residual_forward_validation():
     assert _residual(lib, binding._cdims(TINY), 0, ptrs={k: None for k in ("stream_in", "w_router", "gate", "up",
                      "down", "stream_out", "ids", "w", "counts", "offsets", "slots", "ws")}, ws_bytes=0) == \
         binding.BEAM_MOE_OK
+
+
+_FP8_PTRS = ("x", "w_router", "logit_bias", "select_bias", "q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down",
+             "out", "ids", "w", "counts", "offsets", "slots", "ws")
+_FP8_OPTIONAL = ("logit_bias", "select_bias")
+
+
+def _fp8(lib, cd, T, ptrs=None, ws_bytes=1 << 40):
+    p = ptrs if ptrs is not None else {}
+    args = [p.get(k, None if k in _FP8_OPTIONAL else FAKE) for k in _FP8_PTRS]
+    return lib.beam_moe_forward_fp8(ctypes.byref(cd), T, *args[:16], args[16], ws_bytes, None)
+
+
+def test_forward_fp8_validation():
+    lib = binding.load_library()
+    cd = binding._cdims(BEAM)
+    for name in _FP8_PTRS[:-1]:
+        if name in _FP8_OPTIONAL:
+            assert _fp8(lib, cd, 64, ptrs={name: ctypes.c_void_p((1 << 20) + 4)}) == \
+                binding.BEAM_MOE_ERR_INVALID_ARG, name
+        else:
+            assert _fp8(lib, cd, 64, ptrs={name: None}) == binding.BEAM_MOE_ERR_INVALID_ARG, name
+            assert _fp8(lib, cd, 64, ptrs={name: ctypes.c_void_p((1 << 20) + 8)}) == \
+                binding.BEAM_MOE_ERR_INVALID_ARG, name
+    assert _fp8(lib, cd, 64, ws_bytes=1) == binding.BEAM_MOE_ERR_WORKSPACE
+    assert _fp8(lib, cd, 64, ptrs={"ws": None}) == binding.BEAM_MOE_ERR_WORKSPACE
+    # K of each projection must be whole 256-value stages
+    assert _fp8(lib, binding._cdims(Dims(5120, 2432, 256, 8, 4, 8)), 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert _fp8(lib, binding._cdims(Dims(256, 128, 16, 4, 2, 4)), 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert _fp8(lib, cd, -1) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert _fp8(lib, cd, 0, ptrs={k: None for k in _FP8_PTRS}, ws_bytes=0) == binding.BEAM_MOE_OK

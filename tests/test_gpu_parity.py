@@ -28,6 +28,14 @@ def _announce(name):
 
 
 @pytest.fixture(scope="module")
+def beam_experts_fp8():
+    _announce("generate Beam FP8 expert weights on the device")
+    ex = synth.make_experts_fp8(synth.WORKLOADS["decode"], DEV)
+    torch.cuda.synchronize()
+    return ex
+
+
+@pytest.fixture(scope="module")
 def beam_experts():
     _announce("generate Beam expert weights on the device")
     wl = synth.WORKLOADS["decode"]
@@ -204,6 +212,12 @@ MID = {
     # stream path, I/32 not a multiple of 8
     "mid_stream_i384": (synth.Workload("mid_stream_i384", 40, synth.Dims(512, 384, 64, 8, 4, 4),
                                        router_sigma=0.06), None),
+    # large activations (expert weights N(0, 10^2)): the SwiGLU activations and the expert
+    # outputs exceed 2^15 and travel to the next step with a power-of-two scale
+    "mid_stream_big": (synth.Workload("mid_stream_big", 40, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
+                                      expert_sigma=10.0), None),
+    "mid_tiled_big": (synth.Workload("mid_tiled_big", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06,
+                                     expert_sigma=10.0), None),
     # grouped path just above the stream threshold (about 9 rows per expert) with skew:
     # mostly near-empty tiles, whose idle waves copy no activations
     "mid_grouped_skew": (synth.Workload("mid_grouped_skew", 150, synth.Dims(512, 256, 64, 8, 4, 4),
@@ -401,6 +415,84 @@ def test_residual_beam(beam_experts, T):
     _announce(f"residual Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
     p, stream, g_in, g_out, bufs = _residual_case(wl, 3, True, experts=beam_experts)
-    sample = sorted({0, 1, 2, 3, T // 2, T - 1})
+    sample = sorted({t for t in (0, 1, 2, 3, T // 2, T - 1) if t < T})
     excluded, worst = residual_parity(p, stream, 3, bufs, sample, g_in=g_in, g_out=g_out)
     print(f"  sampled {len(sample)} tokens, excluded {excluded}, worst error / tolerance {worst:.3f}")
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) expert weights with per-row scales
+# --------------------------------------------------------------------------
+def test_fp8_generator_bits_match_cpu():
+    _announce("fp8 generator cpu vs gpu")
+    wl = synth.WORKLOADS["decode"]
+    g = synth.expert_weights_fp8(wl, 5, DEV)
+    c = synth.expert_weights_fp8(wl, 5, "cpu")
+    for a, b in zip(g, c):
+        assert torch.equal(a.cpu(), b)
+
+
+FP8 = {
+    "f8_small": synth.Workload("f8_small", 16, synth.Dims(256, 256, 16, 4, 2, 4), router_sigma=1.0 / 16.0),
+    # several column blocks, experts with more than one 8-row pass
+    "f8_stream": synth.Workload("f8_stream", 40, synth.Dims(512, 512, 64, 8, 4, 6), router_sigma=0.06),
+    # skewed routing: hot experts run many passes
+    "f8_skew": synth.Workload("f8_skew", 60, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06, zipf_s=1.2),
+    # about 75 rows per expert: the FP8 kernels at a batch the bf16 path would give the grouped GEMMs
+    "f8_many_rows": synth.Workload("f8_many_rows", 300, synth.Dims(512, 256, 16, 4, 2, 4), router_sigma=0.06),
+    # large activations: h and y travel with power-of-two scales, codes are converted times 2^s
+    "f8_big": synth.Workload("f8_big", 40, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06, expert_sigma=10.0),
+}
+
+
+@pytest.mark.parametrize("name", list(FP8))
+def test_forward_fp8(name):
+    _announce(f"forward fp8 {name} (all tokens)")
+    p = Problem(FP8[name], DEV, fp8=True)
+    bufs = binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q)
+    excluded, worst = forward_parity(p, bufs)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+    out1 = bufs.out.clone()
+    binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q, bufs=bufs)
+    assert torch.equal(out1, bufs.out)
+
+
+def test_forward_fp8_routing_matches_bf16_entry():
+    # the router does not see the expert weights: both entry points route and dispatch alike
+    _announce("fp8 and bf16 entry points route alike")
+    wl = FP8["f8_stream"]
+    p = Problem(wl, DEV, fp8=True)
+    wg, wu, wd = synth.make_experts(wl, DEV)
+    b16 = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, wg, wu, wd)
+    b8 = binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q)
+    for name in ("ids", "w", "counts", "offsets", "slots"):
+        assert torch.equal(getattr(b16, name), getattr(b8, name)), name
+
+
+def test_forward_fp8_rejects_unsupported_intermediate():
+    wl = MID["mid_stream"][0]  # intermediate 384: not a whole number of 256-value stages
+    d = wl.dims
+    x = synth.make_x(wl, DEV)
+    wr = synth.make_router(wl, DEV)
+    E, I, H = d.num_experts, d.intermediate, d.hidden
+    q = (torch.zeros((E, I, H), dtype=torch.uint8, device=DEV), torch.ones((E, I), device=DEV),
+         torch.zeros((E, I, H), dtype=torch.uint8, device=DEV), torch.ones((E, I), device=DEV),
+         torch.zeros((E, H, I), dtype=torch.uint8, device=DEV), torch.ones((E, H), device=DEV))
+    with pytest.raises(binding.BeamMoeError) as ei:
+        binding.beam_moe_forward_fp8(d, x, wr, None, *q)
+    assert ei.value.status == binding.BEAM_MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("T", [1, 64, 512])
+def test_forward_fp8_beam(beam_experts_fp8, T):
+    _announce(f"forward fp8 Beam T={T}")
+    wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
+    p = Problem(wl, DEV, experts=beam_experts_fp8, fp8=True)
+    bufs = binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q)
+    torch.cuda.synchronize()
+    sample = sorted({t for t in (0, 1, T // 3, T // 2, T - 1) if t < T})
+    excluded, worst = forward_parity(p, bufs, sample)
+    print(f"  sampled {len(sample)} tokens, excluded {excluded}, worst error / tolerance {worst:.3f}")
+    out1 = bufs.out.clone()
+    binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q, bufs=bufs)
+    assert torch.equal(out1, bufs.out)
