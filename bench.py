@@ -116,11 +116,11 @@ def summarize_pmc(fetch_dir, write_dir):
 
     f_scale = COPY_BYTES / 1024.0 / copy_kib(fetch)
     w_scale = COPY_BYTES / 1024.0 / copy_kib(write)
-    lines = ["# HBM traffic per launch of the gate/up kernel, from rocprofv3 counters",
+    lines = ["# HBM traffic per launch of the gate/up kernel (decode, prefill, FP8 decode), from rocprofv3 counters",
              "# fetch:  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-residual --copy-calibration",
              "# write:  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-residual --copy-calibration",
              "# summary: python3 bench.py --summarize-pmc <FETCH_DIR> <WRITE_DIR>",
              f"# calibration: elementwise copy (torch.neg) of {COPY_BYTES} bytes read and written;"
              f" FETCH_SIZE reads {copy_kib(fetch):.0f} KiB (scale {f_scale:.4f}),"
@@ -167,8 +167,10 @@ def summarize_sweep(sweep_json, out_md):
 def summarize_trace(trace_dir, out_md):
     """Per-workload kernel durations of the library's kernels from a kernel-trace run of this script.
 
-    Forward calls are cut at each router_logits_kernel dispatch; a call is a prefill
-    call if it ran the grouped GEMM, a decode call if it ran a stream kernel."""
+    Calls are cut before each router_logits_kernel dispatch, or before the prenorm_kernel that
+    opens a residual-sublayer call.  A call that ran the grouped GEMM is prefill, one that ran
+    the FP8 kernels decode_fp8, the others decode; residual-sublayer calls (prenorm present)
+    get a section of their own."""
     import csv
     import glob
     path = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))[0]
@@ -177,7 +179,10 @@ def summarize_trace(trace_dir, out_md):
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     calls, cur = [], []
     for r in rows:
-        if "router_logits_kernel" in r["Kernel_Name"] and cur:
+        name = r["Kernel_Name"]
+        opens = "prenorm_kernel" in name or (
+            "router_logits_kernel" in name and not (cur and "prenorm_kernel" in cur[-1]["Kernel_Name"]))
+        if opens and cur:
             calls.append(cur)
             cur = []
         cur.append(r)
@@ -188,22 +193,29 @@ def summarize_trace(trace_dir, out_md):
         name = name.replace("void ", "")
         return name[:name.index("(")] if "(" in name else name
 
+    def kind(c):
+        names = " ".join(r["Kernel_Name"] for r in c)
+        wl = "prefill" if "grouped_gemm" in names else ("decode_fp8" if "_fp8_kernel" in names else "decode")
+        return wl + (", residual sublayer" if "prenorm_kernel" in names else "")
+
     per = {}
     for c in calls:
-        wl = "prefill" if any("grouped_gemm" in r["Kernel_Name"] for r in c) else "decode"
+        wl = kind(c)
         for r in c:
             us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             per.setdefault(wl, {}).setdefault(short(r["Kernel_Name"]), []).append(us)
-    out = ["# rocprofv3 kernel times: Beam MoE block forward, decode T=64 and prefill T=16384", "",
-           "Command (repository root on the GPU host):", "", "```",
+    out = ["# rocprofv3 kernel times: Beam MoE block forward, decode T=64, prefill T=16384, FP8 decode T=64",
+           "", "Command (repository root on the GPU host):", "", "```",
            "cd /tmp && export TMPDIR=/tmp",
            "rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- \\",
            "    python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
            "python3 bench.py --summarize-trace <TRACE_DIR> <this file>", "```", "",
-           "Each forward call is cut at its router_logits_kernel dispatch; calls that ran the grouped GEMM are",
-           "prefill, the others decode.  Warmup and timed calls are both counted.  Durations are the",
-           "dispatch end minus start timestamps.", ""]
-    for wl in ("decode", "prefill"):
+           "Calls are cut before each router_logits_kernel dispatch (before the prenorm_kernel of a",
+           "residual-sublayer call); calls that ran the grouped GEMM are prefill, those that ran the FP8",
+           "kernels decode_fp8, the others decode.  Warmup and timed calls, with and without the stage",
+           "markers, are all counted.  Durations are the dispatch end minus start timestamps.", ""]
+    order = ["decode", "prefill", "decode_fp8", "decode, residual sublayer", "prefill, residual sublayer"]
+    for wl in order + sorted(k for k in per if k not in order):
         if wl not in per:
             continue
         ks = per[wl]
