@@ -15,7 +15,8 @@ import torch
 
 from grouped_top_routing_fp32_amd import binding, synth
 from oracle import beam_moe_oracle as orc
-from parity_helpers import Problem, check_dispatch_valid, compare_routing, f64, forward_parity, residual_parity
+from parity_helpers import (Problem, check_dispatch_valid, compare_outputs, compare_routing, f64, forward_parity,
+                            residual_parity)
 
 pytestmark = pytest.mark.gpu
 
@@ -289,6 +290,52 @@ def test_forward_beam_sizes(beam_experts, T):
     _announce(f"forward Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
     _beam_forward_wl(wl, beam_experts, sorted({0, T // 2, T - 1}))
+
+
+# Degenerate and extreme shapes of the method through the whole block (all tokens).
+EDGE = {
+    # one expert, one group, top-1: the block is 2.5 x a dense SwiGLU (stream path, then grouped
+    # with three tiles of 256, 256 and 88 rows)
+    "dense_stream": synth.Workload("dense_stream", 3, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06),
+    "dense_grouped": synth.Workload("dense_grouped", 600, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06),
+    # the largest top-k, on both paths
+    "topk16_stream": synth.Workload("topk16_stream", 16, synth.Dims(256, 128, 64, 8, 8, 16), router_sigma=0.06),
+    "topk16_grouped": synth.Workload("topk16_grouped", 200, synth.Dims(256, 128, 64, 8, 8, 16), router_sigma=0.06),
+    # no grouping (one group), every group kept (plain top-k), one expert per group
+    "one_group": synth.Workload("one_group", 24, synth.Dims(256, 128, 64, 1, 1, 8), router_sigma=0.06),
+    "all_groups": synth.Workload("all_groups", 24, synth.Dims(256, 128, 64, 8, 8, 8), router_sigma=0.06),
+    "group_of_one": synth.Workload("group_of_one", 24, synth.Dims(256, 128, 16, 16, 6, 4), router_sigma=0.06),
+    # the largest intermediate size the library takes, with a wide hidden size
+    "wide": synth.Workload("wide", 12, synth.Dims(2048, 32768, 2, 1, 1, 1), router_sigma=0.03),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_forward_edge_dims(name):
+    _announce(f"forward {name} (all tokens)")
+    p = Problem(EDGE[name], DEV)
+    bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
+    excluded, worst = forward_parity(p, bufs)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+
+
+def test_forward_dense_is_scaled_swiglu():
+    # with one expert every token takes it with weight 2.5: out = 2.5 * SwiGLU(x), checked
+    # against the oracle's dense expert directly (no routing step)
+    _announce("forward dense = 2.5 x SwiGLU")
+    p = Problem(EDGE["dense_grouped"], DEV)
+    bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
+    assert torch.all(bufs.ids == 0) and torch.all(bufs.w == 2.5)
+    want = 2.5 * orc.swiglu_expert(f64(p.x), *p.expert_f64(0))
+    compare_outputs(bufs.out.cpu().numpy().astype(np.float64), want, np.ones(want.shape[0], dtype=bool))
+
+
+def test_forward_empty_batch():
+    _announce("forward T=0")
+    wl = synth.with_tokens(synth.WORKLOADS["tiny"], 0)
+    p = Problem(wl, DEV)
+    bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
+    assert bufs.out.shape == (0, p.dims.hidden) and bufs.ids.shape == (0, p.dims.topk)
 
 
 # --------------------------------------------------------------------------
