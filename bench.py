@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the decode/prefill line: tokens/s and roofline fractions over batch sizes T")
     ap.add_argument("--sweep-tokens", default="1,2,4,8,16,32,64,128,256,512,1024,2048,4096,8192,16384")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_DIR", "OUT_MD"),
+                    help="per-kernel counter summary of a rocprofv3 --pmc run of this script")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="time the GEMM library on the prefill MoE shapes (context for the grouped GEMMs) and exit")
     ap.add_argument("--summarize-sweep", nargs=2, metavar=("SWEEP_JSON", "OUT_MD"),
                     help="write a markdown table from a --sweep JSON line and exit")
     return ap.parse_args()
@@ -471,6 +475,94 @@ def sweep(args, experts):
                       "points": points}), flush=True)
 
 
+def summarize_counters(counter_dir, out_md):
+    """Per-kernel means of every counter of a rocprofv3 --pmc run of this script, plus the
+    derived MFMA-busy and wave-wait fractions where their counters were collected."""
+    import csv
+    import glob
+    per, order = {}, []
+    for path in sorted(glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path) as f:
+            disp = {}
+            for r in csv.DictReader(f):
+                if "beam::" not in r["Kernel_Name"]:
+                    continue
+                d = disp.setdefault(r["Dispatch_Id"], {"kernel": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            for d in disp.values():
+                name = d.pop("kernel").replace("void ", "")
+                name = name[:name.index("(")] if "(" in name else name
+                if name not in per:
+                    order.append(name)
+                per.setdefault(name, []).append(d)
+    simds, xcds = 256 * 4, 8
+    cmd = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+           "SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_LDS_DATA_FIFO_FULL GRBM_GUI_ACTIVE --output-format csv "
+           "-d <COUNTER_DIR> -o run -- python3 bench.py --workloads prefill,decode --steps 2 --warmup 1 "
+           "--no-cpu-baseline --no-residual")
+    out = ["# rocprofv3 counters per kernel: Beam MoE block forward, prefill T=16384 and decode T=64", "",
+           "Commands (repository root on the GPU host, after `cd /tmp && export TMPDIR=/tmp`):", "", "```", cmd,
+           "python3 bench.py --summarize-counters <COUNTER_DIR> <this file>", "```", "",
+           "Values are per dispatch, each counter summed over the dimensions rocprofv3 reports it in, then",
+           "averaged over the dispatches.  Derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x",
+           "GRBM_GUI_ACTIVE / 8 XCDs), the share of every SIMD's cycles its matrix unit was busy; wave wait =",
+           "SQ_WAIT_ANY / SQ_WAVE_CYCLES, the share of wave time spent waiting (on memory counters or a barrier).",
+           ""]
+    for name in order:
+        rows = per[name]
+        keys = sorted({k for d in rows for k in d})
+        mean = {k: sum(d.get(k, 0.0) for d in rows) / len(rows) for k in keys}
+        out += [f"## `{name}` ({len(rows)} dispatches)", "", "| counter | mean per dispatch |", "|---|---|"]
+        out += [f"| {k} | {mean[k]:.4g} |" for k in keys]
+        if mean.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            out.append(f"| MFMA busy (derived) | {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / simds / (mean['GRBM_GUI_ACTIVE'] / xcds):.3f} |")
+        if mean.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in mean:
+            out.append(f"| wave wait (derived) | {mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.3f} |")
+        out.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+
+
+def gemm_reference():
+    """Context for the prefill GEMMs: the platform's GEMM library (torch.bmm / linear on bf16,
+    contiguous operands) on the MoE shapes of the prefill batch, 256 experts x 512 rows."""
+    import torch
+    E, R, H, I = 256, 512, 5120, 2560
+
+    def t(fn, flops, name):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(10):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / 10
+        return {"case": name, "ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
+                "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+
+    g = torch.Generator(device="cuda").manual_seed(0)
+    res = []
+    a = torch.randn(E, R, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(E, H, 2 * I, device="cuda", dtype=torch.bfloat16, generator=g)
+    res.append(t(lambda: torch.bmm(a, b), 2 * E * R * H * 2 * I, "bmm 256 x (512x5120 @ 5120x5120): gate/up shape"))
+    del a, b
+    a = torch.randn(E, R, I, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(E, I, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    res.append(t(lambda: torch.bmm(a, b), 2 * E * R * I * H, "bmm 256 x (512x2560 @ 2560x5120): down shape"))
+    del a, b
+    a = torch.randn(E * R, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    w = torch.randn(2 * I, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    res.append(t(lambda: torch.nn.functional.linear(a, w), 2 * E * R * H * 2 * I,
+                 "linear 131072x5120 @ (5120x5120)^T: one dense GEMM of the same work"))
+    del a, w
+    torch.cuda.empty_cache()
+    print(json.dumps({"gemm_reference": res}), flush=True)
+
+
 def copy_calibration():
     """A plain elementwise copy of COPY_BYTES (read once, written once), outside any timed region."""
     import torch
@@ -491,6 +583,9 @@ def main():
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
         return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.summarize_sweep:
         summarize_sweep(*args.summarize_sweep)
         return
@@ -504,6 +599,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.gemm_reference:
+        gemm_reference()
+        return
     names = [w for w in args.workloads.split(",") if w]
     print(f"[bench] generating Beam expert weights (20.1 GB bf16) on the device", file=sys.stderr, flush=True)
     experts = synth.make_experts(synth.WORKLOADS["decode"], "cuda")
