@@ -45,8 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_hbm_traffic_decode_prefil
 KERNEL_SOURCES = ["grouped_top_routing_fp32_amd/csrc/" + f
                   for f in ("common.h", "experts.hip", "grouped_gemm.hip", "dispatch.hip", "abi.cpp")]
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
-GATE_UP_KERNELS = {"decode": "gateup_stream_lds_kernel", "prefill": "grouped_gemm_kernel<true>",
-                   "decode_fp8": "gateup_stream_fp8_kernel"}
+GATE_UP_KERNELS = {"decode": "gateup_stream_lds_kernel", "prefill": "grouped_gemm_kernel<true, false>",
+                   "decode_fp8": "gateup_stream_fp8_kernel", "prefill_fp8": "grouped_gemm_kernel<true, true>"}
 
 
 def parse():
@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode,prefill,decode_fp8")
+    ap.add_argument("--workloads", default="decode,prefill,decode_fp8,prefill_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-residual", action="store_true",
                     help="skip timing the residual-sublayer entry point on the same batches")
@@ -67,6 +67,7 @@ def parse():
                     help="write a per-workload kernel time table from a rocprofv3 --kernel-trace run and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the decode/prefill line: tokens/s and roofline fractions over batch sizes T")
+    ap.add_argument("--sweep-fp8", action="store_true", help="the T sweep through the FP8-weight entry point")
     ap.add_argument("--sweep-tokens", default="1,2,4,8,16,32,64,128,256,512,1024,2048,4096,8192,16384")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_DIR", "OUT_MD"),
                     help="per-kernel counter summary of a rocprofv3 --pmc run of this script")
@@ -120,7 +121,7 @@ def summarize_pmc(fetch_dir, write_dir):
 
     f_scale = COPY_BYTES / 1024.0 / copy_kib(fetch)
     w_scale = COPY_BYTES / 1024.0 / copy_kib(write)
-    lines = ["# HBM traffic per launch of the gate/up kernel (decode, prefill, FP8 decode), from rocprofv3 counters",
+    lines = ["# HBM traffic per launch of the gate/up kernel (decode and prefill, bf16 and FP8 weights), from rocprofv3 counters",
              "# fetch:  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- "
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-residual --copy-calibration",
              "# write:  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- "
@@ -149,9 +150,11 @@ def summarize_sweep(sweep_json, out_md):
     """Markdown table of a `bench.py --sweep` JSON line."""
     with open(sweep_json) as f:
         d = json.loads(f.read().strip().splitlines()[-1])
-    out = ["# T sweep: Beam MoE block forward, batch sizes 1 .. 16384 on one MI355X", "",
+    fp8 = d["config"].get("weights", "bf16") != "bf16"
+    out = ["# T sweep: Beam MoE block forward" + (" with FP8 E4M3 expert weights" if fp8 else "") +
+           ", batch sizes 1 .. 16384 on one MI355X", "",
            "Command (repository root on the GPU host):", "", "```",
-           "python3 bench.py --sweep --steps 20 --warmup 3 > <SWEEP_JSON>",
+           "python3 bench.py --sweep" + (" --sweep-fp8" if fp8 else "") + " --steps 20 --warmup 3 > <SWEEP_JSON>",
            "python3 bench.py --summarize-sweep <SWEEP_JSON> <this file>", "```", "",
            "Per point: mean ms per forward step over the timed steps (fewer steps for large T), the",
            "expert path the library chose, and the layer's fraction of the HBM roofline (bytes of the",
@@ -199,7 +202,8 @@ def summarize_trace(trace_dir, out_md):
 
     def kind(c):
         names = " ".join(r["Kernel_Name"] for r in c)
-        wl = "prefill" if "grouped_gemm" in names else ("decode_fp8" if "_fp8_kernel" in names else "decode")
+        fp8 = "_fp8_kernel" in names or ", true>" in names
+        wl = ("prefill" if "grouped_gemm" in names else "decode") + ("_fp8" if fp8 else "")
         return wl + (", residual sublayer" if "prenorm_kernel" in names else "")
 
     per = {}
@@ -208,17 +212,18 @@ def summarize_trace(trace_dir, out_md):
         for r in c:
             us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             per.setdefault(wl, {}).setdefault(short(r["Kernel_Name"]), []).append(us)
-    out = ["# rocprofv3 kernel times: Beam MoE block forward, decode T=64, prefill T=16384, FP8 decode T=64",
+    out = ["# rocprofv3 kernel times: Beam MoE block forward, decode T=64 and prefill T=16384, bf16 and FP8 weights",
            "", "Command (repository root on the GPU host):", "", "```",
            "cd /tmp && export TMPDIR=/tmp",
            "rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- \\",
            "    python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
            "python3 bench.py --summarize-trace <TRACE_DIR> <this file>", "```", "",
            "Calls are cut before each router_logits_kernel dispatch (before the prenorm_kernel of a",
-           "residual-sublayer call); calls that ran the grouped GEMM are prefill, those that ran the FP8",
-           "kernels decode_fp8, the others decode.  Warmup and timed calls, with and without the stage",
+           "residual-sublayer call); calls that ran the grouped GEMM are prefill, the others decode, with",
+           "the suffix _fp8 where the FP8 kernels ran.  Warmup and timed calls, with and without the stage",
            "markers, are all counted.  Durations are the dispatch end minus start timestamps.", ""]
-    order = ["decode", "prefill", "decode_fp8", "decode, residual sublayer", "prefill, residual sublayer"]
+    order = ["decode", "prefill", "decode_fp8", "prefill_fp8", "decode, residual sublayer",
+             "prefill, residual sublayer"]
     for wl in order + sorted(k for k in per if k not in order):
         if wl not in per:
             continue
@@ -299,7 +304,7 @@ def time_wl(wl, experts, steps, warmup, fp8=None):
     x = synth.make_x(wl, "cuda")
     wr = synth.make_router(wl, "cuda")
     bias = synth.make_bias(wl, "cuda")
-    wg, wu, wd = experts
+    wg, wu, wd = experts if fp8 is None else (None, None, None)
     bufs = binding.ForwardBuffers(d, wl.tokens, "cuda")
     stream = torch.cuda.current_stream()
     if fp8 is not None:
@@ -448,15 +453,17 @@ def expert_path(wl):
     return "stream" if avg <= 4 else "grouped GEMM"
 
 
-def sweep(args, experts):
-    """Tokens/s and both roofline fractions of the whole layer over batch sizes T."""
+def sweep(args, experts, experts_fp8=None):
+    """Tokens/s and both roofline fractions of the whole layer over batch sizes T (bf16 experts,
+    or FP8 ones through the FP8-weight entry point)."""
     from grouped_top_routing_fp32_amd import synth
     base = synth.WORKLOADS["decode"]
     points = []
     for T in [int(t) for t in args.sweep_tokens.split(",") if t]:
         wl = synth.with_tokens(base, T)
         steps = max(3, min(args.steps, int(2000 / max(1, T))))  # keep large batches short
-        r = time_wl(wl, experts, steps, args.warmup)
+        r = time_wl(wl, experts, steps, args.warmup, fp8=experts_fp8)
+        r["fp8"] = experts_fp8 is not None
         s = layer_summary(r)
         hbm, mfma = s["layer_hbm_frac"], s["layer_mfma_frac"]
         points.append({"T": T, "steps": steps, "ms_per_step": round(r["ms_per_step"], 4),
@@ -471,7 +478,8 @@ def sweep(args, experts):
                       "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "Beam MoE block forward, T swept", "hidden": base.dims.hidden,
                                  "intermediate": base.dims.intermediate, "experts": base.dims.num_experts,
-                                 "topk": base.dims.topk},
+                                 "topk": base.dims.topk,
+                                 "weights": "e4m3 + fp32 row scales" if experts_fp8 is not None else "bf16"},
                       "points": points}), flush=True)
 
 
@@ -604,9 +612,9 @@ def main():
         return
     names = [w for w in args.workloads.split(",") if w]
     print(f"[bench] generating Beam expert weights (20.1 GB bf16) on the device", file=sys.stderr, flush=True)
-    experts = synth.make_experts(synth.WORKLOADS["decode"], "cuda")
+    experts = None if (args.sweep and args.sweep_fp8) else synth.make_experts(synth.WORKLOADS["decode"], "cuda")
     experts_fp8 = None
-    if any(n.endswith("_fp8") for n in names) and not args.sweep:
+    if (any(n.endswith("_fp8") for n in names) and not args.sweep) or (args.sweep and args.sweep_fp8):
         print(f"[bench] generating Beam FP8 expert weights (10.1 GB E4M3 + row scales) on the device",
               file=sys.stderr, flush=True)
         experts_fp8 = synth.make_experts_fp8(synth.WORKLOADS["decode"], "cuda")
@@ -614,7 +622,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     if args.sweep:
-        sweep(args, experts)
+        sweep(args, experts, experts_fp8 if args.sweep_fp8 else None)
         return
     results = {}
     for name in names:

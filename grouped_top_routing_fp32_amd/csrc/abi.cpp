@@ -40,6 +40,13 @@ hipError_t launch_gateup_stream_fp8(const uint16_t* x, const int32_t* slots, con
 hipError_t launch_down_stream_fp8(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
                                   const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd,
                                   uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st);
+hipError_t launch_gateup_grouped_fp8(const uint16_t* x, const int32_t* slots, const Tile* tiles,
+                                     const int32_t* ntiles, int max_tiles, const uint8_t* wg, const uint8_t* wu,
+                                     const float* sg, const float* su, uint16_t* h, uint8_t* hscale, int H, int I,
+                                     int K, hipStream_t st);
+hipError_t launch_down_grouped_fp8(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                                   const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd,
+                                   uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st);
 int grouped_gemm_rows();
 bool residual_fits(int H);
 hipError_t launch_prenorm(const float* stream, const float* g_in, uint16_t* x, int T, int H, float eps,
@@ -83,8 +90,10 @@ bool dims_ok(const beam_moe_dims* d) {
 // tile, so the stream kernels win only while an expert rarely sees more than
 // one pass (measured at Beam dims: T = 128 runs 3.5 ms on the stream kernels,
 // T = 160 .. 1024 run 4.0 .. 4.3 ms on the grouped GEMMs).
-bool use_stream_path(const beam_moe_dims* d, int T) {
-  return (double)T * d->topk / d->num_experts <= 4.0 && beam::stream_fits(d->hidden, d->intermediate);
+bool use_stream_path(const beam_moe_dims* d, int T, bool fp8 = false) {
+  const bool few_rows = (double)T * d->topk / d->num_experts <= 4.0;
+  return few_rows && (fp8 ? beam::stream_fp8_fits(d->hidden, d->intermediate)
+                          : beam::stream_fits(d->hidden, d->intermediate));
 }
 
 struct Plan {
@@ -108,7 +117,7 @@ struct Plan {
   size_t total;
 };
 
-// fp8: the FP8-weight expert kernels, which are stream kernels at every T.
+// fp8: the FP8-weight expert kernels (stream or grouped by the same rule).
 void make_plan(const beam_moe_dims* d, int T, Plan* p, bool fp8 = false) {
   p->T = T;
   p->H = d->hidden;
@@ -127,7 +136,7 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p, bool fp8 = false) {
   p->k_per_split = steps_per * 32;
   p->splits = (ksteps + steps_per - 1) / steps_per;
   p->units = beam::dispatch_units(p->n);
-  p->stream = fp8 || use_stream_path(d, T);
+  p->stream = use_stream_path(d, T, fp8);
   const int touched = p->E < p->n ? p->E : p->n;  // most experts with rows
   if (p->stream) {
     p->mt = kWholeExpert;
@@ -269,9 +278,12 @@ int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* w
   BEAM_TRY(beam::launch_dispatch(a.topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), a.expert_counts,
                                  a.expert_offsets, a.sorted_slots, tiles, p.mt, ntiles, st));
   BEAM_TRY(mark(ev, kStGateUp, st));
-  if (a.qg)
+  if (a.qg && p.stream)
     BEAM_TRY(beam::launch_gateup_stream_fp8(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qg, a.qu, a.sg, a.su,
                                             h, hscale, p.H, p.I, p.K, st));
+  else if (a.qg)
+    BEAM_TRY(beam::launch_gateup_grouped_fp8(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qg, a.qu, a.sg,
+                                             a.su, h, hscale, p.H, p.I, p.K, st));
   else if (p.stream)
     BEAM_TRY(beam::launch_gateup_stream(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wg, a.wu, h, hscale, p.H,
                                         p.I, p.K, st));
@@ -279,9 +291,12 @@ int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* w
     BEAM_TRY(beam::launch_gateup_grouped(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wg, a.wu, h, hscale,
                                          p.H, p.I, p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
-  if (a.qd)
+  if (a.qd && p.stream)
     BEAM_TRY(beam::launch_down_stream_fp8(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qd, a.sd, y16,
                                           yscale, p.H, p.I, st));
+  else if (a.qd)
+    BEAM_TRY(beam::launch_down_grouped_fp8(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qd, a.sd, y16,
+                                           yscale, p.H, p.I, st));
   else if (p.stream)
     BEAM_TRY(beam::launch_down_stream(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wd, y16, yscale, p.H,
                                       p.I, st));

@@ -64,13 +64,22 @@ __device__ __forceinline__ int xcd_lin(int b, int total) {
 // GATEUP: act = x [T, H]; w0 = W_gate, w1 = W_up [E, I, H]; out = h fp16 [n, I]; hscale written.
 // !GATEUP: act = h fp16 [n, I]; w0 = W_down [E, H, I]; hscale read; out = y fp16 [n, H] (row slot),
 //          scaled by 2^-s with s per (tile, 64 columns) written to oscale [n, H / 64].
-template <bool GATEUP>
+// FP8: the weights are E4M3 codes (uint8) with one fp32 scale per output row (s0 for w0, s1 for
+//      w1, [E, Ndim]); every copy of them passes through registers, where the codes are decoded
+//      exactly (to bf16 for gate/up, to fp16 times the stage's 2^s for down), and the row scales
+//      multiply the accumulators before the epilogue.
+template <bool GATEUP, bool FP8>
 __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_slots, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
-    void* __restrict__ out, uint8_t* __restrict__ hscale, uint8_t* __restrict__ oscale, int Kdim, int Ndim, int topk,
-    int nbn, int total_blocks) {
+    const int32_t* __restrict__ ntiles, const void* __restrict__ w0v, const void* __restrict__ w1v,
+    const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
+    uint8_t* __restrict__ hscale, uint8_t* __restrict__ oscale, int Kdim, int Ndim, int topk, int nbn,
+    int total_blocks) {
   using namespace gg;
+  using WT = std::conditional_t<FP8, uint8_t, uint16_t>;  // weight element
+  const WT* w0 = static_cast<const WT*>(w0v);
+  const WT* w1 = static_cast<const WT*>(w1v);
+  constexpr bool kRegB = FP8 || !GATEUP;  // weights through registers
   // two stages of A, then two of B
   __shared__ __attribute__((aligned(16))) uint16_t ring[4 * kSlotHalfs];
   __shared__ float smax[16];
@@ -105,9 +114,9 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   // 1 KB copy: lane i lands at byte 16 i, i.e. row + i/8, position i%8, and so
   // fetches chunk (i%8) ^ swz(row).
   const uint16_t* asrc[4];
-  const uint16_t* bsrc[4];
+  const WT* bsrc[4];
   {
-    const uint16_t* wbase = (GATEUP && wave >= 4 ? w1 : w0) + (size_t)tl.expert * Ndim * Kdim;  // B rows 128..: up
+    const WT* wbase = (GATEUP && wave >= 4 ? w1 : w0) + (size_t)tl.expert * Ndim * Kdim;  // B rows 128..: up
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 32 * wave + 8 * q + (lane >> 3);
@@ -134,19 +143,38 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) lds_copy16(bsrc[q] + k, lds_addr(&sB[slot][(32 * wave + 8 * q) * kBK]));
   };
-  // down: weight stage through registers
-  u32x4 breg[4];
+  // Weights through registers (down, and every FP8 kernel): a lane loads the 8
+  // weights of the chunk its copy would fetch (16 bytes of bf16 or 8 of E4M3 codes),
+  // converts them and writes the 16 bytes where the copy would have put them.
+  using BReg = std::conditional_t<FP8, uint2, u32x4>;
+  BReg breg[4];
   const uint8_t* tscale = GATEUP ? nullptr : hscale + (size_t)tl.row_start * (Kdim / kScaleCols);
   auto load_b = [&](int stage) {
     const int k = stage * kBK;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) breg[q] = ldg16(bsrc[q] + k);
+    for (int q = 0; q < 4; ++q) breg[q] = *reinterpret_cast<const BReg*>(bsrc[q] + k);
   };
   auto store_b = [&](int stage, int slot) {
-    const int sexp = tscale[stage];  // kBK == kScaleCols: one activation block per stage
+    const int sexp = GATEUP ? 0 : tscale[stage];  // kBK == kScaleCols: one activation block per stage
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const u32x4 v = sexp ? bf16x8_to_f16x8_scaled(breg[q], sexp) : bf16x8_to_f16x8(breg[q]);
+      u32x4 v;
+      if constexpr (FP8) {
+        const uint32_t c[2] = {breg[q].x, breg[q].y};
+        const float sc = __builtin_amdgcn_ldexpf(1.0f, sexp);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if constexpr (GATEUP) {
+            v[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false));
+            v[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true));
+          } else {
+            v[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], sc, false));
+            v[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], sc, true));
+          }
+        }
+      } else {
+        v = sexp ? bf16x8_to_f16x8_scaled(breg[q], sexp) : bf16x8_to_f16x8(breg[q]);
+      }
       *reinterpret_cast<u32x4*>(&sB[slot][(32 * wave + 8 * q) * kBK + lane * 8]) = v;
     }
   };
@@ -227,16 +255,16 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   // Stage t lives in slot t % 2.  Step t: wait for this wave's copies of stage t
   // (nothing later is in flight), barrier (stage t complete for all waves, and
   // everyone is done with the other slot), request stage t + 1 into the other
-  // slot, MFMAs on stage t.  Down loads stage t + 1's weights into registers
-  // before the MFMAs and writes them, converted, to the other slot after them;
-  // the next barrier publishes them.
+  // slot, MFMAs on stage t.  Weights through registers: stage t + 1's are loaded
+  // before the MFMAs and written, converted, to the other slot after them; the
+  // next barrier publishes them.
   const int nk = Kdim / kBK;  // Kdim % 128 == 0, so nk >= 2
   issue_a(0, 0);
-  if (GATEUP) {
-    issue_b(0, 0);
-  } else {
+  if constexpr (kRegB) {
     load_b(0);
     store_b(0, 0);
+  } else {
+    issue_b(0, 0);
   }
   auto main_loop = [&](auto full) {
     for (int st = 0; st < nk; ++st) {
@@ -247,18 +275,18 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
       const bool more = st + 1 < nk;
       if (more) {
         issue_a(st + 1, slot ^ 1);
-        if (GATEUP)
-          issue_b(st + 1, slot ^ 1);
-        else
+        if constexpr (kRegB)
           load_b(st + 1);
+        else
+          issue_b(st + 1, slot ^ 1);
       }
-      if (GATEUP) {
+      if constexpr (GATEUP && !FP8) {
         math2(slot, full);
       } else {
         math(slot, 0, full);
         math(slot, 1, full);
       }
-      if (!GATEUP && more) store_b(st + 1, slot ^ 1);
+      if (kRegB && more) store_b(st + 1, slot ^ 1);
     }
   };
   // full tiles (the common case) run without the per-level tests
@@ -269,6 +297,19 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
 
   // ---- epilogue ----------------------------------------------------------
   // lane holds rows 4*(lane/16)+r and column lane%16 of each 16x16 block
+  // FP8: the row scales of this lane's columns (gate/up: the gate and up rows of column
+  // n0 + wn*64 + 16 j + lane%16; down: output column n0 + wn*128 + 16 j + lane%16)
+  float rs[8];
+  if constexpr (FP8) {
+    const size_t sb = (size_t)tl.expert * Ndim + n0 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      rs[j] = GATEUP ? (j < 4 ? s0 : s1)[sb + wn * 64 + 16 * (j & 3)] : s0[sb + wn * 128 + 16 * j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] *= rs[j];
+  }
   if (GATEUP) {
     float mx = 0.f;
 #pragma unroll
@@ -366,8 +407,8 @@ hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const 
                                  int H, int I, int K, hipStream_t st) {
   const int nbn = I / (gg::kBN / 2);  // I % 128 == 0
   const int total = gemm_blocks(max_tiles, nbn);
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(total), dim3(gg::kThreads), 0, st, x, slots, tiles, ntiles, wg,
-                     wu, (void*)h, hscale, nullptr, H, I, K, nbn, total);
+  hipLaunchKernelGGL((grouped_gemm_kernel<true, false>), dim3(total), dim3(gg::kThreads), 0, st, x, slots, tiles,
+                     ntiles, wg, wu, nullptr, nullptr, (void*)h, hscale, nullptr, H, I, K, nbn, total);
   return hipGetLastError();
 }
 
@@ -376,8 +417,31 @@ hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const i
                                uint8_t* yscale, int H, int I, hipStream_t st) {
   const int nbn = H / gg::kBN;  // H % 256 == 0
   const int total = gemm_blocks(max_tiles, nbn);
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(total), dim3(gg::kThreads), 0, st, h, slots, tiles, ntiles, wd,
-                     nullptr, (void*)y16, const_cast<uint8_t*>(hscale), yscale, I, H, 0, nbn, total);
+  hipLaunchKernelGGL((grouped_gemm_kernel<false, false>), dim3(total), dim3(gg::kThreads), 0, st, h, slots, tiles,
+                     ntiles, wd, nullptr, nullptr, nullptr, (void*)y16, const_cast<uint8_t*>(hscale), yscale, I, H, 0,
+                     nbn, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_grouped_fp8(const uint16_t* x, const int32_t* slots, const Tile* tiles,
+                                     const int32_t* ntiles, int max_tiles, const uint8_t* wg, const uint8_t* wu,
+                                     const float* sg, const float* su, uint16_t* h, uint8_t* hscale, int H, int I,
+                                     int K, hipStream_t st) {
+  const int nbn = I / (gg::kBN / 2);
+  const int total = gemm_blocks(max_tiles, nbn);
+  hipLaunchKernelGGL((grouped_gemm_kernel<true, true>), dim3(total), dim3(gg::kThreads), 0, st, x, slots, tiles,
+                     ntiles, wg, wu, sg, su, (void*)h, hscale, nullptr, H, I, K, nbn, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_grouped_fp8(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                                   const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd,
+                                   uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st) {
+  const int nbn = H / gg::kBN;
+  const int total = gemm_blocks(max_tiles, nbn);
+  hipLaunchKernelGGL((grouped_gemm_kernel<false, true>), dim3(total), dim3(gg::kThreads), 0, st, h, slots, tiles,
+                     ntiles, wd, nullptr, sd, nullptr, (void*)y16, const_cast<uint8_t*>(hscale), yscale, I, H, 0,
+                     nbn, total);
   return hipGetLastError();
 }
 

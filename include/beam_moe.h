@@ -156,9 +156,8 @@ int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, c
  * Precision: the codes are decoded exactly to bf16 (gate/up, against the bf16
  * x) or fp16 (down, against the fp16 activations) in registers; products
  * accumulate in FP32 and the row scale multiplies the accumulated sum; the
- * rest as in beam_moe_forward.  The expert kernels are the few-rows-per-expert
- * ones at every T: built for decode-sized batches, correct but slower than
- * the bf16 grouped GEMMs once experts see many rows.
+ * rest as in beam_moe_forward, whose choice between the few-rows-per-expert
+ * kernels and the grouped GEMMs it shares.
  * Supported sizes additionally satisfy hidden % 256 == 0 and
  * intermediate % 256 == 0; the workspace is beam_moe_workspace_bytes(dims, T). */
 int beam_moe_forward_fp8(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,

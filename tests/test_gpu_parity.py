@@ -485,10 +485,18 @@ FP8 = {
     "f8_stream": synth.Workload("f8_stream", 40, synth.Dims(512, 512, 64, 8, 4, 6), router_sigma=0.06),
     # skewed routing: hot experts run many passes
     "f8_skew": synth.Workload("f8_skew", 60, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06, zipf_s=1.2),
-    # about 75 rows per expert: the FP8 kernels at a batch the bf16 path would give the grouped GEMMs
-    "f8_many_rows": synth.Workload("f8_many_rows", 300, synth.Dims(512, 256, 16, 4, 2, 4), router_sigma=0.06),
     # large activations: h and y travel with power-of-two scales, codes are converted times 2^s
     "f8_big": synth.Workload("f8_big", 40, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06, expert_sigma=10.0),
+    # grouped GEMMs with E4M3 weights: about 75 rows per expert (full and ragged tiles), Beam's
+    # expert count with one partial tile each, skewed routing just above the stream threshold,
+    # and large activations
+    "f8_grouped": synth.Workload("f8_grouped", 300, synth.Dims(512, 256, 16, 4, 2, 4), router_sigma=0.06),
+    "f8_grouped_e256": synth.Workload("f8_grouped_e256", 1100, synth.Dims(768, 256, 256, 8, 4, 8),
+                                      router_sigma=0.04),
+    "f8_grouped_skew": synth.Workload("f8_grouped_skew", 150, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
+                                      zipf_s=1.2),
+    "f8_grouped_big": synth.Workload("f8_grouped_big", 900, synth.Dims(512, 512, 16, 4, 2, 4), router_sigma=0.06,
+                                     expert_sigma=10.0),
 }
 
 
@@ -530,7 +538,7 @@ def test_forward_fp8_rejects_unsupported_intermediate():
     assert ei.value.status == binding.BEAM_MOE_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("T", [1, 64, 512])
+@pytest.mark.parametrize("T", [1, 64, 512, 2048])
 def test_forward_fp8_beam(beam_experts_fp8, T):
     _announce(f"forward fp8 Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
