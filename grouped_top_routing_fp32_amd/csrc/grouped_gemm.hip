@@ -28,6 +28,11 @@
 // Down: the weight stage is loaded into registers, converted to fp16 (times
 // 2^s of the stage's 64-column activation block) and written to LDS by the
 // threads themselves, in the same layout the copies produce.
+// FP8 weights (E4M3 codes with one fp32 scale per output row; 「Reflection 放出
+// 501B 的 Beam 权重：四套精度、滑动窗口和一场榜单落差」, the FP8 repository's
+// precision listing): both projections take their weights through registers
+// the same way, decoding 8 codes per lane exactly (bf16 for gate/up, fp16 times
+// 2^s for down); the row scales multiply the accumulators before the epilogue.
 // Blocks are ordered for L2 reuse: each XCD (block b runs on XCD b % 8) takes
 // a contiguous range of a linear order in which an expert's row tiles sweep
 // the column blocks together, so blocks dispatched one after another share the
