@@ -659,36 +659,44 @@ hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const in
 // ---------------------------------------------------------------------------
 // combine: out[t] = sum_k w[t,k] * y[t*K + k], k ascending, FP32
 // ---------------------------------------------------------------------------
-constexpr int kCombineCols = 1024;  // columns per workgroup (256 threads x 4)
+constexpr int kCombineCols = 2048;  // columns per workgroup (256 threads x 8)
 
-// grid: (T, ceil(H / 1024)); block 256.  The K rows of a token (fp16, each with
-// its 64-column scale) are loaded together (up to 16), then summed in
-// ascending k in FP32.
+// grid: (T, ceil(H / 2048)); block 256.  A thread owns 8 consecutive columns:
+// the K rows of its token (fp16, each with its 64-column scale) are loaded
+// together (up to 16, 16 bytes each), then summed in ascending k in FP32.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y16,
                                                       const uint8_t* __restrict__ yscale,
                                                       const float* __restrict__ w, float* __restrict__ out, int H,
                                                       int K) {
   const int t = blockIdx.x;
-  const int c = blockIdx.y * kCombineCols + threadIdx.x * 4;
+  const int c = blockIdx.y * kCombineCols + threadIdx.x * 8;
   if (c >= H) return;
   const size_t row0 = (size_t)t * K;
   const int nsb = H / kScaleCols;
-  f32x4 yv[16];
+  u32x4 raw[16];
+  int sc[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k)
     if (k < K) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(y16 + (row0 + k) * H + c);
-      const int s = yscale[(row0 + k) * nsb + c / kScaleCols];
-      yv[k][0] = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.x & 0xFFFFu)), s);
-      yv[k][1] = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.x >> 16)), s);
-      yv[k][2] = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.y & 0xFFFFu)), s);
-      yv[k][3] = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.y >> 16)), s);
+      raw[k] = *reinterpret_cast<const u32x4*>(y16 + (row0 + k) * H + c);
+      sc[k] = yscale[(row0 + k) * nsb + c / kScaleCols];
     }
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < 16; ++k)
-    if (k < K) acc += w[row0 + k] * yv[k];
-  *reinterpret_cast<f32x4*>(out + (size_t)t * H + c) = acc;
+    if (k < K) {
+      const float wk = w[row0 + k];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw[k][q] & 0xFFFFu)), sc[k]);
+        const float hi = __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(raw[k][q] >> 16)), sc[k]);
+        acc[2 * q] += wk * lo;
+        acc[2 * q + 1] += wk * hi;
+      }
+    }
+  float* o = out + (size_t)t * H + c;
+  *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
 hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
