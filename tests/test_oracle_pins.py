@@ -497,6 +497,30 @@ def test_residual_step_special_cases():
     np.testing.assert_allclose(r2["out"] - a * stream * 4.0, r["out"] - a * stream, rtol=0, atol=1e-12)
 
 
+def test_residual_step_norm_weights_act_where_named():
+    # the pre-norm weight scales the block's input, the post-norm weight only the added term
+    # (identical experts, so the block is 2.5 * SwiGLU whatever the routing): g_out = 2 doubles
+    # the added term and leaves the block's output alone; g_in = 2 doubles the block's input
+    # (exactly: a power of two commutes with the bf16 rounding) and so changes its output
+    rng = np.random.default_rng(5)
+    E, G, TG, K, H, I = 16, 4, 2, 4, 8, 6
+    wg, wu, wd = rng.standard_normal((I, H)), rng.standard_normal((I, H)), rng.standard_normal((H, I))
+    stream = rng.standard_normal((4, H))
+    w_r = rng.standard_normal((E, H))
+    k = 3
+    a, b = math.sqrt(2 / 3), 1 / math.sqrt(3)
+    ex = lambda e: (wg, wu, wd)  # noqa: E731
+    base = orc.moe_residual_step(stream, k, w_r, None, ex, G, TG, K, 2.5)
+    two = np.full(H, 2.0)
+    r_out = orc.moe_residual_step(stream, k, w_r, None, ex, G, TG, K, 2.5, norm_out_weight=two)
+    np.testing.assert_allclose(r_out["moe"], base["moe"], rtol=0, atol=0)
+    np.testing.assert_allclose(r_out["out"] - a * stream, 2.0 * (base["out"] - a * stream), rtol=0, atol=1e-12)
+    r_in = orc.moe_residual_step(stream, k, w_r, None, ex, G, TG, K, 2.5, norm_in_weight=two)
+    np.testing.assert_allclose(r_in["x"], 2.0 * base["x"], rtol=0, atol=0)
+    np.testing.assert_allclose(r_in["moe"], 2.5 * orc.swiglu_expert(2.0 * base["x"], wg, wu, wd), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r_in["out"], a * stream + b * orc.rms_norm(r_in["moe"]), rtol=0, atol=1e-12)
+
+
 # --------------------------------------------------------------------------
 # FP8 (E4M3) expert weights
 # --------------------------------------------------------------------------
