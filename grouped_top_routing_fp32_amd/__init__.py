@@ -8,7 +8,8 @@ and fails loudly when it is missing.
 """
 
 _EXPORTS = ("beam_moe_route", "beam_moe_select", "beam_moe_dispatch", "beam_moe_forward", "beam_moe_forward_fp8",
-            "beam_moe_residual_forward", "beam_moe_workspace_bytes", "beam_moe_status_str", "Dims", "BeamMoeError", "load_library")
+            "beam_moe_residual_forward", "beam_moe_residual_forward_fp8", "beam_moe_workspace_bytes",
+            "beam_moe_status_str", "Dims", "BeamMoeError", "load_library")
 
 
 def __getattr__(name):

@@ -25,8 +25,9 @@ BEAM_MOE_ERR_WORKSPACE = -3
 BEAM_MOE_ERR_HIP = -4
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_select", "beam_moe_dispatch",
-            "beam_moe_forward", "beam_moe_forward_fp8", "beam_moe_residual_forward", "beam_moe_timing_enable",
-            "beam_moe_timing_read", "beam_moe_stage_name", "beam_moe_status_str")
+            "beam_moe_forward", "beam_moe_forward_fp8", "beam_moe_residual_forward",
+            "beam_moe_residual_forward_fp8", "beam_moe_timing_enable", "beam_moe_timing_read", "beam_moe_stage_name",
+            "beam_moe_status_str")
 
 SIZE_MAX = 2 ** 64 - 1
 
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.beam_moe_residual_forward.argtypes = [pd, i32, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, vp, vp, sz, vp]
     lib.beam_moe_residual_forward.restype = ctypes.c_int
+    lib.beam_moe_residual_forward_fp8.argtypes = [pd, i32, vp, i32, vp, vp, ctypes.c_float] + [vp] * 16 + [sz, vp]
+    lib.beam_moe_residual_forward_fp8.restype = ctypes.c_int
     lib.beam_moe_timing_enable.argtypes = [ctypes.c_int]
     lib.beam_moe_timing_enable.restype = ctypes.c_int
     lib.beam_moe_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32),
@@ -313,6 +316,48 @@ def beam_moe_residual_forward(dims: Dims, stream_in: torch.Tensor, step: int, w_
         _ptr(w_down), _ptr(bufs.out), _ptr(bufs.ids), _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets),
         _ptr(bufs.slots), _ptr(bufs.ws), bufs.ws.numel(), _stream(stream))
     _check(st, "beam_moe_residual_forward")
+    return bufs
+
+
+def beam_moe_residual_forward_fp8(dims: Dims, stream_in: torch.Tensor, step: int, w_router: torch.Tensor,
+                                  logit_bias: Optional[torch.Tensor], w_gate_fp8: torch.Tensor,
+                                  gate_scale: torch.Tensor, w_up_fp8: torch.Tensor, up_scale: torch.Tensor,
+                                  w_down_fp8: torch.Tensor, down_scale: torch.Tensor, *,
+                                  select_bias: Optional[torch.Tensor] = None,
+                                  norm_in_weight: Optional[torch.Tensor] = None,
+                                  norm_out_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+                                  stream_out: Optional[torch.Tensor] = None, bufs: Optional[ForwardBuffers] = None,
+                                  stream=None) -> ForwardBuffers:
+    """The block with E4M3 expert weights as a residual sublayer at `step`; bufs.out holds the new stream."""
+    T = stream_in.shape[0]
+    H, I, E = dims.hidden, dims.intermediate, dims.num_experts
+    _req(stream_in, "stream_in", torch.float32, (T, H))
+    _req(w_router, "w_router", torch.float32, (E, H))
+    for t, name, n in ((logit_bias, "logit_bias", E), (select_bias, "select_bias", E),
+                       (norm_in_weight, "norm_in_weight", H), (norm_out_weight, "norm_out_weight", H)):
+        if t is not None:
+            _req(t, name, torch.float32, (n,))
+    _req(w_gate_fp8, "w_gate_fp8", torch.uint8, (E, I, H))
+    _req(w_up_fp8, "w_up_fp8", torch.uint8, (E, I, H))
+    _req(w_down_fp8, "w_down_fp8", torch.uint8, (E, H, I))
+    _req(gate_scale, "gate_scale", torch.float32, (E, I))
+    _req(up_scale, "up_scale", torch.float32, (E, I))
+    _req(down_scale, "down_scale", torch.float32, (E, H))
+    if bufs is None:
+        bufs = ForwardBuffers(dims, T, stream_in.device)
+    if bufs.T != T:
+        raise ValueError("buffers were sized for another T")
+    if stream_out is not None:
+        _req(stream_out, "stream_out", torch.float32, (T, H))
+        bufs.out = stream_out
+    cd = _cdims(dims)
+    st = load_library().beam_moe_residual_forward_fp8(
+        ctypes.byref(cd), T, _ptr(stream_in), int(step), _ptr(norm_in_weight), _ptr(norm_out_weight),
+        float(norm_eps), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate_fp8), _ptr(gate_scale),
+        _ptr(w_up_fp8), _ptr(up_scale), _ptr(w_down_fp8), _ptr(down_scale), _ptr(bufs.out), _ptr(bufs.ids),
+        _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets), _ptr(bufs.slots), _ptr(bufs.ws), bufs.ws.numel(),
+        _stream(stream))
+    _check(st, "beam_moe_residual_forward_fp8")
     return bufs
 
 

@@ -310,6 +310,36 @@ int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* w
   return BEAM_MOE_OK;
 }
 
+// The block as a residual sublayer: pre-norm of the stream into the workspace's
+// x, the block (bf16 or FP8 experts as set in `a`, whose x is filled here), then
+// the fused post-norm and stream update.  Weight pointers are checked by the caller.
+int residual_block(const beam_moe_dims* d, int32_t T, const float* stream_in, int32_t step, const float* g_in,
+                   const float* g_out, float eps, BlockArgs a, bool fp8, float* stream_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (!beam::residual_fits(d->hidden)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (step < 2 || !std::isfinite(eps) || eps < 0.f) return BEAM_MOE_ERR_INVALID_ARG;
+  if (T == 0) return BEAM_MOE_OK;
+  int rc;
+  if ((rc = check_ptrs({stream_in, a.w_router, stream_out, a.topk_ids, a.topk_w, a.expert_counts, a.expert_offsets,
+                        a.sorted_slots})) != BEAM_MOE_OK)
+    return rc;
+  for (const float* opt : {a.logit_bias, a.select_bias, g_in, g_out})
+    if (opt && !aligned16(opt)) return BEAM_MOE_ERR_INVALID_ARG;
+  Plan p;
+  make_plan(d, T, &p, fp8);
+  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* x = at<uint16_t>(ws, p.off_x);
+  a.x = x;
+  const float* topk_w = a.topk_w;
+  return run_block(
+      d, p, a, ws, st, [&] { return beam::launch_prenorm(stream_in, g_in, x, T, p.H, eps, st); },
+      [&](const uint16_t* y16, const uint8_t* yscale) {
+        return beam::launch_combine_residual(y16, yscale, topk_w, stream_in, g_out, stream_out, T, p.H, p.K, step, eps,
+                                             st);
+      });
+}
+
 }  // namespace
 
 extern "C" {
@@ -470,20 +500,8 @@ int beam_moe_residual_forward(const beam_moe_dims* d, int32_t T, const float* st
                               int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(d, T);
   if (rc != BEAM_MOE_OK) return rc;
-  if (!beam::residual_fits(d->hidden)) return BEAM_MOE_ERR_UNSUPPORTED;
-  if (step < 2 || !std::isfinite(norm_eps) || norm_eps < 0.f) return BEAM_MOE_ERR_INVALID_ARG;
-  if (T == 0) return BEAM_MOE_OK;
-  if ((rc = check_ptrs({stream_in, w_router, w_gate, w_up, w_down, stream_out, topk_ids, topk_w, expert_counts,
-                        expert_offsets, sorted_slots})) != BEAM_MOE_OK)
-    return rc;
-  for (const float* opt : {logit_bias, select_bias, norm_in_weight, norm_out_weight})
-    if (opt && !aligned16(opt)) return BEAM_MOE_ERR_INVALID_ARG;
-  Plan p;
-  make_plan(d, T, &p);
-  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  uint16_t* x = at<uint16_t>(ws, p.off_x);
-  BlockArgs a{x,
+  if (T > 0 && (rc = check_ptrs({w_gate, w_up, w_down})) != BEAM_MOE_OK) return rc;
+  BlockArgs a{nullptr,
               w_router,
               logit_bias,
               select_bias,
@@ -501,12 +519,44 @@ int beam_moe_residual_forward(const beam_moe_dims* d, int32_t T, const float* st
               expert_counts,
               expert_offsets,
               sorted_slots};
-  return run_block(
-      d, p, a, ws, st, [&] { return beam::launch_prenorm(stream_in, norm_in_weight, x, T, p.H, norm_eps, st); },
-      [&](const uint16_t* y16, const uint8_t* yscale) {
-        return beam::launch_combine_residual(y16, yscale, topk_w, stream_in, norm_out_weight, stream_out, T, p.H,
-                                             p.K, step, norm_eps, st);
-      });
+  return residual_block(d, T, stream_in, step, norm_in_weight, norm_out_weight, norm_eps, a, false, stream_out, ws,
+                        ws_bytes, stream);
+}
+
+int beam_moe_residual_forward_fp8(const beam_moe_dims* d, int32_t T, const float* stream_in, int32_t step,
+                                  const float* norm_in_weight, const float* norm_out_weight, float norm_eps,
+                                  const float* w_router, const float* logit_bias, const float* select_bias,
+                                  const uint8_t* w_gate_fp8, const float* gate_scale, const uint8_t* w_up_fp8,
+                                  const float* up_scale, const uint8_t* w_down_fp8, const float* down_scale,
+                                  float* stream_out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                                  int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK) return rc;
+  if (!beam::stream_fp8_fits(d->hidden, d->intermediate)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (T > 0 &&
+      (rc = check_ptrs({w_gate_fp8, gate_scale, w_up_fp8, up_scale, w_down_fp8, down_scale})) != BEAM_MOE_OK)
+    return rc;
+  BlockArgs a{nullptr,
+              w_router,
+              logit_bias,
+              select_bias,
+              nullptr,
+              nullptr,
+              nullptr,
+              w_gate_fp8,
+              w_up_fp8,
+              w_down_fp8,
+              gate_scale,
+              up_scale,
+              down_scale,
+              topk_ids,
+              topk_w,
+              expert_counts,
+              expert_offsets,
+              sorted_slots};
+  return residual_block(d, T, stream_in, step, norm_in_weight, norm_out_weight, norm_eps, a, true, stream_out, ws,
+                        ws_bytes, stream);
 }
 
 int beam_moe_timing_enable(int enable) {

@@ -192,9 +192,22 @@ int beam_moe_residual_forward(const beam_moe_dims* dims, int32_t T, const float*
                               int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
                               int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
+/* beam_moe_residual_forward with FP8 expert weights: the arguments of
+ * beam_moe_residual_forward, with the expert weights given as in
+ * beam_moe_forward_fp8 (E4M3 codes and fp32 per-row scales) and the same size
+ * requirements as both. */
+int beam_moe_residual_forward_fp8(const beam_moe_dims* dims, int32_t T, const float* stream_in, int32_t step,
+                                  const float* norm_in_weight, const float* norm_out_weight, float norm_eps,
+                                  const float* w_router, const float* logit_bias, const float* select_bias,
+                                  const uint8_t* w_gate_fp8, const float* gate_scale, const uint8_t* w_up_fp8,
+                                  const float* up_scale, const uint8_t* w_down_fp8, const float* down_scale,
+                                  float* stream_out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                                  int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Diagnostics: device time of the stages of beam_moe_forward,
- * beam_moe_forward_fp8 and beam_moe_residual_forward ("prenorm" is empty
- * except in the last).
+ * beam_moe_forward_fp8 and both residual entry points ("prenorm" is empty
+ * except in the last two).
  * beam_moe_timing_enable(1) makes later calls of either record HIP
  * events between their stages on the caller's stream (a marker per stage,
  * no synchronisation; the events are created by the library on first use and

@@ -197,3 +197,32 @@ def test_forward_fp8_validation():
     assert _fp8(lib, binding._cdims(Dims(256, 128, 16, 4, 2, 4)), 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
     assert _fp8(lib, cd, -1) == binding.BEAM_MOE_ERR_INVALID_ARG
     assert _fp8(lib, cd, 0, ptrs={k: None for k in _FP8_PTRS}, ws_bytes=0) == binding.BEAM_MOE_OK
+
+
+_RES8_PTRS = ("stream_in", "g_in", "g_out", "w_router", "logit_bias", "select_bias", "q_gate", "s_gate", "q_up",
+              "s_up", "q_down", "s_down", "stream_out", "ids", "w", "counts", "offsets", "slots", "ws")
+_RES8_OPTIONAL = ("g_in", "g_out", "logit_bias", "select_bias")
+
+
+def _res8(lib, cd, T, step=2, eps=1e-6, ptrs=None, ws_bytes=1 << 40):
+    p = ptrs if ptrs is not None else {}
+    v = {k: p.get(k, None if k in _RES8_OPTIONAL else FAKE) for k in _RES8_PTRS}
+    return lib.beam_moe_residual_forward_fp8(ctypes.byref(cd), T, v["stream_in"], step, v["g_in"], v["g_out"], eps,
+                                             *[v[k] for k in _RES8_PTRS[3:]], ws_bytes, None)
+
+
+def test_residual_forward_fp8_validation():
+    lib = binding.load_library()
+    cd = binding._cdims(BEAM)
+    assert _res8(lib, cd, 64, step=1) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert _res8(lib, cd, 64, eps=float("inf")) == binding.BEAM_MOE_ERR_INVALID_ARG
+    for name in _RES8_PTRS[:-1]:
+        if name in _RES8_OPTIONAL:
+            assert _res8(lib, cd, 64, ptrs={name: ctypes.c_void_p((1 << 20) + 4)}) == \
+                binding.BEAM_MOE_ERR_INVALID_ARG, name
+        else:
+            assert _res8(lib, cd, 64, ptrs={name: None}) == binding.BEAM_MOE_ERR_INVALID_ARG, name
+    assert _res8(lib, cd, 64, ws_bytes=1) == binding.BEAM_MOE_ERR_WORKSPACE
+    assert _res8(lib, binding._cdims(Dims(5120, 2432, 256, 8, 4, 8)), 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert _res8(lib, binding._cdims(Dims(8448, 2560, 256, 8, 4, 8)), 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert _res8(lib, cd, 0, ptrs={k: None for k in _RES8_PTRS}, ws_bytes=0) == binding.BEAM_MOE_OK

@@ -551,3 +551,33 @@ def test_forward_fp8_beam(beam_experts_fp8, T):
     out1 = bufs.out.clone()
     binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q, bufs=bufs)
     assert torch.equal(out1, bufs.out)
+
+
+@pytest.mark.parametrize("name", ["f8_stream", "f8_grouped"])
+def test_residual_fp8(name):
+    _announce(f"residual fp8 {name} (all tokens)")
+    wl = FP8[name]
+    p = Problem(wl, DEV, fp8=True)
+    stream = synth.make_stream(wl, DEV)
+    g_in, g_out = synth.make_norm_weights(wl, DEV)
+    bufs = binding.beam_moe_residual_forward_fp8(p.dims, stream, 5, p.wr, p.bias, *p.q, norm_in_weight=g_in,
+                                                 norm_out_weight=g_out)
+    excluded, worst = residual_parity(p, stream, 5, bufs, g_in=g_in, g_out=g_out)
+    print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
+    new1 = bufs.out.clone()
+    inplace = stream.clone()
+    binding.beam_moe_residual_forward_fp8(p.dims, inplace, 5, p.wr, p.bias, *p.q, norm_in_weight=g_in,
+                                          norm_out_weight=g_out, stream_out=inplace)
+    assert torch.equal(inplace, new1)
+
+
+def test_residual_fp8_beam(beam_experts_fp8):
+    _announce("residual fp8 Beam T=64")
+    wl = synth.with_tokens(synth.WORKLOADS["decode"], 64)
+    p = Problem(wl, DEV, experts=beam_experts_fp8, fp8=True)
+    stream = synth.make_stream(wl, DEV)
+    bufs = binding.beam_moe_residual_forward_fp8(p.dims, stream, 2, p.wr, p.bias, *p.q)
+    torch.cuda.synchronize()
+    sample = [0, 1, 31, 63]
+    excluded, worst = residual_parity(p, stream, 2, bufs, sample)
+    print(f"  sampled {len(sample)} tokens, excluded {excluded}, worst error / tolerance {worst:.3f}")
