@@ -23,6 +23,8 @@
 // LDS in whole 256-byte row segments.  Batches with more rows per expert use
 // the grouped GEMMs (grouped_gemm.hip), which read an expert's weights once
 // per 256-row tile rather than once per pass.
+#include <atomic>
+
 #include "common.h"
 
 namespace beam {
@@ -573,8 +575,22 @@ __global__ __launch_bounds__(256) void down_stream_fp8_kernel(const uint16_t* __
   }
 }
 
-// LDS of one gfx950 compute unit, the most one workgroup can take.
-constexpr size_t kLdsBytesPerCU = 160 * 1024;
+// Dynamic LDS the stream kernels may take: 128 KB of a gfx950 CU's 160 KB,
+// leaving room for their small static arrays.
+constexpr size_t kStreamLdsMax = 128 * 1024;
+
+// Raises `fn`'s dynamic-LDS limit to kStreamLdsMax, once per device (the
+// attribute is per device; later launches, graph captures included, only launch).
+static hipError_t allow_full_lds(const void* fn, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 size_t gateup_stream_lds_bytes() { return (size_t)kSSlots * (128 + kLdsRows) * StageGeom<kSk>::kRowBytes; }
 size_t down_stream_lds_bytes(int I) {
@@ -584,8 +600,8 @@ size_t down_stream_lds_bytes(int I) {
 // Whether the stream kernels can run at this shape: K of both projections in
 // whole stages, and the staged rows and the down kernel's scales fit in LDS.
 bool stream_fits(int H, int I) {
-  return H % kSk == 0 && I % kSk == 0 && gateup_stream_lds_bytes() <= kLdsBytesPerCU &&
-         down_stream_lds_bytes(I) <= kLdsBytesPerCU;
+  return H % kSk == 0 && I % kSk == 0 && gateup_stream_lds_bytes() <= kStreamLdsMax &&
+         down_stream_lds_bytes(I) <= kStreamLdsMax;
 }
 
 size_t gateup_stream_fp8_lds_bytes() { return (size_t)kF8Slots * (128 * kF8WRow + kLdsRows * kF8ARow); }
@@ -596,8 +612,8 @@ size_t down_stream_fp8_lds_bytes(int I) {
 // Whether the FP8 stream kernels can run at this shape: K of both projections
 // in whole 256-value stages, and the staged rows and scales fit in LDS.
 bool stream_fp8_fits(int H, int I) {
-  return H % kF8Sk == 0 && I % kF8Sk == 0 && gateup_stream_fp8_lds_bytes() <= kLdsBytesPerCU &&
-         down_stream_fp8_lds_bytes(I) <= kLdsBytesPerCU;
+  return H % kF8Sk == 0 && I % kF8Sk == 0 && gateup_stream_fp8_lds_bytes() <= kStreamLdsMax &&
+         down_stream_fp8_lds_bytes(I) <= kStreamLdsMax;
 }
 
 hipError_t launch_gateup_stream_fp8(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
@@ -606,8 +622,8 @@ hipError_t launch_gateup_stream_fp8(const uint16_t* x, const int32_t* slots, con
                                     hipStream_t st) {
   dim3 grid(max_tiles, I / 64);
   const size_t bytes = gateup_stream_fp8_lds_bytes();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<kF8Slots>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<kF8Slots>), lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gateup_stream_fp8_kernel<kF8Slots>), grid, dim3(256), bytes, st, x, slots, tiles, ntiles, wg,
                      wu, sg, su, h, hscale, H, I, K);
@@ -619,8 +635,8 @@ hipError_t launch_down_stream_fp8(const uint16_t* h, const uint8_t* hscale, cons
                                   uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st) {
   dim3 grid(max_tiles, H / 64);
   const size_t bytes = down_stream_fp8_lds_bytes(I);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_stream_fp8_kernel<kF8Slots>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_fp8_kernel<kF8Slots>), lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((down_stream_fp8_kernel<kF8Slots>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
                      ntiles, wd, sd, y16, yscale, H, I);
@@ -635,8 +651,8 @@ hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const T
                                 int H, int I, int K, hipStream_t st) {
   dim3 grid(max_tiles, I / 64);  // I % 64 == 0
   const size_t bytes = gateup_stream_lds_bytes();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<kSSlots, kSk>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<kSSlots, kSk>), lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gateup_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, x, slots, tiles, ntiles,
                      wg, wu, h, hscale, H, I, K);
@@ -648,8 +664,8 @@ hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const in
                               uint8_t* yscale, int H, int I, hipStream_t st) {
   dim3 grid(max_tiles, H / 64);  // H % 64 == 0
   const size_t bytes = down_stream_lds_bytes(I);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&down_stream_lds_kernel<kSSlots, kSk>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_lds_kernel<kSSlots, kSk>), lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((down_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
                      ntiles, wd, y16, yscale, H, I);

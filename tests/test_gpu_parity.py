@@ -581,3 +581,43 @@ def test_residual_fp8_beam(beam_experts_fp8):
     sample = [0, 1, 31, 63]
     excluded, worst = residual_parity(p, stream, 2, bufs, sample)
     print(f"  sampled {len(sample)} tokens, excluded {excluded}, worst error / tolerance {worst:.3f}")
+
+
+# --------------------------------------------------------------------------
+# graph capture: every call is stream-ordered and allocation-free, so a captured
+# forward replays to the eager bits (outputs overwritten by eager work in between)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name,fp8", [("mid_stream", False), ("mid_tiled", False), ("f8_stream", True),
+                                      ("f8_grouped", True)])
+def test_forward_graph_replay(name, fp8):
+    _announce(f"graph replay {name}")
+    wl = FP8[name] if fp8 else MID[name][0]
+    p = Problem(wl, DEV, fp8=fp8)
+    if fp8:
+        run = lambda b: binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q, bufs=b)  # noqa: E731
+    else:
+        run = lambda b: binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd, bufs=b)  # noqa: E731
+    names = ("out", "ids", "w", "counts", "offsets", "slots")
+    eager = binding.ForwardBuffers(p.dims, wl.tokens, DEV)
+    run(eager)
+    torch.cuda.synchronize()
+    ref = {k: getattr(eager, k).clone() for k in names}
+    bufs = binding.ForwardBuffers(p.dims, wl.tokens, DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(bufs)
+    for i in range(3):
+        bufs.out.fill_(float("nan"))
+        bufs.ids.fill_(-1)
+        bufs.slots.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(getattr(bufs, k), ref[k]), (i, k)
