@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode,prefill,decode_fp8,prefill_fp8")
+    ap.add_argument("--workloads", default="decode,prefill,decode_fp8,prefill_fp8,skewed,router_dispatch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-residual", action="store_true",
                     help="skip timing the residual-sublayer entry point on the same batches")
@@ -265,6 +265,43 @@ def time_workload(name, experts, steps, warmup, experts_fp8=None):
     if name.endswith("_fp8"):
         return time_wl(synth.WORKLOADS[name[:-4]], experts, steps, warmup, fp8=experts_fp8)
     return time_wl(synth.WORKLOADS[name], experts, steps, warmup)
+
+
+def time_router_dispatch(steps, warmup):
+    """Router + group-limited selection + dispatch alone on the router_dispatch workload
+    (T = 4096 at Beam dims), through beam_moe_route and beam_moe_dispatch."""
+    import torch
+    from grouped_top_routing_fp32_amd import binding, synth
+
+    wl = synth.WORKLOADS["router_dispatch"]
+    d = wl.dims
+    x = synth.make_x(wl, "cuda")
+    wr = synth.make_router(wl, "cuda")
+    ws = binding.workspace(d, wl.tokens, "cuda")
+    st = torch.cuda.current_stream()
+
+    def call():
+        ids, _, _ = binding.beam_moe_route(d, x, wr, ws=ws, stream=st)
+        binding.beam_moe_dispatch(d, ids, ws=ws, stream=st)
+
+    for _ in range(warmup):
+        call()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(st)
+    for _ in range(steps):
+        call()
+    end.record(st)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    T, H, E = wl.tokens, d.hidden, d.num_experts
+    flops = 2 * T * H * E
+    return {"value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+            "config": {"workload": f"router_dispatch: router, selection and dispatch, T={T}", "tokens": T,
+                       "hidden": H, "experts": E, "groups": d.num_groups, "topk_groups": d.topk_groups,
+                       "topk": d.topk},
+            "router_tflops_fp32_equivalent": round(flops / ms / 1e9, 2),
+            "algorithmic_bytes": T * H * 2 + E * H * 4 + T * d.topk * 4 * 4}
 
 
 def timed_loops(call, steps, warmup, stream):
@@ -625,6 +662,11 @@ def main():
         sweep(args, experts, experts_fp8 if args.sweep_fp8 else None)
         return
     results = {}
+    extra = {}
+    if "router_dispatch" in names:
+        names = [n for n in names if n != "router_dispatch"]
+        print("[bench] timing router_dispatch", file=sys.stderr, flush=True)
+        extra["router_dispatch"] = time_router_dispatch(args.steps, args.warmup)
     for name in names:
         print(f"[bench] timing {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
         r = time_workload(name, experts, args.steps, args.warmup, experts_fp8)
@@ -671,6 +713,7 @@ def main():
         line["cpu_baseline"] = cpu_baseline(results[head], args.cpu_seconds)
     for name in names[1:]:
         line[name] = record(name)
+    line.update(extra)
     print(json.dumps(line), flush=True)
 
 
