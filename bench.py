@@ -45,6 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_hbm_traffic_decode_prefil
 KERNEL_SOURCES = ["grouped_top_routing_fp32_amd/csrc/" + f
                   for f in ("common.h", "experts.hip", "grouped_gemm.hip", "dispatch.hip", "abi.cpp")]
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
+# Workloads of the counter runs behind TRAFFIC_FILE: one per gate/up kernel.
+TRAFFIC_WORKLOADS = "decode,prefill,decode_fp8,prefill_fp8"
 GATE_UP_KERNELS = {"decode": "gateup_stream_lds_kernel", "prefill": "grouped_gemm_kernel<true, false>",
                    "decode_fp8": "gateup_stream_fp8_kernel", "prefill_fp8": "grouped_gemm_kernel<true, true>"}
 
@@ -123,9 +125,12 @@ def summarize_pmc(fetch_dir, write_dir):
     w_scale = COPY_BYTES / 1024.0 / copy_kib(write)
     lines = ["# HBM traffic per launch of the gate/up kernel (decode and prefill, bf16 and FP8 weights), from rocprofv3 counters",
              "# fetch:  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-residual --copy-calibration",
+             f"python3 bench.py --workloads {TRAFFIC_WORKLOADS} --steps 3 --warmup 1 --no-cpu-baseline --no-residual "
+             "--copy-calibration",
              "# write:  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-residual --copy-calibration",
+             f"python3 bench.py --workloads {TRAFFIC_WORKLOADS} --steps 3 --warmup 1 --no-cpu-baseline --no-residual "
+             "--copy-calibration",
+             "# (one workload per gate/up kernel: dispatches are told apart by kernel name)",
              "# summary: python3 bench.py --summarize-pmc <FETCH_DIR> <WRITE_DIR>",
              f"# calibration: elementwise copy (torch.neg) of {COPY_BYTES} bytes read and written;"
              f" FETCH_SIZE reads {copy_kib(fetch):.0f} KiB (scale {f_scale:.4f}),"
@@ -216,7 +221,7 @@ def summarize_trace(trace_dir, out_md):
            "", "Command (repository root on the GPU host):", "", "```",
            "cd /tmp && export TMPDIR=/tmp",
            "rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- \\",
-           "    python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+           f"    python3 $REPO/bench.py --workloads {TRAFFIC_WORKLOADS} --steps 10 --warmup 2 --no-cpu-baseline",
            "python3 bench.py --summarize-trace <TRACE_DIR> <this file>", "```", "",
            "Calls are cut before each router_logits_kernel dispatch (before the prenorm_kernel of a",
            "residual-sublayer call); calls that ran the grouped GEMM are prefill, the others decode, with",
