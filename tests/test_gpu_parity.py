@@ -177,7 +177,8 @@ def test_dispatch_on_router_ids():
 # --------------------------------------------------------------------------
 # router end to end (FP32 on the GPU vs FP64 oracle)
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("name,T", [("tiny", 16), ("router_dispatch", 4096), ("skewed", 1000)])
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("router_dispatch", 4096), ("skewed", 1000),
+                                    ("router_dispatch", 16384)])
 def test_route_end_to_end(name, T):
     _announce(f"route e2e {name} T={T}")
     wl = synth.with_tokens(synth.WORKLOADS[name], T)
