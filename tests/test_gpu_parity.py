@@ -285,8 +285,9 @@ def test_forward_skewed(beam_experts):
 
 # Beam dims across the batch sizes where the expert path changes form: T <= 128
 # stream kernels (T = 128: several experts with more than one 8-row pass); from
-# T = 160 the grouped GEMMs, first with nearly empty tiles, then partial ones.
-@pytest.mark.parametrize("T", [1, 8, 128, 160, 512, 1024, 2048])
+# T = 160 the grouped GEMMs, first with nearly empty tiles, then partial ones;
+# T = 32768, twice the prefill batch: about 1024 rows, four tiles, per expert.
+@pytest.mark.parametrize("T", [1, 8, 128, 160, 512, 1024, 2048, 32768])
 def test_forward_beam_sizes(beam_experts, T):
     _announce(f"forward Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
