@@ -219,32 +219,59 @@ class ForwardBuffers:
         self.ws = workspace(dims, T, device)
 
 
+def _req_router(dims: Dims, w_router, logit_bias, select_bias) -> None:
+    E, H = dims.num_experts, dims.hidden
+    _req(w_router, "w_router", torch.float32, (E, H))
+    for t, name in ((logit_bias, "logit_bias"), (select_bias, "select_bias")):
+        if t is not None:
+            _req(t, name, torch.float32, (E,))
+
+
+def _req_bf16_experts(dims: Dims, w_gate, w_up, w_down) -> None:
+    E, I, H = dims.num_experts, dims.intermediate, dims.hidden
+    _req(w_gate, "w_gate", torch.bfloat16, (E, I, H))
+    _req(w_up, "w_up", torch.bfloat16, (E, I, H))
+    _req(w_down, "w_down", torch.bfloat16, (E, H, I))
+
+
+def _req_fp8_experts(dims: Dims, w_gate_fp8, gate_scale, w_up_fp8, up_scale, w_down_fp8, down_scale) -> None:
+    E, I, H = dims.num_experts, dims.intermediate, dims.hidden
+    _req(w_gate_fp8, "w_gate_fp8", torch.uint8, (E, I, H))
+    _req(w_up_fp8, "w_up_fp8", torch.uint8, (E, I, H))
+    _req(w_down_fp8, "w_down_fp8", torch.uint8, (E, H, I))
+    _req(gate_scale, "gate_scale", torch.float32, (E, I))
+    _req(up_scale, "up_scale", torch.float32, (E, I))
+    _req(down_scale, "down_scale", torch.float32, (E, H))
+
+
+def _buffers(dims: Dims, T: int, device, bufs: Optional[ForwardBuffers]) -> ForwardBuffers:
+    if bufs is None:
+        return ForwardBuffers(dims, T, device)
+    if bufs.T != T:
+        raise ValueError("buffers were sized for another T")
+    return bufs
+
+
+def _outputs(bufs: ForwardBuffers, out: torch.Tensor):
+    """Pointer arguments from `out` through the workspace, as every forward entry point takes them."""
+    return (_ptr(out), _ptr(bufs.ids), _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets), _ptr(bufs.slots),
+            _ptr(bufs.ws), bufs.ws.numel())
+
+
 def beam_moe_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],
                      w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, *,
                      select_bias: Optional[torch.Tensor] = None, bufs: Optional[ForwardBuffers] = None,
                      stream=None) -> ForwardBuffers:
     """The whole block. Returns the ForwardBuffers holding out and the routing by-products."""
     T = x.shape[0]
-    H, I, E = dims.hidden, dims.intermediate, dims.num_experts
-    _req(x, "x", torch.bfloat16, (T, H))
-    _req(w_router, "w_router", torch.float32, (E, H))
-    if logit_bias is not None:
-        _req(logit_bias, "logit_bias", torch.float32, (E,))
-    if select_bias is not None:
-        _req(select_bias, "select_bias", torch.float32, (E,))
-    _req(w_gate, "w_gate", torch.bfloat16, (E, I, H))
-    _req(w_up, "w_up", torch.bfloat16, (E, I, H))
-    _req(w_down, "w_down", torch.bfloat16, (E, H, I))
-    if bufs is None:
-        bufs = ForwardBuffers(dims, T, x.device)
-    if bufs.T != T:
-        raise ValueError("buffers were sized for another T")
+    _req(x, "x", torch.bfloat16, (T, dims.hidden))
+    _req_router(dims, w_router, logit_bias, select_bias)
+    _req_bf16_experts(dims, w_gate, w_up, w_down)
+    bufs = _buffers(dims, T, x.device, bufs)
     cd = _cdims(dims)
     st = load_library().beam_moe_forward(
         ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate), _ptr(w_up),
-        _ptr(w_down),
-        _ptr(bufs.out), _ptr(bufs.ids), _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets), _ptr(bufs.slots),
-        _ptr(bufs.ws), bufs.ws.numel(), _stream(stream))
+        _ptr(w_down), *_outputs(bufs, bufs.out), _stream(stream))
     _check(st, "beam_moe_forward")
     return bufs
 
@@ -256,31 +283,30 @@ def beam_moe_forward_fp8(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, lo
                          stream=None) -> ForwardBuffers:
     """The whole block with E4M3 expert weights (uint8 codes) and fp32 per-row scales."""
     T = x.shape[0]
-    H, I, E = dims.hidden, dims.intermediate, dims.num_experts
-    _req(x, "x", torch.bfloat16, (T, H))
-    _req(w_router, "w_router", torch.float32, (E, H))
-    if logit_bias is not None:
-        _req(logit_bias, "logit_bias", torch.float32, (E,))
-    if select_bias is not None:
-        _req(select_bias, "select_bias", torch.float32, (E,))
-    _req(w_gate_fp8, "w_gate_fp8", torch.uint8, (E, I, H))
-    _req(w_up_fp8, "w_up_fp8", torch.uint8, (E, I, H))
-    _req(w_down_fp8, "w_down_fp8", torch.uint8, (E, H, I))
-    _req(gate_scale, "gate_scale", torch.float32, (E, I))
-    _req(up_scale, "up_scale", torch.float32, (E, I))
-    _req(down_scale, "down_scale", torch.float32, (E, H))
-    if bufs is None:
-        bufs = ForwardBuffers(dims, T, x.device)
-    if bufs.T != T:
-        raise ValueError("buffers were sized for another T")
+    _req(x, "x", torch.bfloat16, (T, dims.hidden))
+    _req_router(dims, w_router, logit_bias, select_bias)
+    _req_fp8_experts(dims, w_gate_fp8, gate_scale, w_up_fp8, up_scale, w_down_fp8, down_scale)
+    bufs = _buffers(dims, T, x.device, bufs)
     cd = _cdims(dims)
     st = load_library().beam_moe_forward_fp8(
         ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate_fp8),
         _ptr(gate_scale), _ptr(w_up_fp8), _ptr(up_scale), _ptr(w_down_fp8), _ptr(down_scale),
-        _ptr(bufs.out), _ptr(bufs.ids), _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets), _ptr(bufs.slots),
-        _ptr(bufs.ws), bufs.ws.numel(), _stream(stream))
+        *_outputs(bufs, bufs.out), _stream(stream))
     _check(st, "beam_moe_forward_fp8")
     return bufs
+
+
+def _residual_prelude(dims: Dims, stream_in, norm_in_weight, norm_out_weight, stream_out, bufs):
+    T = stream_in.shape[0]
+    H = dims.hidden
+    _req(stream_in, "stream_in", torch.float32, (T, H))
+    for t, name in ((norm_in_weight, "norm_in_weight"), (norm_out_weight, "norm_out_weight")):
+        if t is not None:
+            _req(t, name, torch.float32, (H,))
+    bufs = _buffers(dims, T, stream_in.device, bufs)
+    if stream_out is not None:
+        _req(stream_out, "stream_out", torch.float32, (T, H))
+    return T, bufs, (stream_out if stream_out is not None else bufs.out)
 
 
 def beam_moe_residual_forward(dims: Dims, stream_in: torch.Tensor, step: int, w_router: torch.Tensor,
@@ -290,31 +316,16 @@ def beam_moe_residual_forward(dims: Dims, stream_in: torch.Tensor, step: int, w_
                               norm_out_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
                               stream_out: Optional[torch.Tensor] = None, bufs: Optional[ForwardBuffers] = None,
                               stream=None) -> ForwardBuffers:
-    """The block as a residual sublayer at `step`. bufs.out holds the new stream (stream_out if given)."""
-    T = stream_in.shape[0]
-    H, I, E = dims.hidden, dims.intermediate, dims.num_experts
-    _req(stream_in, "stream_in", torch.float32, (T, H))
-    _req(w_router, "w_router", torch.float32, (E, H))
-    for t, name, n in ((logit_bias, "logit_bias", E), (select_bias, "select_bias", E),
-                       (norm_in_weight, "norm_in_weight", H), (norm_out_weight, "norm_out_weight", H)):
-        if t is not None:
-            _req(t, name, torch.float32, (n,))
-    _req(w_gate, "w_gate", torch.bfloat16, (E, I, H))
-    _req(w_up, "w_up", torch.bfloat16, (E, I, H))
-    _req(w_down, "w_down", torch.bfloat16, (E, H, I))
-    if bufs is None:
-        bufs = ForwardBuffers(dims, T, stream_in.device)
-    if bufs.T != T:
-        raise ValueError("buffers were sized for another T")
-    if stream_out is not None:
-        _req(stream_out, "stream_out", torch.float32, (T, H))
-        bufs.out = stream_out
+    """The block as a residual sublayer at `step`: the new stream goes to stream_out if given (it may be
+    stream_in itself), else to bufs.out; the routing by-products to bufs."""
+    T, bufs, out = _residual_prelude(dims, stream_in, norm_in_weight, norm_out_weight, stream_out, bufs)
+    _req_router(dims, w_router, logit_bias, select_bias)
+    _req_bf16_experts(dims, w_gate, w_up, w_down)
     cd = _cdims(dims)
     st = load_library().beam_moe_residual_forward(
         ctypes.byref(cd), T, _ptr(stream_in), int(step), _ptr(norm_in_weight), _ptr(norm_out_weight),
         float(norm_eps), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate), _ptr(w_up),
-        _ptr(w_down), _ptr(bufs.out), _ptr(bufs.ids), _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets),
-        _ptr(bufs.slots), _ptr(bufs.ws), bufs.ws.numel(), _stream(stream))
+        _ptr(w_down), *_outputs(bufs, out), _stream(stream))
     _check(st, "beam_moe_residual_forward")
     return bufs
 
@@ -328,35 +339,15 @@ def beam_moe_residual_forward_fp8(dims: Dims, stream_in: torch.Tensor, step: int
                                   norm_out_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
                                   stream_out: Optional[torch.Tensor] = None, bufs: Optional[ForwardBuffers] = None,
                                   stream=None) -> ForwardBuffers:
-    """The block with E4M3 expert weights as a residual sublayer at `step`; bufs.out holds the new stream."""
-    T = stream_in.shape[0]
-    H, I, E = dims.hidden, dims.intermediate, dims.num_experts
-    _req(stream_in, "stream_in", torch.float32, (T, H))
-    _req(w_router, "w_router", torch.float32, (E, H))
-    for t, name, n in ((logit_bias, "logit_bias", E), (select_bias, "select_bias", E),
-                       (norm_in_weight, "norm_in_weight", H), (norm_out_weight, "norm_out_weight", H)):
-        if t is not None:
-            _req(t, name, torch.float32, (n,))
-    _req(w_gate_fp8, "w_gate_fp8", torch.uint8, (E, I, H))
-    _req(w_up_fp8, "w_up_fp8", torch.uint8, (E, I, H))
-    _req(w_down_fp8, "w_down_fp8", torch.uint8, (E, H, I))
-    _req(gate_scale, "gate_scale", torch.float32, (E, I))
-    _req(up_scale, "up_scale", torch.float32, (E, I))
-    _req(down_scale, "down_scale", torch.float32, (E, H))
-    if bufs is None:
-        bufs = ForwardBuffers(dims, T, stream_in.device)
-    if bufs.T != T:
-        raise ValueError("buffers were sized for another T")
-    if stream_out is not None:
-        _req(stream_out, "stream_out", torch.float32, (T, H))
-        bufs.out = stream_out
+    """beam_moe_residual_forward with E4M3 expert weights and fp32 per-row scales."""
+    T, bufs, out = _residual_prelude(dims, stream_in, norm_in_weight, norm_out_weight, stream_out, bufs)
+    _req_router(dims, w_router, logit_bias, select_bias)
+    _req_fp8_experts(dims, w_gate_fp8, gate_scale, w_up_fp8, up_scale, w_down_fp8, down_scale)
     cd = _cdims(dims)
     st = load_library().beam_moe_residual_forward_fp8(
         ctypes.byref(cd), T, _ptr(stream_in), int(step), _ptr(norm_in_weight), _ptr(norm_out_weight),
         float(norm_eps), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate_fp8), _ptr(gate_scale),
-        _ptr(w_up_fp8), _ptr(up_scale), _ptr(w_down_fp8), _ptr(down_scale), _ptr(bufs.out), _ptr(bufs.ids),
-        _ptr(bufs.w), _ptr(bufs.counts), _ptr(bufs.offsets), _ptr(bufs.slots), _ptr(bufs.ws), bufs.ws.numel(),
-        _stream(stream))
+        _ptr(w_up_fp8), _ptr(up_scale), _ptr(w_down_fp8), _ptr(down_scale), *_outputs(bufs, out), _stream(stream))
     _check(st, "beam_moe_residual_forward_fp8")
     return bufs
 

@@ -247,6 +247,42 @@ struct BlockArgs {
   int32_t* sorted_slots;
 };
 
+// The block's arguments with bf16 experts, or with FP8 ones (codes and row
+// scales); x may be filled in later (the residual entry points' pre-norm).
+BlockArgs bf16_block(const void* x, const float* w_router, const float* logit_bias, const float* select_bias,
+                     const void* w_gate, const void* w_up, const void* w_down, int32_t* topk_ids, float* topk_w,
+                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots) {
+  BlockArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w_router = w_router;
+  a.logit_bias = logit_bias;
+  a.select_bias = select_bias;
+  a.wg = static_cast<const uint16_t*>(w_gate);
+  a.wu = static_cast<const uint16_t*>(w_up);
+  a.wd = static_cast<const uint16_t*>(w_down);
+  a.topk_ids = topk_ids;
+  a.topk_w = topk_w;
+  a.expert_counts = expert_counts;
+  a.expert_offsets = expert_offsets;
+  a.sorted_slots = sorted_slots;
+  return a;
+}
+
+BlockArgs fp8_block(const void* x, const float* w_router, const float* logit_bias, const float* select_bias,
+                    const uint8_t* w_gate, const float* gate_scale, const uint8_t* w_up, const float* up_scale,
+                    const uint8_t* w_down, const float* down_scale, int32_t* topk_ids, float* topk_w,
+                    int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots) {
+  BlockArgs a = bf16_block(x, w_router, logit_bias, select_bias, nullptr, nullptr, nullptr, topk_ids, topk_w,
+                           expert_counts, expert_offsets, sorted_slots);
+  a.qg = w_gate;
+  a.qu = w_up;
+  a.qd = w_down;
+  a.sg = gate_scale;
+  a.su = up_scale;
+  a.sd = down_scale;
+  return a;
+}
+
 // `pre()` (whatever produces the block's input; nothing for beam_moe_forward),
 // then router, selection, dispatch and the expert projections on the caller's
 // stream, then `combine(y16, yscale)` (the final step of the entry point).
@@ -422,24 +458,8 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   Plan p;
   make_plan(d, T, &p);
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
-  BlockArgs a{static_cast<const uint16_t*>(x_bf16),
-              w_router,
-              logit_bias,
-              select_bias,
-              static_cast<const uint16_t*>(w_gate),
-              static_cast<const uint16_t*>(w_up),
-              static_cast<const uint16_t*>(w_down),
-              nullptr,
-              nullptr,
-              nullptr,
-              nullptr,
-              nullptr,
-              nullptr,
-              topk_ids,
-              topk_w,
-              expert_counts,
-              expert_offsets,
-              sorted_slots};
+  BlockArgs a = bf16_block(x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, topk_ids, topk_w,
+                           expert_counts, expert_offsets, sorted_slots);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return run_block(
       d, p, a, ws, st, [] { return hipSuccess; },
@@ -466,24 +486,8 @@ int beam_moe_forward_fp8(const beam_moe_dims* d, int32_t T, const void* x_bf16, 
   Plan p;
   make_plan(d, T, &p, true);
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
-  BlockArgs a{static_cast<const uint16_t*>(x_bf16),
-              w_router,
-              logit_bias,
-              select_bias,
-              nullptr,
-              nullptr,
-              nullptr,
-              w_gate_fp8,
-              w_up_fp8,
-              w_down_fp8,
-              gate_scale,
-              up_scale,
-              down_scale,
-              topk_ids,
-              topk_w,
-              expert_counts,
-              expert_offsets,
-              sorted_slots};
+  BlockArgs a = fp8_block(x_bf16, w_router, logit_bias, select_bias, w_gate_fp8, gate_scale, w_up_fp8, up_scale,
+                          w_down_fp8, down_scale, topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return run_block(
       d, p, a, ws, st, [] { return hipSuccess; },
@@ -501,24 +505,8 @@ int beam_moe_residual_forward(const beam_moe_dims* d, int32_t T, const float* st
   int rc = check_common(d, T);
   if (rc != BEAM_MOE_OK) return rc;
   if (T > 0 && (rc = check_ptrs({w_gate, w_up, w_down})) != BEAM_MOE_OK) return rc;
-  BlockArgs a{nullptr,
-              w_router,
-              logit_bias,
-              select_bias,
-              static_cast<const uint16_t*>(w_gate),
-              static_cast<const uint16_t*>(w_up),
-              static_cast<const uint16_t*>(w_down),
-              nullptr,
-              nullptr,
-              nullptr,
-              nullptr,
-              nullptr,
-              nullptr,
-              topk_ids,
-              topk_w,
-              expert_counts,
-              expert_offsets,
-              sorted_slots};
+  BlockArgs a = bf16_block(nullptr, w_router, logit_bias, select_bias, w_gate, w_up, w_down, topk_ids, topk_w,
+                           expert_counts, expert_offsets, sorted_slots);
   return residual_block(d, T, stream_in, step, norm_in_weight, norm_out_weight, norm_eps, a, false, stream_out, ws,
                         ws_bytes, stream);
 }
@@ -537,24 +525,8 @@ int beam_moe_residual_forward_fp8(const beam_moe_dims* d, int32_t T, const float
   if (T > 0 &&
       (rc = check_ptrs({w_gate_fp8, gate_scale, w_up_fp8, up_scale, w_down_fp8, down_scale})) != BEAM_MOE_OK)
     return rc;
-  BlockArgs a{nullptr,
-              w_router,
-              logit_bias,
-              select_bias,
-              nullptr,
-              nullptr,
-              nullptr,
-              w_gate_fp8,
-              w_up_fp8,
-              w_down_fp8,
-              gate_scale,
-              up_scale,
-              down_scale,
-              topk_ids,
-              topk_w,
-              expert_counts,
-              expert_offsets,
-              sorted_slots};
+  BlockArgs a = fp8_block(nullptr, w_router, logit_bias, select_bias, w_gate_fp8, gate_scale, w_up_fp8, up_scale,
+                          w_down_fp8, down_scale, topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots);
   return residual_block(d, T, stream_in, step, norm_in_weight, norm_out_weight, norm_eps, a, true, stream_out, ws,
                         ws_bytes, stream);
 }

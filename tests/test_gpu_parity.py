@@ -443,8 +443,10 @@ def test_residual_mid(name):
     new1 = bufs.out.clone()
     inplace = stream.clone()
     binding.beam_moe_residual_forward(p.dims, inplace, 4, p.wr, p.bias, p.wg, p.wu, p.wd, norm_in_weight=g_in,
-                                      norm_out_weight=g_out, stream_out=inplace)
+                                      norm_out_weight=g_out, stream_out=inplace, bufs=bufs)
     assert torch.equal(inplace, new1)
+    # stream_out is per call: the buffers keep their own out, untouched by that call
+    assert bufs.out.data_ptr() != inplace.data_ptr() and torch.equal(bufs.out, new1)
     binding.beam_moe_residual_forward(p.dims, stream, 4, p.wr, p.bias, p.wg, p.wu, p.wd, norm_in_weight=g_in,
                                       norm_out_weight=g_out, bufs=bufs)
     assert torch.equal(bufs.out, new1)
