@@ -71,8 +71,9 @@ def parse():
                     help="instead of the decode/prefill line: tokens/s and roofline fractions over batch sizes T")
     ap.add_argument("--sweep-fp8", action="store_true", help="the T sweep through the FP8-weight entry point")
     ap.add_argument("--sweep-tokens", default="1,2,4,8,16,32,64,128,256,512,1024,2048,4096,8192,16384")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_DIR", "OUT_MD"),
-                    help="per-kernel counter summary of a rocprofv3 --pmc run of this script")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="OUT_MD WORKLOADS=COUNTER_DIR",
+                    help="per-kernel counter summary of rocprofv3 --pmc runs of this script, one run per "
+                         "WORKLOADS (the --workloads value it was given) and COUNTER_DIR")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="time the GEMM library on the prefill MoE shapes (context for the grouped GEMMs) and exit")
     ap.add_argument("--summarize-sweep", nargs=2, metavar=("SWEEP_JSON", "OUT_MD"),
@@ -525,50 +526,62 @@ def sweep(args, experts, experts_fp8=None):
                       "points": points}), flush=True)
 
 
-def summarize_counters(counter_dir, out_md):
-    """Per-kernel means of every counter of a rocprofv3 --pmc run of this script, plus the
-    derived MFMA-busy and wave-wait fractions where their counters were collected."""
+COUNTER_SET = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+               "SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_LDS_DATA_FIFO_FULL GRBM_GUI_ACTIVE")
+
+
+def summarize_counters(out_md, *passes):
+    """Per-kernel means of every counter of rocprofv3 --pmc runs of this script, plus the derived
+    MFMA-busy and wave-wait fractions where their counters were collected.  Each pass is
+    WORKLOADS=COUNTER_DIR: one run with --workloads WORKLOADS, so that workloads whose kernels share
+    a name (prefill and skewed) are summarised apart."""
     import csv
     import glob
-    per, order = {}, []
-    for path in sorted(glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True)):
-        with open(path) as f:
-            disp = {}
-            for r in csv.DictReader(f):
-                if "beam::" not in r["Kernel_Name"]:
-                    continue
-                d = disp.setdefault(r["Dispatch_Id"], {"kernel": r["Kernel_Name"]})
-                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-            for d in disp.values():
-                name = d.pop("kernel").replace("void ", "")
-                name = name[:name.index("(")] if "(" in name else name
-                if name not in per:
-                    order.append(name)
-                per.setdefault(name, []).append(d)
     simds, xcds = 256 * 4, 8
-    cmd = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
-           "SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_LDS_DATA_FIFO_FULL GRBM_GUI_ACTIVE --output-format csv "
-           "-d <COUNTER_DIR> -o run -- python3 bench.py --workloads prefill,decode --steps 2 --warmup 1 "
-           "--no-cpu-baseline --no-residual")
-    out = ["# rocprofv3 counters per kernel: Beam MoE block forward, prefill T=16384 and decode T=64", "",
-           "Commands (repository root on the GPU host, after `cd /tmp && export TMPDIR=/tmp`):", "", "```", cmd,
-           "python3 bench.py --summarize-counters <COUNTER_DIR> <this file>", "```", "",
+    sections, cmds = [], []
+    for spec in passes:
+        workloads, counter_dir = spec.split("=", 1)
+        cmds.append(f"rocprofv3 --pmc {COUNTER_SET} --output-format csv -d <COUNTER_DIR_{len(cmds) + 1}> -o run "
+                    f"-- python3 bench.py --workloads {workloads} --steps 2 --warmup 1 --no-cpu-baseline --no-residual")
+        per, order = {}, []
+        for path in sorted(glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True)):
+            with open(path) as f:
+                disp = {}
+                for r in csv.DictReader(f):
+                    if "beam::" not in r["Kernel_Name"]:
+                        continue
+                    d = disp.setdefault(r["Dispatch_Id"], {"kernel": r["Kernel_Name"]})
+                    d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                for d in disp.values():
+                    name = d.pop("kernel").replace("void ", "")
+                    name = name[:name.index("(")] if "(" in name else name
+                    if name not in per:
+                        order.append(name)
+                    per.setdefault(name, []).append(d)
+        for name in order:
+            rows = per[name]
+            keys = sorted({k for d in rows for k in d})
+            mean = {k: sum(d.get(k, 0.0) for d in rows) / len(rows) for k in keys}
+            sec = [f"## {workloads}: `{name}` ({len(rows)} dispatches)", "", "| counter | mean per dispatch |",
+                   "|---|---|"]
+            sec += [f"| {k} | {mean[k]:.4g} |" for k in keys]
+            if mean.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / (mean["GRBM_GUI_ACTIVE"] / xcds)
+                sec.append(f"| MFMA busy (derived) | {busy:.3f} |")
+            if mean.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in mean:
+                sec.append(f"| wave wait (derived) | {mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.3f} |")
+            sections += sec + [""]
+    out = ["# rocprofv3 counters per kernel: Beam MoE block forward, decode T=64, prefill T=16384, "
+           "skewed T=8192", "",
+           "Commands (repository root on the GPU host, after `cd /tmp && export TMPDIR=/tmp`), one counter run per "
+           "line of workloads:", "", "```"] + cmds + [
+           "python3 bench.py --summarize-counters <this file> " +
+           " ".join(f"{spec.split('=', 1)[0]}=<COUNTER_DIR_{i + 1}>" for i, spec in enumerate(passes)), "```", "",
            "Values are per dispatch, each counter summed over the dimensions rocprofv3 reports it in, then",
            "averaged over the dispatches.  Derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x",
            "GRBM_GUI_ACTIVE / 8 XCDs), the share of every SIMD's cycles its matrix unit was busy; wave wait =",
            "SQ_WAIT_ANY / SQ_WAVE_CYCLES, the share of wave time spent waiting (on memory counters or a barrier).",
-           ""]
-    for name in order:
-        rows = per[name]
-        keys = sorted({k for d in rows for k in d})
-        mean = {k: sum(d.get(k, 0.0) for d in rows) / len(rows) for k in keys}
-        out += [f"## `{name}` ({len(rows)} dispatches)", "", "| counter | mean per dispatch |", "|---|---|"]
-        out += [f"| {k} | {mean[k]:.4g} |" for k in keys]
-        if mean.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
-            out.append(f"| MFMA busy (derived) | {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / simds / (mean['GRBM_GUI_ACTIVE'] / xcds):.3f} |")
-        if mean.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in mean:
-            out.append(f"| wave wait (derived) | {mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.3f} |")
-        out.append("")
+           ""] + sections
     with open(out_md, "w") as f:
         f.write("\n".join(out))
     print("\n".join(out))
