@@ -34,7 +34,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// SiLU in FP32: g / (1 + e^-g), with e^-g = 2^(-g log2 e) from the hardware base-2
+// exponential and the quotient from the hardware reciprocal (each about 1 ulp);
+// large negative g gives e^-g = inf, a zero reciprocal and silu = -0.
+__device__ __forceinline__ float silu_f32(float g) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // Eight bf16 values (one 16-byte operand) to eight fp16 values. bf16 has 8
 // significant bits and fp16 11, so the conversion is exact for magnitudes in
