@@ -133,9 +133,11 @@ int beam_moe_dispatch(const beam_moe_dims* dims, int32_t T, const int32_t* topk_
  * times a power-of-two scale shared by a block of 64 columns of a row group,
  * chosen so the block's largest magnitude stays below 2^15 (no overflow);
  * the down projection runs on fp16 MFMA with FP32 accumulation, with W_down
- * converted from bf16 to fp16 exactly (magnitudes below 2^-14 after scaling
- * become fp16 subnormals, rounded toward zero). Expert outputs and the
- * weighted sum are FP32, summed over k in ascending k order.
+ * converted from bf16 to fp16, exactly where representable (magnitudes below
+ * 2^-14 after scaling become fp16 subnormals, rounded toward zero). The expert
+ * outputs leave the down projection the same way (fp16 times a power-of-two
+ * scale per 64 columns of a row group); out is their weighted sum in FP32,
+ * over k in ascending order.
  * Supported intermediate sizes additionally satisfy intermediate <= 32768. */
 int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
                      const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
@@ -208,7 +210,7 @@ int beam_moe_residual_forward_fp8(const beam_moe_dims* dims, int32_t T, const fl
 /* Diagnostics: device time of the stages of beam_moe_forward,
  * beam_moe_forward_fp8 and both residual entry points ("prenorm" is empty
  * except in the last two).
- * beam_moe_timing_enable(1) makes later calls of either record HIP
+ * beam_moe_timing_enable(1) makes later calls of any of them record HIP
  * events between their stages on the caller's stream (a marker per stage,
  * no synchronisation; the events are created by the library on first use and
  * kept for reuse). beam_moe_timing_read waits for the last recorded call,
