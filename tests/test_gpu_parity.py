@@ -461,10 +461,12 @@ def test_residual_selection_bias():
     print(f"  excluded {excluded}, worst error / tolerance {worst:.3f}")
 
 
-@pytest.mark.parametrize("T", [64, 1024])
-def test_residual_beam(beam_experts, T):
-    _announce(f"residual Beam T={T}")
-    wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
+# the three batches the residual entry point is timed on (decode, prefill and the skewed
+# batch), plus one in between
+@pytest.mark.parametrize("name,T", [("decode", 64), ("decode", 1024), ("prefill", 16384), ("skewed", 8192)])
+def test_residual_beam(beam_experts, name, T):
+    _announce(f"residual Beam {name} T={T}")
+    wl = synth.with_tokens(synth.WORKLOADS[name], T)
     p, stream, g_in, g_out, bufs = _residual_case(wl, 3, True, experts=beam_experts)
     sample = sorted({t for t in (0, 1, 2, 3, T // 2, T - 1) if t < T})
     excluded, worst = residual_parity(p, stream, 3, bufs, sample, g_in=g_in, g_out=g_out)
@@ -542,7 +544,7 @@ def test_forward_fp8_rejects_unsupported_intermediate():
     assert ei.value.status == binding.BEAM_MOE_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("T", [1, 64, 512, 2048])
+@pytest.mark.parametrize("T", [1, 64, 512, 2048, 16384])
 def test_forward_fp8_beam(beam_experts_fp8, T):
     _announce(f"forward fp8 Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
