@@ -154,13 +154,17 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   using BReg = std::conditional_t<FP8, uint2, u32x4>;
   BReg breg[4];
   const uint8_t* tscale = GATEUP ? nullptr : hscale + (size_t)tl.row_start * (Kdim / kScaleCols);
+  // down: the stage's activation scale exponent is loaded with its weights, so
+  // that its latency, like theirs, passes under the MFMAs of the current step
+  int bsexp = 0;
   auto load_b = [&](int stage) {
     const int k = stage * kBK;
+    if constexpr (!GATEUP) bsexp = tscale[stage];  // kBK == kScaleCols: one activation block per stage
 #pragma unroll
     for (int q = 0; q < 4; ++q) breg[q] = *reinterpret_cast<const BReg*>(bsrc[q] + k);
   };
   auto store_b = [&](int stage, int slot) {
-    const int sexp = GATEUP ? 0 : tscale[stage];  // kBK == kScaleCols: one activation block per stage
+    const int sexp = bsexp;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       u32x4 v;
