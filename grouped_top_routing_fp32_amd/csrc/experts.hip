@@ -32,9 +32,18 @@ namespace beam {
 // ---------------------------------------------------------------------------
 // stream kernels (few rows per expert)
 // ---------------------------------------------------------------------------
+// Destination slots of this lane's rows (4 (lane / 16) + r) of a pass, read
+// when the pass starts so that the loads complete under its main loop; rows
+// past the pass's end read its last row and are never stored.
+__device__ __forceinline__ void load_y_slots(const int32_t* __restrict__ slot_of, int nrows, int32_t (&yslot)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) yslot[r] = slot_of[min((lane >> 4) * 4 + r, nrows - 1)];
+}
+
 // Writes one pass of y: fp16 bits of acc * 2^-s, s from the largest magnitude
 // of the pass's rows in the workgroup's 64 columns, and s per (row, block).
-__device__ __forceinline__ void store_y_pass(const f32x4& acc, int nrows, const int32_t* __restrict__ slot_of,
+__device__ __forceinline__ void store_y_pass(const f32x4& acc, int nrows, const int32_t (&yslot)[4],
                                              uint16_t* __restrict__ y16, uint8_t* __restrict__ yscale, int H,
                                              int col, float* smax) {
   const int lane = threadIdx.x & 63;
@@ -51,7 +60,7 @@ __device__ __forceinline__ void store_y_pass(const f32x4& acc, int nrows, const 
   for (int r = 0; r < 4; ++r) {
     const int row = (lane >> 4) * 4 + r;
     if (row < nrows) {
-      const size_t slot = (size_t)slot_of[row];
+      const size_t slot = (size_t)yslot[r];
       y16[slot * H + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[r], -sexp));
       if (wave == 0 && (lane & 15) == 0) yscale[slot * (H / kScaleCols) + blockIdx.y] = (uint8_t)sexp;
     }
@@ -250,6 +259,8 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
 
   for (int p = 0; p < tl.rows; p += kLdsRows) {
     const int nrows = min(kLdsRows, tl.rows - p);
+    int32_t yslot[4];
+    load_y_slots(sorted_slots + tl.row_start + p, nrows, yslot);
     const int xr = 2 * wave + min(1, lane / G::kLPR);
     const uint16_t* xsrc = stage_src<SK>(h + (size_t)(tl.row_start + p + min(xr, nrows - 1)) * I, 64 + xr, lane);
     auto issue = [&](int st, int slot) {
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
         acc = mfma16x16x32_f16(rv ? a : u32x4{0u, 0u, 0u, 0u}, bh, acc);
       }
     }
-    store_y_pass(acc, nrows, sorted_slots + tl.row_start + p, y16, yscale, H, col, smax);
+    store_y_pass(acc, nrows, yslot, y16, yscale, H, col, smax);
     __syncthreads();  // every wave is done with the ring and the scales before the next pass
   }
 }
@@ -513,6 +524,8 @@ __global__ __launch_bounds__(256) void down_stream_fp8_kernel(const uint16_t* __
 
   for (int p = 0; p < tl.rows; p += kLdsRows) {
     const int nrows = min(kLdsRows, tl.rows - p);
+    int32_t yslot[4];
+    load_y_slots(sorted_slots + tl.row_start + p, nrows, yslot);
     const int xr = 2 * wave + (lane >> 5);
     const unsigned char* xsrc =
         reinterpret_cast<const unsigned char*>(h + (size_t)(tl.row_start + p + min(xr, nrows - 1)) * I) +
@@ -570,7 +583,7 @@ __global__ __launch_bounds__(256) void down_stream_fp8_kernel(const uint16_t* __
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] *= scale_d;
-    store_y_pass(acc, nrows, sorted_slots + tl.row_start + p, y16, yscale, H, col, smax);
+    store_y_pass(acc, nrows, yslot, y16, yscale, H, col, smax);
     __syncthreads();  // every wave is done with the ring and the scales before the next pass
   }
 }
