@@ -1,6 +1,7 @@
 """CPU tests of bench.py's measurement tooling, on synthetic rocprofv3 csv files: the source hash
 that gates the reported traffic, the traffic summary (copy calibration, per-kernel means, the
-hash stamp) with its reader, and the labelled per-kernel counter summary."""
+hash stamp) with its reader, the labelled per-kernel counter summary and the kernel-trace
+summary's cutting of a trace into calls."""
 import csv
 import os
 
@@ -75,3 +76,44 @@ def test_counter_summary_keeps_passes_apart(tmp_path):
     assert "| MFMA busy (derived) | 0.500 |" in prefill and "| MFMA busy (derived) | 0.250 |" in skewed
     assert "| wave wait (derived) | 0.300 |" in prefill
     assert "--workloads prefill " in text and "--workloads skewed " in text
+
+
+def test_trace_summary_cuts_and_classifies_calls(tmp_path):
+    """Four calls in a row (decode, prefill, FP8 decode, a residual-sublayer decode): each is cut at
+    its router (or its prenorm) and filed under its workload; other kernels are ignored."""
+    calls = [
+        ["router_logits_kernel<64>", "select_kernel", "dispatch_small_kernel", "gateup_stream_lds_kernel<3, 128>",
+         "down_stream_lds_kernel<3, 128>", "combine_kernel"],
+        ["router_logits_kernel<128>", "select_kernel", "dispatch_hist_kernel", "dispatch_scan_kernel",
+         "dispatch_scatter_kernel", "grouped_gemm_kernel<true, false>", "grouped_gemm_kernel<false, false>",
+         "combine_kernel"],
+        ["router_logits_kernel<64>", "select_kernel", "dispatch_small_kernel", "gateup_stream_fp8_kernel<3>",
+         "down_stream_fp8_kernel<3>", "combine_kernel"],
+        ["prenorm_kernel", "router_logits_kernel<64>", "select_kernel", "dispatch_small_kernel",
+         "gateup_stream_lds_kernel<3, 128>", "down_stream_lds_kernel<3, 128>", "combine_residual_kernel"],
+    ]
+    os.makedirs(tmp_path / "trace" / "host")
+    t = 1000
+    with open(tmp_path / "trace" / "host" / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for ci, c in enumerate(calls):
+            for ki, k in enumerate(c):
+                dur = 1000 * (ci + 1) + 100 * ki  # ns
+                w.writerow([f"void beam::{k}(int)", t, t + dur])
+                t += dur + 50
+            w.writerow(["void at::native::fill_kernel(int)", t, t + 5])  # not the library's
+            t += 100
+    out = tmp_path / "kernels.md"
+    bench.summarize_trace(str(tmp_path / "trace"), str(out))
+    text = out.read_text()
+    sections = {s.split("\n", 1)[0]: s for s in text.split("\n## ")[1:]}
+    assert set(sections) == {"decode", "prefill", "decode_fp8", "decode, residual sublayer"}
+    # each call's kernels are filed under its own workload, with its own durations (1 us per call
+    # index, plus 0.1 us per position in the call)
+    assert "`beam::grouped_gemm_kernel<true, false>` | 1 | 2.5 |" in sections["prefill"]
+    assert "`beam::gateup_stream_fp8_kernel<3>` | 1 | 3.3 |" in sections["decode_fp8"]
+    assert "`beam::prenorm_kernel` | 1 | 4.0 |" in sections["decode, residual sublayer"]
+    assert "`beam::router_logits_kernel<64>` | 1 | 4.1 |" in sections["decode, residual sublayer"]
+    assert "`beam::combine_kernel` | 1 | 1.5 |" in sections["decode"]
+    assert "fill_kernel" not in text
