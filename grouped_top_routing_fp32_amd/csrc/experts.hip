@@ -25,6 +25,8 @@
 // per 256-row tile rather than once per pass.
 #include <atomic>
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace beam {
@@ -688,17 +690,20 @@ hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const in
 // ---------------------------------------------------------------------------
 // combine: out[t] = sum_k w[t,k] * y[t*K + k], k ascending, FP32
 // ---------------------------------------------------------------------------
-constexpr int kCombineCols = 2048;  // columns per workgroup (256 threads x 8)
+constexpr int kCombineMaxThreads = 1024;
 
-// grid: (T, ceil(H / 2048)); block 256.  A thread owns 8 consecutive columns:
-// the K rows of its token (fp16, each with its 64-column scale) are loaded
-// together (up to 16, 16 bytes each), then summed in ascending k in FP32.
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y16,
-                                                      const uint8_t* __restrict__ yscale,
-                                                      const float* __restrict__ w, float* __restrict__ out, int H,
-                                                      int K) {
+// grid: (T, ceil(H / (8 * blockDim.x))); from 512 tokens blockDim.x = H / 8
+// rounded up to whole waves (at most 1024), so a token's row is one workgroup up
+// to H = 8192; below that 256 (2048 columns per workgroup).  A
+// thread owns 8 consecutive columns: the K rows of its token (fp16, each with
+// its 64-column scale) are loaded together (up to 16, 16 bytes each), then
+// summed in ascending k in FP32.
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(const uint16_t* __restrict__ y16,
+                                                                     const uint8_t* __restrict__ yscale,
+                                                                     const float* __restrict__ w,
+                                                                     float* __restrict__ out, int H, int K) {
   const int t = blockIdx.x;
-  const int c = blockIdx.y * kCombineCols + threadIdx.x * 8;
+  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (c >= H) return;
   const size_t row0 = (size_t)t * K;
   const int nsb = H / kScaleCols;
@@ -730,8 +735,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
                           hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T, (H + kCombineCols - 1) / kCombineCols), dim3(256), 0, st, y16, yscale, w,
-                     out, H, K);
+  // a workgroup per token row from 512 tokens (0.321 -> 0.292 ms at T = 16384); below that,
+  // rows of 2048 columns, so that a decode batch still spreads over the CUs
+  const int threads = T >= 512 ? std::min(kCombineMaxThreads, (H / 8 + 63) / 64 * 64) : 256;
+  const int cols = threads * 8;
+  hipLaunchKernelGGL(combine_kernel, dim3(T, (H + cols - 1) / cols), dim3(threads), 0, st, y16, yscale, w, out, H, K);
   return hipGetLastError();
 }
 
