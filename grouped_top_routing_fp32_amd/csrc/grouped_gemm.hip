@@ -88,6 +88,9 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   // two stages of A, then two of B
   __shared__ __attribute__((aligned(16))) uint16_t ring[4 * kSlotHalfs];
   __shared__ float smax[16];
+  // down: destination slots of the tile's rows, read when the block starts so that the
+  // epilogue's stores need no dependent global loads
+  __shared__ int32_t srow[GATEUP ? 1 : kBM];
   uint16_t(*sA)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring);
   uint16_t(*sB)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring + 2 * kSlotHalfs);
 
@@ -136,6 +139,8 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   // reads those LDS rows (a computed fragment starts below the tile's end, so its
   // rows are in the range of a wave that copies).  The main loop waits for all
   // copies at every step, so waves may issue different numbers of copies.
+  if constexpr (!GATEUP)
+    for (int r = tid; r < tl.rows; r += kThreads) srow[r] = sorted_slots[tl.row_start + r];
   const bool copy_a = 32 * wave < tl.rows;
   auto issue_a = [&](int stage, int slot) {
     if (!copy_a) return;
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
       for (int r = 0; r < 4; ++r) {
         const int row = 64 * i + 16 * wm + (lane >> 4) * 4 + r;
         if (row < tl.rows) {
-          uint16_t* yrow = y16 + (size_t)sorted_slots[tl.row_start + row] * Ndim + n0 + wn * 128 + (lane & 15);
+          uint16_t* yrow = y16 + (size_t)srow[row] * Ndim + n0 + wn * 128 + (lane & 15);
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             yrow[16 * j] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[i][j][r], -(j < 4 ? sexp0 : sexp1)));
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     const int nsb = Ndim / kScaleCols;
     for (int q = tid; q < tl.rows * 4; q += kThreads) {
       const int row = q >> 2, b = q & 3;
-      oscale[(size_t)sorted_slots[tl.row_start + row] * nsb + n0 / kScaleCols + b] = (uint8_t)block_exp(b);
+      oscale[(size_t)srow[row] * nsb + n0 / kScaleCols + b] = (uint8_t)block_exp(b);
     }
   }
 }
