@@ -148,7 +148,7 @@ def forward_parity(p: Problem, bufs, tokens=None):
     y = orc.expert_outputs(X[keep], ids_o[keep], p.expert_f64)
     out_o = np.zeros((len(tokens), d.hidden))
     out_o[keep] = orc.combine(y, w_o[keep])
-    out_g = bufs.out.cpu().numpy().astype(np.float64)[tokens]
+    out_g = bufs.out[torch.as_tensor(tokens, device=bufs.out.device)].cpu().numpy().astype(np.float64)
     worst = compare_outputs(out_g, out_o, keep)
     return excluded, worst
 

@@ -294,6 +294,16 @@ def test_forward_beam_sizes(beam_experts, T):
     _beam_forward_wl(wl, beam_experts, sorted({0, T // 2, T - 1}))
 
 
+# The largest batch tried: 2,097,152 routed rows, so the expert outputs y [n, H] hold 1.07e10
+# elements and every offset past 2^31 must be formed in 64 bits; the last token's rows sit at
+# the highest offsets.  (About 70 GB of device memory with the experts.)
+def test_forward_beam_offsets_past_2_31(beam_experts):
+    T = 262144
+    _announce(f"forward Beam T={T}")
+    wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
+    _beam_forward_wl(wl, beam_experts, [0, 1, T // 2, T - 2, T - 1])
+
+
 # Degenerate and extreme shapes of the method through the whole block (all tokens).
 EDGE = {
     # one expert, one group, top-1: the block is 2.5 x a dense SwiGLU (stream path, then grouped
