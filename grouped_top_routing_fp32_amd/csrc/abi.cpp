@@ -382,9 +382,12 @@ extern "C" {
 
 size_t beam_moe_workspace_bytes(const beam_moe_dims* dims, int32_t T) {
   if (check_common(dims, T) != BEAM_MOE_OK) return SIZE_MAX;
-  Plan p;
+  // one size for every entry point: the larger of the bf16 and FP8 plans (they differ
+  // only if the two kernel families choose different expert paths)
+  Plan p, q;
   make_plan(dims, T, &p);
-  return p.total;
+  make_plan(dims, T, &q, true);
+  return p.total > q.total ? p.total : q.total;
 }
 
 const char* beam_moe_status_str(int status) {
