@@ -117,3 +117,17 @@ def test_trace_summary_cuts_and_classifies_calls(tmp_path):
     assert "`beam::router_logits_kernel<64>` | 1 | 4.1 |" in sections["decode, residual sublayer"]
     assert "`beam::combine_kernel` | 1 | 1.5 |" in sections["decode"]
     assert "fill_kernel" not in text
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The block runs on one GPU: --gpus N with N > 1 (or a multi-rank launch) exits with status 2
+    and says why, before anything touches a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2, r.stderr
+        assert "one GPU" in r.stderr
+        assert r.stdout == ""
