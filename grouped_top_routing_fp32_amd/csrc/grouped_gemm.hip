@@ -17,6 +17,12 @@
 // per SIMD) as 4 (rows) x 2 (columns); each wave owns 4 x 8 tiles of
 // v_mfma_f32_16x16x32 (128 accumulators): row fragments 64 i + 16 wm, so a
 // short tile drops whole levels i on every wave alike.
+// Gate/up: when an expert's last tile has at most 64 rows (one level), the
+// tile before it takes those rows as a fifth level (320 rows, 5 x 8 tiles per
+// wave) and the last tile's blocks exit: the per-step copies and barrier of a
+// one-level tile cost almost as much as a full one.  The activation scales are
+// then those of the merged tile; down keeps the tiles as cut, each inside one
+// gate/up tile, so its scale per stage is still uniform over its rows.
 //
 // Memory: a stage's operand tiles (2 x 32 KB) are copied global -> LDS by the
 // load unit (global_load_lds_dwordx4, no registers), each copy fetching 8 rows
@@ -52,6 +58,11 @@ constexpr int kBN = 256;        // B-rows per tile
 constexpr int kBK = 64;         // K per stage
 constexpr int kThreads = 512;
 constexpr int kSlotHalfs = kBM * kBK;  // 16384 elements = 32 KB per operand
+// Gate/up: a tile followed by its expert's last tile, when that has at most
+// kMergeRows rows, takes those rows too (kBM + kMergeRows rows, five levels):
+// one block instead of two per column block.  Down keeps the tiles as cut.
+constexpr int kMergeRows = 64;
+constexpr int kGateUpRingHalfs = 2 * (kBM + kMergeRows + kBN) * kBK;  // 144 KB: two stages of 320 + 256 rows
 static_assert(kBK == kScaleCols, "down reads one activation scale per stage");
 static_assert(kBN == 4 * kScaleCols, "the down output tile spans four scale blocks");
 
@@ -66,72 +77,53 @@ __device__ __forceinline__ int xcd_lin(int b, int total) {
 
 }  // namespace gg
 
-// GATEUP: act = x [T, H]; w0 = W_gate, w1 = W_up [E, I, H]; out = h fp16 [n, I]; hscale written.
-// !GATEUP: act = h fp16 [n, I]; w0 = W_down [E, H, I]; hscale read; out = y fp16 [n, H] (row slot),
-//          scaled by 2^-s with s per (tile, 64 columns) written to oscale [n, H / 64].
-// FP8: the weights are E4M3 codes (uint8) with one fp32 scale per output row (s0 for w0, s1 for
-//      w1, [E, Ndim]); every copy of them passes through registers, where the codes are decoded
-//      exactly (to bf16 for gate/up, to fp16 times the stage's 2^s for down), and the row scales
-//      multiply the accumulators before the epilogue.
-template <bool GATEUP, bool FP8>
-__global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_slots, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, const void* __restrict__ w0v, const void* __restrict__ w1v,
-    const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
-    uint8_t* __restrict__ hscale, uint8_t* __restrict__ oscale, int Kdim, int Ndim, int topk, int nbn,
-    int total_blocks) {
+// One block of a tile of at most 64 kLev rows (kLev row levels) against one
+// column block; ring holds two A stages of 64 kLev rows, then two B stages.
+template <bool GATEUP, bool FP8, int kLev>
+__device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t* srow, const Tile tl, int nblk,
+                                           const uint16_t* __restrict__ act,
+                                           const int32_t* __restrict__ sorted_slots, const void* __restrict__ w0v,
+                                           const void* __restrict__ w1v, const float* __restrict__ s0,
+                                           const float* __restrict__ s1, void* __restrict__ out,
+                                           uint8_t* __restrict__ hscale, uint8_t* __restrict__ oscale, int Kdim,
+                                           int Ndim, int topk) {
   using namespace gg;
   using WT = std::conditional_t<FP8, uint8_t, uint16_t>;  // weight element
   const WT* w0 = static_cast<const WT*>(w0v);
   const WT* w1 = static_cast<const WT*>(w1v);
   constexpr bool kRegB = FP8 || !GATEUP;  // weights through registers
-  // two stages of A, then two of B
-  __shared__ __attribute__((aligned(16))) uint16_t ring[4 * kSlotHalfs];
-  __shared__ float smax[16];
-  // down: destination slots of the tile's rows, read when the block starts so that the
-  // epilogue's stores need no dependent global loads
-  __shared__ int32_t srow[GATEUP ? 1 : kBM];
-  uint16_t(*sA)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring);
-  uint16_t(*sB)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring + 2 * kSlotHalfs);
-
-  // The grid is sized for the most tiles a batch can have; the order spans the
-  // tiles this batch has, so every XCD gets an equal share and the surplus
-  // blocks (the highest indices) exit here.  Linear order: tile group by tile
-  // group (an expert's tiles, at most kTileGroupMax), inside a group column
-  // block by column block, the group's tiles in snake order, so consecutive
-  // blocks share either the weight columns or (at each turn) the row tile.
-  const int real_blocks = min(total_blocks, ntiles[0] * nbn);
-  if ((int)blockIdx.x >= real_blocks) return;
-  const int lin = xcd_lin(blockIdx.x, real_blocks);
-  const Tile tg = tiles[lin / nbn];  // a tile of the block's group
-  const int r = lin - nbn * tg.group_first;
-  const int nblk = r / tg.group_size;
-  int j = r - nblk * tg.group_size;
-  if (nblk & 1) j = tg.group_size - 1 - j;
-  const Tile tl = tiles[tg.group_first + j];
+  constexpr int BM = 64 * kLev;           // rows per A stage
+  constexpr int kAPer = BM / 8;           // A rows copied per wave
+  uint16_t(*sA)[BM * kBK] = reinterpret_cast<uint16_t(*)[BM * kBK]>(ring);
+  uint16_t(*sB)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring + 2 * BM * kBK);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;  // row fragments 16*(4i + wm), i = 0..3
+  const int wm = wave >> 1;  // row fragments 64 i + 16 wm, i < kLev
   const int wn = wave & 1;   // column half
   const int BNc = GATEUP ? kBN / 2 : kBN;
   const int n0 = nblk * BNc;
 
   // ---- stage loads -----------------------------------------------------------
-  // Wave w fills rows [32w, 32w+32) of the A slot and of the B slot, 8 rows per
-  // 1 KB copy: lane i lands at byte 16 i, i.e. row + i/8, position i%8, and so
-  // fetches chunk (i%8) ^ swz(row).
-  const uint16_t* asrc[4];
+  // Wave w fills rows [kAPer w, kAPer (w + 1)) of the A slot and [32w, 32w+32) of
+  // the B slot, 8 rows per 1 KB copy: lane i lands at byte 16 i, i.e. row + i/8,
+  // position i%8, and so fetches chunk (i%8) ^ swz(row).
+  const uint16_t* asrc[kLev];
   const WT* bsrc[4];
   {
     const WT* wbase = (GATEUP && wave >= 4 ? w1 : w0) + (size_t)tl.expert * Ndim * Kdim;  // B rows 128..: up
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 32 * wave + 8 * q + (lane >> 3);
+    for (int q = 0; q < kLev; ++q) {
+      const int r = kAPer * wave + 8 * q + (lane >> 3);
       const int c = (lane & 7) ^ swz(r);
       const int rr = min(r, tl.rows - 1);  // rows past the tile's end repeat its last row; never stored
       const size_t arow = GATEUP ? (size_t)(sorted_slots[tl.row_start + rr] / topk) : (size_t)(tl.row_start + rr);
       asrc[q] = act + arow * Kdim + c * 8;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 32 * wave + 8 * q + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
       bsrc[q] = wbase + (size_t)(n0 + (GATEUP ? (r & 127) : r)) * Kdim + c * 8;
     }
   }
@@ -141,12 +133,12 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   // copies at every step, so waves may issue different numbers of copies.
   if constexpr (!GATEUP)
     for (int r = tid; r < tl.rows; r += kThreads) srow[r] = sorted_slots[tl.row_start + r];
-  const bool copy_a = 32 * wave < tl.rows;
+  const bool copy_a = kAPer * wave < tl.rows;
   auto issue_a = [&](int stage, int slot) {
     if (!copy_a) return;
     const int k = stage * kBK;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lds_copy16(asrc[q] + k, lds_addr(&sA[slot][(32 * wave + 8 * q) * kBK]));
+    for (int q = 0; q < kLev; ++q) lds_copy16(asrc[q] + k, lds_addr(&sA[slot][(kAPer * wave + 8 * q) * kBK]));
   };
   auto issue_b = [&](int stage, int slot) {
     const int k = stage * kBK;
@@ -204,11 +196,11 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   const int brow = (GATEUP ? wn * 64 : wn * 128) + l16;
   const int boff0 = brow * kBK + ((fc ^ sw) << 3);
   const int boff1 = brow * kBK + (((4 + fc) ^ sw) << 3);
-  const int nlev = min(4, (tl.rows - 16 * wm + 63) / 64);  // >= 0: levels with rows for this wave
+  const int nlev = min(kLev, (tl.rows - 16 * wm + 63) / 64);  // >= 0: levels with rows for this wave
 
-  f32x4 acc[4][8];
+  f32x4 acc[kLev][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kLev; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -217,7 +209,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     const uint16_t* B = sB[slot];
     const int ao = sub ? aoff1 : aoff0;
     const int bo = sub ? boff1 : boff0;
-    u32x4 fa[4], fb[8];
+    u32x4 fa[kLev], fb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // gate/up: j < 4 gate rows, j >= 4 the matching up rows (128 B-rows further)
@@ -226,7 +218,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
       fb[j] = *reinterpret_cast<const u32x4*>(&B[bo + jj * 16 * kBK + extra]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kLev; ++i) {
       if (decltype(full)::value || i < nlev) {
         fa[i] = *reinterpret_cast<const u32x4*>(&A[ao + i * 64 * kBK]);
 #pragma unroll
@@ -294,7 +286,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
         else
           issue_b(st + 1, slot ^ 1);
       }
-      if constexpr (GATEUP && !FP8) {
+      if constexpr (GATEUP && !FP8 && kLev == 4) {
         math2(slot, full);
       } else {
         math(slot, 0, full);
@@ -304,7 +296,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     }
   };
   // full tiles (the common case) run without the per-level tests
-  if (tl.rows >= kBM)
+  if (tl.rows >= BM)
     main_loop(std::true_type{});
   else
     main_loop(std::false_type{});
@@ -320,14 +312,14 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     for (int j = 0; j < 8; ++j)
       rs[j] = GATEUP ? (j < 4 ? s0 : s1)[sb + wn * 64 + 16 * (j & 3)] : s0[sb + wn * 128 + 16 * j];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kLev; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] *= rs[j];
   }
   if (GATEUP) {
     float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kLev; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = 64 * i + 16 * wm + (lane >> 4) * 4 + r < tl.rows;
@@ -351,7 +343,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
       for (int b = 0; b < 128 / kScaleCols; ++b)
         hscale[(size_t)(tl.row_start + r) * nsb + n0 / kScaleCols + b] = (uint8_t)sexp;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kLev; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 64 * i + 16 * wm + (lane >> 4) * 4 + r;
@@ -369,7 +361,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     // (Staging the tile in LDS to store whole rows measured slower.)
     float mx[2] = {0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kLev; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = 64 * i + 16 * wm + (lane >> 4) * 4 + r < tl.rows;
@@ -393,7 +385,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     const int sexp0 = block_exp(2 * wn), sexp1 = block_exp(2 * wn + 1);
     uint16_t* y16 = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kLev; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 64 * i + 16 * wm + (lane >> 4) * 4 + r;
@@ -410,6 +402,62 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
       oscale[(size_t)srow[row] * nsb + n0 / kScaleCols + b] = (uint8_t)block_exp(b);
     }
   }
+}
+
+// GATEUP: act = x [T, H]; w0 = W_gate, w1 = W_up [E, I, H]; out = h fp16 [n, I]; hscale written.
+// !GATEUP: act = h fp16 [n, I]; w0 = W_down [E, H, I]; hscale read; out = y fp16 [n, H] (row slot),
+//          scaled by 2^-s with s per (tile, 64 columns) written to oscale [n, H / 64].
+// FP8: the weights are E4M3 codes (uint8) with one fp32 scale per output row (s0 for w0, s1 for
+//      w1, [E, Ndim]); every copy of them passes through registers, where the codes are decoded
+//      exactly (to bf16 for gate/up, to fp16 times the stage's 2^s for down), and the row scales
+//      multiply the accumulators before the epilogue.
+template <bool GATEUP, bool FP8>
+__global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_slots, const Tile* __restrict__ tiles,
+    const int32_t* __restrict__ ntiles, const void* __restrict__ w0v, const void* __restrict__ w1v,
+    const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
+    uint8_t* __restrict__ hscale, uint8_t* __restrict__ oscale, int Kdim, int Ndim, int topk, int nbn,
+    int total_blocks) {
+  using namespace gg;
+  // two stages of A, then two of B
+  __shared__ __attribute__((aligned(16))) uint16_t ring[GATEUP ? kGateUpRingHalfs : 4 * kSlotHalfs];
+  __shared__ float smax[16];
+  // down: destination slots of the tile's rows, read when the block starts so that the
+  // epilogue's stores need no dependent global loads
+  __shared__ int32_t srow[GATEUP ? 1 : kBM];
+
+  // The grid is sized for the most tiles a batch can have; the order spans the
+  // tiles this batch has, so every XCD gets an equal share and the surplus
+  // blocks (the highest indices) exit here.  Linear order: tile group by tile
+  // group (an expert's tiles, at most kTileGroupMax), inside a group column
+  // block by column block, the group's tiles in snake order, so consecutive
+  // blocks share either the weight columns or (at each turn) the row tile.
+  const int nt = ntiles[0];
+  const int real_blocks = min(total_blocks, nt * nbn);
+  if ((int)blockIdx.x >= real_blocks) return;
+  const int lin = xcd_lin(blockIdx.x, real_blocks);
+  const Tile tg = tiles[lin / nbn];  // a tile of the block's group
+  const int r = lin - nbn * tg.group_first;
+  const int nblk = r / tg.group_size;
+  int j = r - nblk * tg.group_size;
+  if (nblk & 1) j = tg.group_size - 1 - j;
+  const int idx = tg.group_first + j;
+  Tile tl = tiles[idx];
+  if constexpr (GATEUP) {
+    // Only an expert's last tile can be short, and the tile before it has kBM
+    // rows, so a merged tile has at most kBM + kMergeRows rows.
+    const Tile prev = tiles[max(idx - 1, 0)];
+    const Tile next = tiles[min(idx + 1, nt - 1)];
+    if (idx > 0 && prev.expert == tl.expert && tl.rows <= kMergeRows) return;  // merged into the tile before
+    if (idx + 1 < nt && next.expert == tl.expert && next.rows <= kMergeRows) {
+      tl.rows += next.rows;
+      gemm_block<GATEUP, FP8, (kBM + kMergeRows) / 64>(ring, smax, srow, tl, nblk, act, sorted_slots, w0v, w1v, s0,
+                                                       s1, out, hscale, oscale, Kdim, Ndim, topk);
+      return;
+    }
+  }
+  gemm_block<GATEUP, FP8, kBM / 64>(ring, smax, srow, tl, nblk, act, sorted_slots, w0v, w1v, s0, s1, out, hscale,
+                                    oscale, Kdim, Ndim, topk);
 }
 
 int grouped_gemm_rows() { return gg::kBM; }
