@@ -17,12 +17,11 @@
 // per SIMD) as 4 (rows) x 2 (columns); each wave owns 4 x 8 tiles of
 // v_mfma_f32_16x16x32 (128 accumulators): row fragments 64 i + 16 wm, so a
 // short tile drops whole levels i on every wave alike.
-// Gate/up: when an expert's last tile has at most 64 rows (one level), the
-// tile before it takes those rows as a fifth level (320 rows, 5 x 8 tiles per
-// wave) and the last tile's blocks exit: the per-step copies and barrier of a
-// one-level tile cost almost as much as a full one.  The activation scales are
-// then those of the merged tile; down keeps the tiles as cut, each inside one
-// gate/up tile, so its scale per stage is still uniform over its rows.
+// When an expert's last tile has at most 64 rows (one level), the tile before
+// it takes those rows as a fifth level (320 rows, 5 x 8 tiles per wave) and the
+// last tile's blocks exit: the per-step copies and barrier of a one-level tile
+// cost almost as much as a full one.  Both projections merge the same tiles, so
+// a down tile is a gate/up tile and its per-stage activation scale is uniform.
 //
 // Memory: a stage's operand tiles (2 x 32 KB) are copied global -> LDS by the
 // load unit (global_load_lds_dwordx4, no registers), each copy fetching 8 rows
@@ -58,11 +57,11 @@ constexpr int kBN = 256;        // B-rows per tile
 constexpr int kBK = 64;         // K per stage
 constexpr int kThreads = 512;
 constexpr int kSlotHalfs = kBM * kBK;  // 16384 elements = 32 KB per operand
-// Gate/up: a tile followed by its expert's last tile, when that has at most
-// kMergeRows rows, takes those rows too (kBM + kMergeRows rows, five levels):
-// one block instead of two per column block.  Down keeps the tiles as cut.
+// A tile followed by its expert's last tile, when that has at most kMergeRows
+// rows, takes those rows too (kBM + kMergeRows rows, five levels): one block
+// instead of two per column block.
 constexpr int kMergeRows = 64;
-constexpr int kGateUpRingHalfs = 2 * (kBM + kMergeRows + kBN) * kBK;  // 144 KB: two stages of 320 + 256 rows
+constexpr int kRingHalfs = 2 * (kBM + kMergeRows + kBN) * kBK;  // 144 KB: two stages of 320 + 256 rows
 static_assert(kBK == kScaleCols, "down reads one activation scale per stage");
 static_assert(kBN == 4 * kScaleCols, "the down output tile spans four scale blocks");
 
@@ -420,11 +419,11 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     int total_blocks) {
   using namespace gg;
   // two stages of A, then two of B
-  __shared__ __attribute__((aligned(16))) uint16_t ring[GATEUP ? kGateUpRingHalfs : 4 * kSlotHalfs];
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kRingHalfs];
   __shared__ float smax[16];
   // down: destination slots of the tile's rows, read when the block starts so that the
   // epilogue's stores need no dependent global loads
-  __shared__ int32_t srow[GATEUP ? 1 : kBM];
+  __shared__ int32_t srow[GATEUP ? 1 : kBM + kMergeRows];
 
   // The grid is sized for the most tiles a batch can have; the order spans the
   // tiles this batch has, so every XCD gets an equal share and the surplus
@@ -443,7 +442,7 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   if (nblk & 1) j = tg.group_size - 1 - j;
   const int idx = tg.group_first + j;
   Tile tl = tiles[idx];
-  if constexpr (GATEUP) {
+  {
     // Only an expert's last tile can be short, and the tile before it has kBM
     // rows, so a merged tile has at most kBM + kMergeRows rows.
     const Tile prev = tiles[max(idx - 1, 0)];
