@@ -310,6 +310,13 @@ EDGE = {
     # with three tiles of 256, 256 and 88 rows)
     "dense_stream": synth.Workload("dense_stream", 3, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06),
     "dense_grouped": synth.Workload("dense_grouped", 600, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06),
+    # a last tile of at most 64 rows joins the tile before it (256 + 48 = 304 rows, five levels) in
+    # both projections; large weights, so h and y carry non-zero power-of-two scales
+    "dense_merged_big": synth.Workload("dense_merged_big", 560, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06,
+                                       expert_sigma=10.0),
+    # about 300 rows per expert: some experts' tails are merged (<= 64 rows), others are not
+    "merged_tails_big": synth.Workload("merged_tails_big", 1200, synth.Dims(512, 256, 8, 2, 1, 2), router_sigma=0.06,
+                                       expert_sigma=10.0),
     # the largest top-k, on both paths
     "topk16_stream": synth.Workload("topk16_stream", 16, synth.Dims(256, 128, 64, 8, 8, 16), router_sigma=0.06),
     "topk16_grouped": synth.Workload("topk16_grouped", 200, synth.Dims(256, 128, 64, 8, 8, 16), router_sigma=0.06),
@@ -513,6 +520,11 @@ FP8 = {
                                       zipf_s=1.2),
     "f8_grouped_big": synth.Workload("f8_grouped_big", 900, synth.Dims(512, 512, 16, 4, 2, 4), router_sigma=0.06,
                                      expert_sigma=10.0),
+    # merged tails (a last tile of at most 64 rows joins the tile before it) with large activations
+    "f8_dense_merged_big": synth.Workload("f8_dense_merged_big", 560, synth.Dims(256, 256, 1, 1, 1, 1),
+                                          router_sigma=0.06, expert_sigma=10.0),
+    "f8_merged_tails_big": synth.Workload("f8_merged_tails_big", 1200, synth.Dims(512, 256, 8, 2, 1, 2),
+                                          router_sigma=0.06, expert_sigma=10.0),
 }
 
 
