@@ -393,6 +393,20 @@ def time_residual(r, steps, warmup):
             "extra_algorithmic_bytes": extra_bytes, "step": 2, "norm": "RMSNorm, eps 1e-6, unit weights"}
 
 
+# The arithmetic types of the path (include/beam_moe.h states the same).
+DTYPE_BF16 = "mixed bf16/fp16/fp32"
+DTYPE_FP8 = "mixed e4m3 weights, bf16/fp16/fp32"
+PRECISION = {
+    "weights": "bf16 (fp8 records: E4M3 codes with an fp32 scale per output row)",
+    "router": "fp32 (bf16 x times fp32 W_r, FP32 accumulation); selection and weights fp32",
+    "gate_up": "bf16 MFMA, fp32 accumulation, SwiGLU in fp32",
+    "h": "fp16 times 2^-s per 64 columns of a row group",
+    "down": "fp16 MFMA on W_down converted exactly to fp16, fp32 accumulation",
+    "y": "fp16 times 2^-s per 64 columns of a row group",
+    "combine_out": "fp32",
+}
+
+
 def accounting(r):
     """Algorithmic bytes and FLOPs of each kernel of one step (no cache effects, no re-reads)."""
     wl = r["wl"]
@@ -446,9 +460,19 @@ def layer_summary(r):
             "experts_touched": r["n_touched"], "max_rows_per_expert": r["max_count"]}
 
 
-def cpu_baseline(r, target_s):
-    """The FP64 oracle on the host cores, on the first tokens of the same batch."""
+_HOST_EXPERTS = {}   # host copies of expert weights, shared by the baselines of one run
+
+
+def cpu_baseline(r, target_s, seed=0):
+    """The FP64 oracle on the host cores, on a seeded random subset of the same batch.
+
+    The oracle runs the whole block (router, selection, dispatch, experts, combine) on
+    n tokens, n sized from an untimed one-token pilot so that the run takes about
+    target_s.  Expert weights are copied to the host before the timed region; inside
+    it the oracle reads them as it always does (bf16 values widened to FP64, or E4M3
+    codes decoded and scaled by their row scales)."""
     import numpy as np
+    import torch
     from oracle import beam_moe_oracle as orc
     try:
         import threadpoolctl
@@ -459,32 +483,42 @@ def cpu_baseline(r, target_s):
         blas_threads, blas = os.cpu_count(), "?"
     wl = r["wl"]
     d = wl.dims
+    fp8 = r.get("fp8")
     X_all = r["x"].float().cpu().numpy()
     W_r = r["wr"].cpu().numpy()
     bias = None if r["bias"] is None else r["bias"].cpu().numpy()
-    wg, wu, wd = r["experts"]
-    host = {}
+    src = r["experts_fp8"] if fp8 else r["experts"]
+    e4m3 = orc.e4m3_decode(np.arange(256)) if fp8 else None
 
     def fetch(ids):
         for e in np.unique(ids):
-            e = int(e)
-            if e not in host:
-                host[e] = (wg[e].float().cpu().numpy(), wu[e].float().cpu().numpy(), wd[e].float().cpu().numpy())
+            key = (bool(fp8), int(e))
+            if key not in _HOST_EXPERTS:
+                _HOST_EXPERTS[key] = tuple(t[int(e)].cpu() for t in src)
 
-    # untimed calibration on one token: how many tokens fit the target time
-    ids1, *_ = orc.route(X_all[:1], W_r, bias, d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
-    fetch(ids1)
-    t0 = time.perf_counter()
-    orc.moe_forward(X_all[:1], W_r, bias, lambda e: host[e], d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
-    per_token = time.perf_counter() - t0
+    def weights(e):
+        h = _HOST_EXPERTS[(bool(fp8), int(e))]
+        if fp8:
+            # W = decode(q) * row scale: the oracle's value of each of the 256 codes, looked up
+            return tuple(e4m3[q.numpy()] * sc.numpy().astype(np.float64)[:, None]
+                         for q, sc in ((h[0], h[1]), (h[2], h[3]), (h[4], h[5])))
+        return tuple(t.float().numpy() for t in h)
+
+    def run(tok):
+        ids, *_ = orc.route(X_all[tok], W_r, bias, d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
+        fetch(ids)
+        t0 = time.perf_counter()
+        orc.moe_forward(X_all[tok], W_r, bias, weights, d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
+        return time.perf_counter() - t0
+
+    rng = np.random.default_rng(seed)
+    per_token = run(rng.choice(wl.tokens, 1, replace=False))     # untimed pilot
     n = int(max(1, min(wl.tokens, target_s / max(per_token, 1e-3))))
-    ids_n, *_ = orc.route(X_all[:n], W_r, bias, d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
-    fetch(ids_n)
-    t0 = time.perf_counter()
-    orc.moe_forward(X_all[:n], W_r, bias, lambda e: host[e], d.num_groups, d.topk_groups, d.topk, d.routed_scaling)
-    el = time.perf_counter() - t0
+    tok = np.sort(rng.choice(wl.tokens, n, replace=False))
+    el = run(tok)
     return {"value": round(n / el, 3), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"first {n} of the {wl.tokens} tokens of the {wl.name} batch, whole block in FP64 "
+            "sample": f"{n} of the {wl.tokens} tokens of the {wl.name} batch (seeded random subset, seed {seed})"
+                      f"{' with FP8 expert weights' if fp8 else ''}, whole block in FP64 "
                       f"(numpy, BLAS={blas}); {el:.1f} s",
             "host_cpus": len(os.sched_getaffinity(0))}
 
@@ -689,6 +723,7 @@ def main():
         print(f"[bench] timing {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
         r = time_workload(name, experts, args.steps, args.warmup, experts_fp8)
         r["experts"] = experts
+        r["experts_fp8"] = experts_fp8
         r["fp8"] = name.endswith("_fp8")
         results[name] = r
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step; stages {r['stage_ms']}", file=sys.stderr, flush=True)
@@ -696,6 +731,8 @@ def main():
             r["residual"] = time_residual(r, args.steps, args.warmup)
             print(f"[bench] {name} as a residual sublayer: {r['residual']['ms_per_step']:.4f} ms/step",
                   file=sys.stderr, flush=True)
+
+    head = names[0]
 
     def record(name):
         r = results[name]
@@ -710,16 +747,20 @@ def main():
         out = {"value": round(wl.tokens / (r["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
                "ms_per_step": round(r["ms_per_step"], 4), "config": cfg, "roofline": roofline(r, bound, name)}
         out.update(layer_summary(r))
+        out["dtype"] = DTYPE_FP8 if r["fp8"] else DTYPE_BF16
         if "residual" in r:
             out["residual_sublayer"] = r["residual"]
+        if not args.no_cpu_baseline and name != head:
+            print(f"[bench] cpu baseline (oracle) on {name}", file=sys.stderr, flush=True)
+            out["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds / 2)
         return out
 
-    head = names[0]
     line = {"metric": METRIC}
     main_rec = record(head)
     line.update({"value": main_rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
                  "warmup": args.warmup, "ms_per_step": main_rec["ms_per_step"], "higher_is_better": True,
-                 "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                 "scaling": "weak", "vs_baseline": None, "dtype": main_rec["dtype"], "precision": PRECISION,
+                 "data": "synthetic",
                  "config": main_rec["config"], "roofline": main_rec["roofline"]})
     for k in ("layer_hbm_gbs", "layer_hbm_frac", "layer_expert_tflops", "layer_mfma_frac", "stage_ms",
               "experts_touched", "max_rows_per_expert", "residual_sublayer"):

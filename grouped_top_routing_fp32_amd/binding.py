@@ -24,7 +24,8 @@ BEAM_MOE_ERR_UNSUPPORTED = -2
 BEAM_MOE_ERR_WORKSPACE = -3
 BEAM_MOE_ERR_HIP = -4
 
-EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_select", "beam_moe_dispatch",
+EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route_workspace_bytes", "beam_moe_dispatch_workspace_bytes",
+            "beam_moe_route", "beam_moe_select", "beam_moe_dispatch",
             "beam_moe_forward", "beam_moe_forward_fp8", "beam_moe_residual_forward",
             "beam_moe_residual_forward_fp8", "beam_moe_timing_enable", "beam_moe_timing_read", "beam_moe_stage_name",
             "beam_moe_status_str")
@@ -57,8 +58,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pd = ctypes.POINTER(CDims)
-    lib.beam_moe_workspace_bytes.argtypes = [pd, i32]
-    lib.beam_moe_workspace_bytes.restype = sz
+    for fn in ("beam_moe_workspace_bytes", "beam_moe_route_workspace_bytes", "beam_moe_dispatch_workspace_bytes"):
+        getattr(lib, fn).argtypes = [pd, i32]
+        getattr(lib, fn).restype = sz
     lib.beam_moe_status_str.argtypes = [ctypes.c_int]
     lib.beam_moe_status_str.restype = ctypes.c_char_p
     lib.beam_moe_route.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -128,21 +130,34 @@ def _req(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
 # --------------------------------------------------------------------------
 # raw entry points (same names as the C ABI)
 # --------------------------------------------------------------------------
-def beam_moe_workspace_bytes(dims: Dims, T: int) -> int:
+def _ws_query(fn: str, dims: Dims, T: int) -> int:
     cd = _cdims(dims)
-    n = load_library().beam_moe_workspace_bytes(ctypes.byref(cd), int(T))
+    n = getattr(load_library(), fn)(ctypes.byref(cd), int(T))
     if n == SIZE_MAX:
-        raise BeamMoeError(BEAM_MOE_ERR_UNSUPPORTED, "beam_moe_workspace_bytes")
+        raise BeamMoeError(BEAM_MOE_ERR_UNSUPPORTED, fn)
     return int(n)
+
+
+def beam_moe_workspace_bytes(dims: Dims, T: int) -> int:
+    return _ws_query("beam_moe_workspace_bytes", dims, T)
+
+
+def beam_moe_route_workspace_bytes(dims: Dims, T: int) -> int:
+    return _ws_query("beam_moe_route_workspace_bytes", dims, T)
+
+
+def beam_moe_dispatch_workspace_bytes(dims: Dims, T: int) -> int:
+    return _ws_query("beam_moe_dispatch_workspace_bytes", dims, T)
 
 
 def beam_moe_status_str(status: int) -> str:
     return status_text(status)
 
 
-def workspace(dims: Dims, T: int, device="cuda") -> torch.Tensor:
-    """A uint8 device buffer of beam_moe_workspace_bytes(dims, T) bytes."""
-    return torch.empty(max(1, beam_moe_workspace_bytes(dims, T)), dtype=torch.uint8, device=device)
+def workspace(dims: Dims, T: int, device="cuda", size_fn=None) -> torch.Tensor:
+    """A uint8 device buffer of size_fn(dims, T) bytes (default beam_moe_workspace_bytes)."""
+    n = (size_fn or beam_moe_workspace_bytes)(dims, T)
+    return torch.empty(max(16, n), dtype=torch.uint8, device=device)
 
 
 def beam_moe_route(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor] = None,
@@ -162,7 +177,7 @@ def beam_moe_route(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_bi
     w = torch.empty((T, K), dtype=torch.float32, device=dev)
     scores = torch.empty((T, E), dtype=torch.float32, device=dev) if want_scores else None
     if ws is None:
-        ws = workspace(dims, T, dev)
+        ws = workspace(dims, T, dev, beam_moe_route_workspace_bytes)
     cd = _cdims(dims)
     st = load_library().beam_moe_route(ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias),
                                        _ptr(select_bias), _ptr(ids), _ptr(w), _ptr(scores), _ptr(ws), ws.numel(),
@@ -196,7 +211,7 @@ def beam_moe_dispatch(dims: Dims, topk_ids: torch.Tensor, *, ws: Optional[torch.
     offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     slots = torch.empty((T * dims.topk,), dtype=torch.int32, device=dev)
     if ws is None:
-        ws = workspace(dims, T, dev)
+        ws = workspace(dims, T, dev, beam_moe_dispatch_workspace_bytes)
     cd = _cdims(dims)
     st = load_library().beam_moe_dispatch(ctypes.byref(cd), T, _ptr(topk_ids), _ptr(counts), _ptr(offsets),
                                           _ptr(slots), _ptr(ws), ws.numel(), _stream(stream))

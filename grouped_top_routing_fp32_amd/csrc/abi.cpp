@@ -3,7 +3,7 @@
 // stated in include/beam_moe.h.
 #include "../../include/beam_moe.h"
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <array>
 #include <cmath>
@@ -167,6 +167,11 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p, bool fp8 = false) {
   p->total = off;
 }
 
+// Scratch of the standalone route (split-K partial logits) and dispatch (unit
+// histograms) calls; the forward plan holds both inside its own layout.
+size_t route_ws_bytes(const Plan& p) { return (size_t)p.splits * p.T * p.E * sizeof(float); }
+size_t dispatch_ws_bytes(const Plan& p) { return (size_t)p.units * p.E * sizeof(int32_t); }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <typename Tp>
@@ -288,7 +293,7 @@ BlockArgs fp8_block(const void* x, const float* w_router, const float* logit_bia
 // stream, then `combine(y16, yscale)` (the final step of the entry point).
 template <typename PreFn, typename CombineFn>
 int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* ws, hipStream_t st, PreFn pre,
-              CombineFn combine) {
+              CombineFn combine, bool timed = true) {
   const int T = p.T;
   float* part = at<float>(ws, p.off_part);
   beam::Tile* tiles = at<beam::Tile>(ws, p.off_tiles);
@@ -297,7 +302,7 @@ int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* w
   uint8_t* hscale = at<uint8_t>(ws, p.off_hscale);
   uint16_t* y16 = at<uint16_t>(ws, p.off_y);
   uint8_t* yscale = at<uint8_t>(ws, p.off_yscale);
-  hipEvent_t* ev = timing_slot();
+  hipEvent_t* ev = timed ? timing_slot() : nullptr;
   int rc = BEAM_MOE_OK;
 #define BEAM_TRY(expr)                                     \
   do {                                                     \
@@ -376,6 +381,37 @@ int residual_block(const beam_moe_dims* d, int32_t T, const float* stream_in, in
       });
 }
 
+// Checks of beam_moe_forward's arguments (everything but
+// the workspace); fills the plan.
+int check_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                  const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
+                  const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                  int32_t* expert_offsets, int32_t* sorted_slots, Plan* p) {
+  int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK || T == 0) return rc;
+  if ((rc = check_ptrs({x_bf16, w_router, w_gate, w_up, w_down, out, topk_ids, topk_w, expert_counts,
+                        expert_offsets, sorted_slots})) != BEAM_MOE_OK)
+    return rc;
+  if ((logit_bias && !aligned16(logit_bias)) || (select_bias && !aligned16(select_bias)))
+    return BEAM_MOE_ERR_INVALID_ARG;
+  make_plan(d, T, p);
+  return BEAM_MOE_OK;
+}
+
+int forward_bf16(const beam_moe_dims* d, const Plan& p, const void* x_bf16, const float* w_router,
+                 const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
+                 const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* sorted_slots, void* ws, hipStream_t st, bool timed) {
+  BlockArgs a = bf16_block(x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, topk_ids, topk_w,
+                           expert_counts, expert_offsets, sorted_slots);
+  return run_block(
+      d, p, a, ws, st, [] { return hipSuccess; },
+      [&](const uint16_t* y16, const uint8_t* yscale) {
+        return beam::launch_combine(y16, yscale, topk_w, out, p.T, p.H, p.K, st);
+      },
+      timed);
+}
+
 }  // namespace
 
 extern "C" {
@@ -401,6 +437,23 @@ const char* beam_moe_status_str(int status) {
   }
 }
 
+size_t beam_moe_route_workspace_bytes(const beam_moe_dims* dims, int32_t T) {
+  if (check_common(dims, T) != BEAM_MOE_OK) return SIZE_MAX;
+  Plan p;
+  make_plan(dims, T, &p);
+  return route_ws_bytes(p);
+}
+
+size_t beam_moe_dispatch_workspace_bytes(const beam_moe_dims* dims, int32_t T) {
+  if (check_common(dims, T) != BEAM_MOE_OK) return SIZE_MAX;
+  Plan p;
+  make_plan(dims, T, &p);
+  return dispatch_ws_bytes(p);
+}
+
+// Standalone route and dispatch carve their scratch from the start of the
+// caller's workspace (the forward entry points place the same buffers inside
+// their larger plan).
 int beam_moe_route(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
                    const float* logit_bias, const float* select_bias, int32_t* topk_ids, float* topk_w,
                    float* scores_out, void* ws, size_t ws_bytes, void* stream) {
@@ -412,9 +465,9 @@ int beam_moe_route(const beam_moe_dims* d, int32_t T, const void* x_bf16, const 
     return BEAM_MOE_ERR_INVALID_ARG;
   Plan p;
   make_plan(d, T, &p);
-  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  if (!ws || !aligned16(ws) || ws_bytes < route_ws_bytes(p)) return BEAM_MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* part = at<float>(ws, p.off_part);
+  float* part = static_cast<float*>(ws);
   rc = hip_status(beam::launch_router_logits(static_cast<const uint16_t*>(x_bf16), w_router, part, T, p.H, p.E,
                                              p.splits, p.k_per_split, st));
   if (rc != BEAM_MOE_OK) return rc;
@@ -441,8 +494,8 @@ int beam_moe_dispatch(const beam_moe_dims* d, int32_t T, const int32_t* topk_ids
   if ((rc = check_ptrs({topk_ids, expert_counts, expert_offsets, sorted_slots})) != BEAM_MOE_OK) return rc;
   Plan p;
   make_plan(d, T, &p);
-  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
-  return hip_status(beam::launch_dispatch(topk_ids, p.n, p.E, at<int32_t>(ws, p.off_hist), expert_counts,
+  if (!ws || !aligned16(ws) || ws_bytes < dispatch_ws_bytes(p)) return BEAM_MOE_ERR_WORKSPACE;
+  return hip_status(beam::launch_dispatch(topk_ids, p.n, p.E, static_cast<int32_t*>(ws), expert_counts,
                                           expert_offsets, sorted_slots, nullptr, 0, nullptr,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -451,24 +504,13 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
                      const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
                      const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
                      int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_common(d, T);
-  if (rc != BEAM_MOE_OK || T == 0) return rc;
-  if ((rc = check_ptrs({x_bf16, w_router, w_gate, w_up, w_down, out, topk_ids, topk_w, expert_counts,
-                        expert_offsets, sorted_slots})) != BEAM_MOE_OK)
-    return rc;
-  if ((logit_bias && !aligned16(logit_bias)) || (select_bias && !aligned16(select_bias)))
-    return BEAM_MOE_ERR_INVALID_ARG;
   Plan p;
-  make_plan(d, T, &p);
+  int rc = check_forward(d, T, x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, out, topk_ids,
+                         topk_w, expert_counts, expert_offsets, sorted_slots, &p);
+  if (rc != BEAM_MOE_OK || T == 0) return rc;
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
-  BlockArgs a = bf16_block(x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, topk_ids, topk_w,
-                           expert_counts, expert_offsets, sorted_slots);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return run_block(
-      d, p, a, ws, st, [] { return hipSuccess; },
-      [&](const uint16_t* y16, const uint8_t* yscale) {
-        return beam::launch_combine(y16, yscale, topk_w, out, T, p.H, p.K, st);
-      });
+  return forward_bf16(d, p, x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, out, topk_ids, topk_w,
+                      expert_counts, expert_offsets, sorted_slots, ws, static_cast<hipStream_t>(stream), true);
 }
 
 int beam_moe_forward_fp8(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,

@@ -39,7 +39,8 @@
  *   num_experts % num_groups == 0, 1 <= topk_groups <= num_groups,
  *   1 <= topk <= min(16, topk_groups * num_experts / num_groups),
  *   hidden % 256 == 0, intermediate % 128 == 0, routed_scaling finite.
- *   0 <= T and T * topk < 2^31; T == 0 is a valid no-op.
+ *   0 <= T and T * topk <= 2^28 (268,435,456 routed pairs); T == 0 is a valid
+ *   no-op. Larger batches return BEAM_MOE_ERR_UNSUPPORTED.
  * - Determinism: no floating-point atomics are used; every output, integer
  *   or floating point, is bitwise identical from run to run on one device.
  * - Ties in scores are broken towards the lower group / expert index; the K
@@ -73,13 +74,24 @@ enum {
   BEAM_MOE_ERR_HIP = -4          /* a HIP launch failed                          */
 };
 
-/* Bytes of workspace that beam_moe_route, beam_moe_dispatch and the forward
- * entry points need for T tokens (one size serves all of them; it grows
- * linearly in T: at Beam dims about 132 KB per token, mostly the fp16 SwiGLU
- * activations [T*K, I] and the fp16 expert outputs [T*K, H], each with a
- * power-of-two scale per 64 columns).
- * Returns SIZE_MAX for invalid or unsupported dims. */
+/* Bytes of workspace that the forward entry points need for T tokens (one size
+ * serves all of them, and it is also enough for beam_moe_route and
+ * beam_moe_dispatch; it grows linearly in T: at Beam dims about 132 KB per
+ * token, mostly the fp16 SwiGLU activations [T*K, I] and the fp16 expert
+ * outputs [T*K, H], each with a power-of-two scale per 64 columns).
+ * Returns SIZE_MAX for invalid or unsupported dims or T. */
 size_t beam_moe_workspace_bytes(const beam_moe_dims* dims, int32_t T);
+
+/* The smaller workspace that beam_moe_route alone needs: its split-K partial
+ * logits, fp32 [splits, T, E] with splits <= 16 (T * E * 4 bytes from about
+ * 4096 tokens at Beam dims, where every token tile gets its own workgroup).
+ * Returns SIZE_MAX for invalid or unsupported dims or T. */
+size_t beam_moe_route_workspace_bytes(const beam_moe_dims* dims, int32_t T);
+
+/* The smaller workspace that beam_moe_dispatch alone needs: int32 expert
+ * histograms of each unit of 1024 pairs, ceil(T * K / 1024) * E * 4 bytes.
+ * Returns SIZE_MAX for invalid or unsupported dims or T. */
+size_t beam_moe_dispatch_workspace_bytes(const beam_moe_dims* dims, int32_t T);
 
 /* Router + group-limited top-k (steps 1-3 above).
  *   x_bf16      [T, H]  bf16 hidden states
@@ -93,7 +105,8 @@ size_t beam_moe_workspace_bytes(const beam_moe_dims* dims, int32_t T);
  *   topk_ids    [T, K]  int32 out
  *   topk_w      [T, K]  fp32 out: normalised weights times routed_scaling
  *   scores_out  [T, E]  fp32 out, post-sigmoid scores; NULL = not written
- *   ws, ws_bytes        workspace of at least beam_moe_workspace_bytes(dims, T)
+ *   ws, ws_bytes        workspace of at least beam_moe_route_workspace_bytes(dims, T)
+ *                       (beam_moe_workspace_bytes(dims, T) is always enough)
  * The logits are accumulated in FP32 (bf16 x times fp32 W_r, exact products). */
 int beam_moe_route(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
                    const float* logit_bias, const float* select_bias, int32_t* topk_ids, float* topk_w,
@@ -118,7 +131,10 @@ int beam_moe_select(const beam_moe_dims* dims, int32_t T, const float* scores, c
  *   expert_counts   [E]     int32 out: pairs routed to each expert
  *   expert_offsets  [E+1]   int32 out: exclusive prefix sum, [E] = T*K
  *   sorted_slots    [T*K]   int32 out: values i = t*K + k, ascending expert,
- *                           ascending i inside an expert (stable; unique) */
+ *                           ascending i inside an expert (stable; unique)
+ *   ws, ws_bytes            workspace of at least
+ *                           beam_moe_dispatch_workspace_bytes(dims, T)
+ *                           (beam_moe_workspace_bytes(dims, T) is always enough) */
 int beam_moe_dispatch(const beam_moe_dims* dims, int32_t T, const int32_t* topk_ids, int32_t* expert_counts,
                       int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 

@@ -60,6 +60,45 @@ def test_workspace_bytes():
     assert binding.beam_moe_workspace_bytes(TINY, 0) >= 0
 
 
+@pytest.mark.parametrize("T", [1, 64, 4096, 16384, 262144])
+def test_route_and_dispatch_workspace_sizes(T):
+    """Route and dispatch need only their own scratch (split-K partial logits, unit
+    histograms), and the forward workspace is always enough for either."""
+    full = binding.beam_moe_workspace_bytes(BEAM, T)
+    route = binding.beam_moe_route_workspace_bytes(BEAM, T)
+    disp = binding.beam_moe_dispatch_workspace_bytes(BEAM, T)
+    E, K = BEAM.num_experts, BEAM.topk
+    assert T * E * 4 <= route <= 16 * T * E * 4 and route <= full
+    assert disp == -(-T * K // 1024) * E * 4 and disp <= full
+    if T >= 4096:
+        # one split per token tile: T * E * 4 bytes, far below the forward's ~132 KB per token
+        assert route == T * E * 4 and route * 100 < full
+
+
+@pytest.mark.parametrize("K", [1, 8])
+def test_routed_pair_limit(K):
+    """T * K <= 2^28 is accepted; one token more is UNSUPPORTED before any pointer is read."""
+    lib = binding.load_library()
+    cd = binding._cdims(Dims(256, 128, 16, 4, 2, K))
+    T = (1 << 28) // K
+    for fn in (lib.beam_moe_workspace_bytes, lib.beam_moe_route_workspace_bytes,
+               lib.beam_moe_dispatch_workspace_bytes):
+        assert fn(ctypes.byref(cd), T) != binding.SIZE_MAX
+        assert fn(ctypes.byref(cd), T + 1) == binding.SIZE_MAX
+    # at the limit validation reaches the pointers (NULL x: INVALID_ARG); past it, dims fail first
+    args = [None] + [FAKE] * 13
+    assert lib.beam_moe_forward(ctypes.byref(cd), T, *args, 1 << 40, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert lib.beam_moe_forward(ctypes.byref(cd), T + 1, *args, 1 << 40, None) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert lib.beam_moe_dispatch(ctypes.byref(cd), T, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
+        binding.BEAM_MOE_ERR_INVALID_ARG
+    assert lib.beam_moe_dispatch(ctypes.byref(cd), T + 1, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
+        binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert lib.beam_moe_select(ctypes.byref(cd), T + 1, FAKE, None, FAKE, FAKE, None) == \
+        binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert lib.beam_moe_route(ctypes.byref(cd), T + 1, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, 1 << 40,
+                              None) == binding.BEAM_MOE_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("bad", [
     Dims(5120, 2560, 256, 7, 4, 8),      # E % G != 0
     Dims(5120, 2560, 512, 8, 4, 8),      # E > 256
@@ -120,9 +159,15 @@ def test_short_or_missing_workspace_rejected():
     args = list(ok)
     args[13] = None
     assert lib.beam_moe_forward(ctypes.byref(cd), 64, *args, need, None) == binding.BEAM_MOE_ERR_WORKSPACE
-    assert lib.beam_moe_dispatch(ctypes.byref(cd), 64, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+    need_d = lib.beam_moe_dispatch_workspace_bytes(ctypes.byref(cd), 64)
+    need_r = lib.beam_moe_route_workspace_bytes(ctypes.byref(cd), 64)
+    assert lib.beam_moe_dispatch(ctypes.byref(cd), 64, FAKE, FAKE, FAKE, FAKE, FAKE, need_d - 1, None) == \
         binding.BEAM_MOE_ERR_WORKSPACE
-    assert lib.beam_moe_route(ctypes.byref(cd), 64, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, need - 1,
+    assert lib.beam_moe_dispatch(ctypes.byref(cd), 64, FAKE, FAKE, FAKE, FAKE, None, need_d, None) == \
+        binding.BEAM_MOE_ERR_WORKSPACE
+    assert lib.beam_moe_route(ctypes.byref(cd), 64, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, need_r - 1,
+                              None) == binding.BEAM_MOE_ERR_WORKSPACE
+    assert lib.beam_moe_route(ctypes.byref(cd), 64, FAKE, FAKE, None, None, FAKE, FAKE, None, None, need_r,
                               None) == binding.BEAM_MOE_ERR_WORKSPACE
 
 
@@ -226,3 +271,4 @@ def test_residual_forward_fp8_validation():
     assert _res8(lib, binding._cdims(Dims(5120, 2432, 256, 8, 4, 8)), 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
     assert _res8(lib, binding._cdims(Dims(8448, 2560, 256, 8, 4, 8)), 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
     assert _res8(lib, cd, 0, ptrs={k: None for k in _RES8_PTRS}, ws_bytes=0) == binding.BEAM_MOE_OK
+
