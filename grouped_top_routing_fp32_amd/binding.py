@@ -23,10 +23,12 @@ BEAM_MOE_ERR_INVALID_ARG = -1
 BEAM_MOE_ERR_UNSUPPORTED = -2
 BEAM_MOE_ERR_WORKSPACE = -3
 BEAM_MOE_ERR_HIP = -4
+BEAM_MOE_ERR_SCRATCH = -5
+SCRATCH_BYTES = 64 << 20       # BEAM_MOE_SCRATCH_BYTES: scratch of beam_moe_forward_noalloc
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route_workspace_bytes", "beam_moe_dispatch_workspace_bytes",
             "beam_moe_route", "beam_moe_select", "beam_moe_dispatch",
-            "beam_moe_forward", "beam_moe_forward_fp8", "beam_moe_residual_forward",
+            "beam_moe_forward", "beam_moe_forward_noalloc", "beam_moe_forward_fp8", "beam_moe_residual_forward",
             "beam_moe_residual_forward_fp8", "beam_moe_timing_enable", "beam_moe_timing_read", "beam_moe_stage_name",
             "beam_moe_status_str")
 
@@ -71,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.beam_moe_dispatch.restype = ctypes.c_int
     lib.beam_moe_forward.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.beam_moe_forward.restype = ctypes.c_int
+    lib.beam_moe_forward_noalloc.argtypes = [pd, i32] + [vp] * 13 + [vp]
+    lib.beam_moe_forward_noalloc.restype = ctypes.c_int
     lib.beam_moe_forward_fp8.argtypes = [pd, i32] + [vp] * 17 + [sz, vp]
     lib.beam_moe_forward_fp8.restype = ctypes.c_int
     lib.beam_moe_residual_forward.argtypes = [pd, i32, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
@@ -288,6 +292,24 @@ def beam_moe_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_
         ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), *_outputs(bufs, bufs.out), _stream(stream))
     _check(st, "beam_moe_forward")
+    return bufs
+
+
+def beam_moe_forward_noalloc(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
+                             logit_bias: Optional[torch.Tensor], w_gate: torch.Tensor, w_up: torch.Tensor,
+                             w_down: torch.Tensor, *, select_bias: Optional[torch.Tensor] = None,
+                             bufs: Optional[ForwardBuffers] = None, stream=None) -> ForwardBuffers:
+    """beam_moe_forward on the library's built-in scratch (no workspace); bufs.ws is not used."""
+    T = x.shape[0]
+    _req(x, "x", torch.bfloat16, (T, dims.hidden))
+    _req_router(dims, w_router, logit_bias, select_bias)
+    _req_bf16_experts(dims, w_gate, w_up, w_down)
+    bufs = _buffers(dims, T, x.device, bufs)
+    cd = _cdims(dims)
+    st = load_library().beam_moe_forward_noalloc(
+        ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), *_outputs(bufs, bufs.out)[:6], _stream(stream))
+    _check(st, "beam_moe_forward_noalloc")
     return bufs
 
 

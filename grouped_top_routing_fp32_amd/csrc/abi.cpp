@@ -381,7 +381,7 @@ int residual_block(const beam_moe_dims* d, int32_t T, const float* stream_in, in
       });
 }
 
-// Checks of beam_moe_forward's arguments (everything but
+// Checks shared by beam_moe_forward and beam_moe_forward_noalloc (everything but
 // the workspace); fills the plan.
 int check_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
                   const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
@@ -414,6 +414,53 @@ int forward_bf16(const beam_moe_dims* d, const Plan& p, const void* x_bf16, cons
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// scratch of beam_moe_forward_noalloc
+// ---------------------------------------------------------------------------
+// A static device array: every GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device on the first call there, and only
+// that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[BEAM_MOE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchTable {
+  std::mutex mu;
+  std::array<void*, kMaxDevices> ptr{};
+};
+
+ScratchTable& scratch_table() {
+  static ScratchTable t;
+  return t;
+}
+
+// Device address of the current GPU's scratch; `st` must belong to that GPU.
+int scratch_address(hipStream_t st, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BEAM_MOE_ERR_HIP;
+  if (st) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(st, &sdev) != hipSuccess) return BEAM_MOE_ERR_HIP;
+    if (sdev != dev) return BEAM_MOE_ERR_INVALID_ARG;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return BEAM_MOE_ERR_UNSUPPORTED;
+  ScratchTable& t = scratch_table();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (!t.ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BEAM_MOE_ERR_HIP;
+    t.ptr[dev] = p;
+  }
+  *out = t.ptr[dev];
+  return BEAM_MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t beam_moe_workspace_bytes(const beam_moe_dims* dims, int32_t T) {
@@ -433,6 +480,8 @@ const char* beam_moe_status_str(int status) {
     case BEAM_MOE_ERR_UNSUPPORTED: return "unsupported dims";
     case BEAM_MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case BEAM_MOE_ERR_HIP: return "HIP launch failed";
+    case BEAM_MOE_ERR_SCRATCH:
+      return "batch needs more scratch than the allocation-free entry point holds (BEAM_MOE_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -511,6 +560,24 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
   return forward_bf16(d, p, x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, out, topk_ids, topk_w,
                       expert_counts, expert_offsets, sorted_slots, ws, static_cast<hipStream_t>(stream), true);
+}
+
+int beam_moe_forward_noalloc(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                             const float* logit_bias, const float* select_bias, const void* w_gate,
+                             const void* w_up, const void* w_down, float* out, int32_t* topk_ids, float* topk_w,
+                             int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+                             void* stream) {
+  Plan p;
+  int rc = check_forward(d, T, x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, out, topk_ids,
+                         topk_w, expert_counts, expert_offsets, sorted_slots, &p);
+  if (rc != BEAM_MOE_OK || T == 0) return rc;
+  // the documented rule: a batch fits when the one-size workspace does
+  if (beam_moe_workspace_bytes(d, T) > (size_t)BEAM_MOE_SCRATCH_BYTES) return BEAM_MOE_ERR_SCRATCH;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((rc = scratch_address(st, &ws)) != BEAM_MOE_OK) return rc;
+  return forward_bf16(d, p, x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, out, topk_ids, topk_w,
+                      expert_counts, expert_offsets, sorted_slots, ws, st, false);
 }
 
 int beam_moe_forward_fp8(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,

@@ -71,8 +71,14 @@ enum {
   BEAM_MOE_ERR_INVALID_ARG = -1, /* null pointer, misaligned pointer, negative T */
   BEAM_MOE_ERR_UNSUPPORTED = -2, /* dims outside the supported set above        */
   BEAM_MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
-  BEAM_MOE_ERR_HIP = -4          /* a HIP launch failed                          */
+  BEAM_MOE_ERR_HIP = -4,         /* a HIP launch failed                          */
+  BEAM_MOE_ERR_SCRATCH = -5      /* beam_moe_forward_noalloc: the batch's workspace
+                                    exceeds BEAM_MOE_SCRATCH_BYTES                */
 };
+
+/* Size of the device scratch array built into the library for
+ * beam_moe_forward_noalloc (one per GPU, held until the process ends). */
+#define BEAM_MOE_SCRATCH_BYTES (64u << 20)
 
 /* Bytes of workspace that the forward entry points need for T tokens (one size
  * serves all of them, and it is also enough for beam_moe_route and
@@ -159,6 +165,30 @@ int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, c
                      const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
                      const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
                      int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* beam_moe_forward without the workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It allocates nothing: the scratch that
+ * beam_moe_forward takes from `ws` (router partials, dispatch histograms, tile
+ * table, SwiGLU activations, expert outputs) lives in a static device array of
+ * BEAM_MOE_SCRATCH_BYTES (64 MiB) built into the library, one copy per GPU,
+ * held until the process ends; its address is looked up once per device on the
+ * first call there.
+ *   - A batch fits when beam_moe_workspace_bytes(dims, T) <= BEAM_MOE_SCRATCH_BYTES
+ *     (at Beam dims: T <= 471 tokens); larger ones return BEAM_MOE_ERR_SCRATCH
+ *     before any launch.
+ *   - Every call on one GPU uses that GPU's single array, which keeps what the
+ *     last call left there: calls that overlap on one GPU (other streams, other
+ *     threads) race and must be ordered by the caller.  Nothing in the array
+ *     has to start at zero: a call writes every byte it reads before reading it.
+ *   - `stream` must belong to the current device (BEAM_MOE_ERR_INVALID_ARG
+ *     otherwise); the stage-timing diagnostics record nothing for this call.
+ * Arguments, outputs and results are those of beam_moe_forward, bit for bit. */
+int beam_moe_forward_noalloc(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                             const float* logit_bias, const float* select_bias, const void* w_gate,
+                             const void* w_up, const void* w_down, float* out, int32_t* topk_ids, float* topk_w,
+                             int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+                             void* stream);
 
 /* The whole block with FP8 expert weights (steps 1-5 as beam_moe_forward).
  * The FP8 checkpoint of the model stores every expert weight as E4M3 and keeps

@@ -44,7 +44,7 @@ def test_library_symbols_are_plain_c():
 
 def test_status_strings():
     lib = binding.load_library()
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert lib.beam_moe_status_str(st)
     assert b"unknown" in lib.beam_moe_status_str(7)
 
@@ -272,3 +272,24 @@ def test_residual_forward_fp8_validation():
     assert _res8(lib, binding._cdims(Dims(8448, 2560, 256, 8, 4, 8)), 64) == binding.BEAM_MOE_ERR_UNSUPPORTED
     assert _res8(lib, cd, 0, ptrs={k: None for k in _RES8_PTRS}, ws_bytes=0) == binding.BEAM_MOE_OK
 
+
+def test_forward_noalloc_validation():
+    """Every rejection returns before any device call (no GPU is touched here)."""
+    lib = binding.load_library()
+    cd = binding._cdims(BEAM)
+    ok = [FAKE] * 13
+    assert lib.beam_moe_workspace_bytes(ctypes.byref(cd), 472) > binding.SCRATCH_BYTES
+    assert lib.beam_moe_forward_noalloc(ctypes.byref(cd), 472, *ok, None) == binding.BEAM_MOE_ERR_SCRATCH
+    assert lib.beam_moe_forward_noalloc(ctypes.byref(cd), 1 << 20, *ok, None) == binding.BEAM_MOE_ERR_SCRATCH
+    for i in range(13):
+        if i in (2, 3):   # the optional biases: NULL allowed, misaligned not
+            args = list(ok)
+            args[i] = ctypes.c_void_p((1 << 20) + 4)
+        else:
+            args = list(ok)
+            args[i] = None
+        assert lib.beam_moe_forward_noalloc(ctypes.byref(cd), 64, *args, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert lib.beam_moe_forward_noalloc(ctypes.byref(cd), -1, *ok, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    bad = binding._cdims(Dims(5120, 2560, 256, 7, 4, 8))
+    assert lib.beam_moe_forward_noalloc(ctypes.byref(bad), 64, *ok, None) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert lib.beam_moe_forward_noalloc(ctypes.byref(cd), 0, *([None] * 13), None) == binding.BEAM_MOE_OK
