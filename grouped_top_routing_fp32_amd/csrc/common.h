@@ -57,21 +57,22 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   return r;
 }
 
-// Same, each value multiplied by 2^s first (exact).
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8_scaled(u32x4 v, int s) {
-  u32x4 r;
+// acc * 2^d, exact (power-of-two scaling of FP32 values far from its range limits).
+__device__ __forceinline__ f32x4 ldexp4(f32x4 v, int d) {
+  f32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(v[i] << 16), s);
-    const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), s);
-    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-  }
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_ldexpf(v[i], d);
   return r;
 }
 
 // Power-of-two scale exponent s >= 0 for a block of SwiGLU activations whose
 // largest magnitude is maxabs: maxabs * 2^-s < 2^15, so every value of the
 // block fits fp16 (max 65504) after scaling by 2^-s.
+// The down projection multiplies the stored h * 2^-s by the unscaled weights
+// and keeps its FP32 accumulators in units of 2^s of the block it consumes
+// last: moving to a block of exponent s' multiplies them by 2^(s - s'), and
+// the output is acc * 2^s at the end.  The weights never carry the scale, so
+// no weight range limit comes with large activations.
 __device__ __forceinline__ int act_scale_exp(float maxabs) {
   const int e = __builtin_amdgcn_frexp_expf(maxabs);  // maxabs < 2^e
   return e > 15 ? e - 15 : 0;

@@ -11,8 +11,11 @@
 // h is handed to the down projection as fp16 (11 significant bits against
 // bf16's 8) with a power-of-two scale 2^-s per block of 64 columns of a pass
 // of rows, s chosen so the block's largest magnitude stays below 2^15; W_down
-// is converted from bf16 to fp16 exactly (times 2^s) as it is loaded.  y goes
-// to the combine the same way: fp16 scaled by 2^-s per (row group, 64 columns).
+// is converted from bf16 to fp16 exactly as it is read, and the FP32
+// accumulators are kept in units of 2^s of the activation block they consume
+// (rescaled exactly when s changes), so the weights never carry the scale.  y
+// goes to the combine the same way: fp16 scaled by 2^-s per (row group, 64
+// columns).
 // Rows are processed in expert-sorted order (the dispatch permutation); a
 // tile table produced by the dispatch maps workgroups to experts.
 //
@@ -288,6 +291,7 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
     const bool rv = m < nrows;
     const int arow = 64 + (rv ? m : 0);
     const int brow = wave * 16 + m;
+    int s_acc = 0;  // acc holds y * 2^-s_acc (the activation block consumed last)
     for (int st = 0; st < nst; ++st) {
       const int later = min(SLOTS - 2, nst - 1 - st);
       if (later >= 2)
@@ -305,11 +309,17 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
         const int c = 4 * s + (lane >> 4);
         const u32x4 a = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(arow, c));
         const u32x4 b = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(brow, c));
-        const int kb = (st * SK + 32 * s) / kScaleCols;
-        const u32x4 bh = scaled ? bf16x8_to_f16x8_scaled(b, ssc[kb]) : bf16x8_to_f16x8(b);
-        acc = mfma16x16x32_f16(rv ? a : u32x4{0u, 0u, 0u, 0u}, bh, acc);
+        if (scaled) {
+          const int sk = __builtin_amdgcn_readfirstlane(ssc[(st * SK + 32 * s) / kScaleCols]);
+          if (sk != s_acc) {
+            acc = ldexp4(acc, s_acc - sk);
+            s_acc = sk;
+          }
+        }
+        acc = mfma16x16x32_f16(rv ? a : u32x4{0u, 0u, 0u, 0u}, bf16x8_to_f16x8(b), acc);
       }
     }
+    acc = ldexp4(acc, s_acc);
     store_y_pass(acc, nrows, yslot, y16, yscale, H, col, smax);
     __syncthreads();  // every wave is done with the ring and the scales before the next pass
   }
@@ -323,8 +333,8 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
 // the granularity of its scales is not given, taken here as one fp32 scale
 // per output row.  W[r, :] = decode(q[r, :]) * scale[r]: the codes are decoded
 // exactly to bf16 (gate/up, against bf16 activations) or fp16 (down, against
-// the fp16 activations, times the activations' 2^s) in registers, the MFMAs
-// accumulate in FP32 and the row scale multiplies the accumulator.  Half the
+// the fp16 activations, whose 2^s the accumulator carries) in registers, the
+// MFMAs accumulate in FP32 and the row scale multiplies the accumulator.  Half the
 // bytes of the bf16 weights for the same arithmetic.
 //
 // Stage of kF8Sk = 256 of K: weight rows of 256 bytes (256 codes) and
@@ -354,15 +364,15 @@ __device__ __forceinline__ void fp8x16_to_bf16(u32x4 q, u32x4& lo, u32x4& hi) {
   }
 }
 
-// 16 E4M3 codes times sc (a power of two) -> two operands of 8 fp16 (exact
-// while |value * sc| stays within fp16's range).
-__device__ __forceinline__ void fp8x16_to_f16(u32x4 q, float sc, u32x4& lo, u32x4& hi) {
+// 16 E4M3 codes -> two operands of 8 fp16 (exact: every E4M3 value, at most 448
+// in magnitude, is an fp16 value).
+__device__ __forceinline__ void fp8x16_to_f16(u32x4 q, u32x4& lo, u32x4& hi) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i], sc, false));
-    lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i], sc, true));
-    hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i + 2], sc, false));
-    hi[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i + 2], sc, true));
+    lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i], 1.0f, false));
+    lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i], 1.0f, true));
+    hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i + 2], 1.0f, false));
+    hi[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q[i + 2], 1.0f, true));
   }
 }
 
@@ -556,6 +566,7 @@ __global__ __launch_bounds__(256) void down_stream_fp8_kernel(const uint16_t* __
     const int arow = rv ? m : 0;
     const int brow = wave * 16 + m;
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+    int s_acc = 0;  // acc holds y * 2^-s_acc (the activation block consumed last)
     for (int st = 0; st < nst; ++st) {
       const int later = min(SLOTS - 2, nst - 1 - st);
       if (later >= 2)
@@ -576,13 +587,20 @@ __global__ __launch_bounds__(256) void down_stream_fp8_kernel(const uint16_t* __
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw));
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw + 1));
         // the 64 K values of step j share one activation scale block
-        const float sc = scaled ? __builtin_amdgcn_ldexpf(1.0f, ssc[(st * kF8Sk) / kScaleCols + j]) : 1.0f;
+        if (scaled) {
+          const int sk = __builtin_amdgcn_readfirstlane(ssc[(st * kF8Sk) / kScaleCols + j]);
+          if (sk != s_acc) {
+            acc = ldexp4(acc, s_acc - sk);
+            s_acc = sk;
+          }
+        }
         u32x4 b0, b1;
-        fp8x16_to_f16(bq, sc, b0, b1);
+        fp8x16_to_f16(bq, b0, b1);
         acc = mfma16x16x32_f16(rv ? a0 : zero, b0, acc);
         acc = mfma16x16x32_f16(rv ? a1 : zero, b1, acc);
       }
     }
+    acc = ldexp4(acc, s_acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] *= scale_d;
     store_y_pass(acc, nrows, yslot, y16, yscale, H, col, smax);

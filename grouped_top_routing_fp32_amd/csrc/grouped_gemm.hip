@@ -30,14 +30,16 @@
 // the start of step t.  The copies are issued with inline assembly and waited
 // for explicitly (s_waitcnt vmcnt, then s_barrier for the other waves): the
 // compiler's own tracking of LDS copies adds a full drain at each loop head.
-// Down: the weight stage is loaded into registers, converted to fp16 (times
-// 2^s of the stage's 64-column activation block) and written to LDS by the
-// threads themselves, in the same layout the copies produce.
+// Down: the weight stage is loaded into registers, converted to fp16 and
+// written to LDS by the threads themselves, in the same layout the copies
+// produce; the accumulators are kept in units of 2^s of the stage's 64-column
+// activation block and rescaled (exactly) when s changes from one stage to the
+// next, so the weights are never scaled.
 // FP8 weights (E4M3 codes with one fp32 scale per output row; 「Reflection 放出
 // 501B 的 Beam 权重：四套精度、滑动窗口和一场榜单落差」, the FP8 repository's
 // precision listing): both projections take their weights through registers
-// the same way, decoding 8 codes per lane exactly (bf16 for gate/up, fp16 times
-// 2^s for down); the row scales multiply the accumulators before the epilogue.
+// the same way, decoding 8 codes per lane exactly (bf16 for gate/up, fp16 for
+// down); the row scales multiply the accumulators before the epilogue.
 // Blocks are ordered for L2 reuse: each XCD (block b runs on XCD b % 8) takes
 // a contiguous range of a linear order in which an expert's row tiles sweep
 // the column blocks together, so blocks dispatched one after another share the
@@ -159,26 +161,25 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
 #pragma unroll
     for (int q = 0; q < 4; ++q) breg[q] = *reinterpret_cast<const BReg*>(bsrc[q] + k);
   };
-  auto store_b = [&](int stage, int slot) {
-    const int sexp = bsexp;
+  // the weights are converted unscaled: down's accumulators carry the activations' 2^s
+  auto store_b = [&](int slot) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       u32x4 v;
       if constexpr (FP8) {
         const uint32_t c[2] = {breg[q].x, breg[q].y};
-        const float sc = __builtin_amdgcn_ldexpf(1.0f, sexp);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           if constexpr (GATEUP) {
             v[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false));
             v[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true));
           } else {
-            v[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], sc, false));
-            v[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], sc, true));
+            v[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], 1.0f, false));
+            v[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], 1.0f, true));
           }
         }
       } else {
-        v = sexp ? bf16x8_to_f16x8_scaled(breg[q], sexp) : bf16x8_to_f16x8(breg[q]);
+        v = bf16x8_to_f16x8(breg[q]);
       }
       *reinterpret_cast<u32x4*>(&sB[slot][(32 * wave + 8 * q) * kBK + lane * 8]) = v;
     }
@@ -264,10 +265,15 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
   // before the MFMAs and written, converted, to the other slot after them; the
   // next barrier publishes them.
   const int nk = Kdim / kBK;  // Kdim % 128 == 0, so nk >= 2
+  // down: the accumulators hold y * 2^-s_acc, s_acc the exponent of the last stage
+  // consumed; s_next is the exponent of the stage waiting in the other slot
+  int s_acc = 0, s_next = 0;
   issue_a(0, 0);
   if constexpr (kRegB) {
     load_b(0);
-    store_b(0, 0);
+    store_b(0);
+    s_next = bsexp;
+    s_acc = bsexp;
   } else {
     issue_b(0, 0);
   }
@@ -278,6 +284,7 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_s_barrier();
       const bool more = st + 1 < nk;
+      const int s_st = s_next;
       if (more) {
         issue_a(st + 1, slot ^ 1);
         if constexpr (kRegB)
@@ -285,13 +292,25 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
         else
           issue_b(st + 1, slot ^ 1);
       }
+      if constexpr (!GATEUP) {
+        if (s_st != s_acc) {  // uniform: one exponent per tile and stage
+#pragma unroll
+          for (int i = 0; i < kLev; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = ldexp4(acc[i][j], s_acc - s_st);
+          s_acc = s_st;
+        }
+      }
       if constexpr (GATEUP && !FP8 && kLev == 4) {
         math2(slot, full);
       } else {
         math(slot, 0, full);
         math(slot, 1, full);
       }
-      if (kRegB && more) store_b(st + 1, slot ^ 1);
+      if (kRegB && more) {
+        store_b(slot ^ 1);
+        s_next = bsexp;
+      }
     }
   };
   // full tiles (the common case) run without the per-level tests
@@ -314,6 +333,12 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
     for (int i = 0; i < kLev; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] *= rs[j];
+  }
+  if (!GATEUP && s_acc != 0) {  // y = acc * 2^s_acc
+#pragma unroll
+    for (int i = 0; i < kLev; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = ldexp4(acc[i][j], s_acc);
   }
   if (GATEUP) {
     float mx = 0.f;
@@ -408,8 +433,8 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
 //          scaled by 2^-s with s per (tile, 64 columns) written to oscale [n, H / 64].
 // FP8: the weights are E4M3 codes (uint8) with one fp32 scale per output row (s0 for w0, s1 for
 //      w1, [E, Ndim]); every copy of them passes through registers, where the codes are decoded
-//      exactly (to bf16 for gate/up, to fp16 times the stage's 2^s for down), and the row scales
-//      multiply the accumulators before the epilogue.
+//      exactly (to bf16 for gate/up, to fp16 for down), and the row scales multiply the
+//      accumulators before the epilogue.
 template <bool GATEUP, bool FP8>
 __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_slots, const Tile* __restrict__ tiles,

@@ -156,7 +156,10 @@ int beam_moe_dispatch(const beam_moe_dims* dims, int32_t T, const int32_t* topk_
  * chosen so the block's largest magnitude stays below 2^15 (no overflow);
  * the down projection runs on fp16 MFMA with FP32 accumulation, with W_down
  * converted from bf16 to fp16, exactly where representable (magnitudes below
- * 2^-14 after scaling become fp16 subnormals, rounded toward zero). The expert
+ * 2^-14 become fp16 subnormals, rounded toward zero; above 65504 they would
+ * not be representable, far outside any weight range). The accumulators carry
+ * the activations' power-of-two scales (rescaled exactly from one 64-column
+ * block to the next), so large activations set no limit on the weights. The expert
  * outputs leave the down projection the same way (fp16 times a power-of-two
  * scale per 64 columns of a row group); out is their weighted sum in FP32,
  * over k in ascending order.

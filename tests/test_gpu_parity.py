@@ -222,6 +222,14 @@ MID = {
                                       expert_sigma=10.0), None),
     "mid_tiled_big": (synth.Workload("mid_tiled_big", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06,
                                      expert_sigma=10.0), None),
+    # huge activations (expert weights N(0, 200^2)): SwiGLU activations near 2^24 and expert
+    # outputs near 2^36, so h and y carry scales 2^-s with s >= 9.  The down projection keeps
+    # its accumulators in units of 2^s and never scales its weights: weights times 2^s would
+    # pass fp16's 65504 here
+    "mid_stream_huge": (synth.Workload("mid_stream_huge", 40, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
+                                       expert_sigma=200.0), None),
+    "mid_tiled_huge": (synth.Workload("mid_tiled_huge", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06,
+                                      expert_sigma=200.0), None),
     # grouped path just above the stream threshold (about 9 rows per expert) with skew:
     # mostly near-empty tiles, whose idle waves copy no activations
     "mid_grouped_skew": (synth.Workload("mid_grouped_skew", 150, synth.Dims(512, 256, 64, 8, 4, 4),
@@ -536,6 +544,12 @@ FP8 = {
                                       zipf_s=1.2),
     "f8_grouped_big": synth.Workload("f8_grouped_big", 900, synth.Dims(512, 512, 16, 4, 2, 4), router_sigma=0.06,
                                      expert_sigma=10.0),
+    # huge activations (near 2^24, scales 2^-s with s >= 9): E4M3 values up to 448 times 2^s would
+    # pass fp16's range if the down weights carried the scale; the accumulators carry it instead
+    "f8_huge": synth.Workload("f8_huge", 40, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
+                              expert_sigma=200.0),
+    "f8_grouped_huge": synth.Workload("f8_grouped_huge", 900, synth.Dims(512, 512, 16, 4, 2, 4), router_sigma=0.06,
+                                      expert_sigma=200.0),
     # merged tails (a last tile of at most 64 rows joins the tile before it) with large activations
     "f8_dense_merged_big": synth.Workload("f8_dense_merged_big", 560, synth.Dims(256, 256, 1, 1, 1, 1),
                                           router_sigma=0.06, expert_sigma=10.0),
