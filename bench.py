@@ -523,11 +523,11 @@ def cpu_baseline(r, target_s, seed=0):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
-def expert_path(wl):
-    """Which expert kernels the library runs for this batch (its rule: at most 4 rows per
-    expert on average -> stream kernels, else the grouped GEMMs)."""
-    avg = wl.tokens * wl.dims.topk / wl.dims.num_experts
-    return "stream" if avg <= 4 else "grouped GEMM"
+def expert_path(wl, fp8=False):
+    """Which expert kernels the library runs for this batch, as it reports them."""
+    from grouped_top_routing_fp32_amd import binding
+    rows = binding.beam_moe_stream_rows(wl.dims, wl.tokens, fp8)
+    return f"stream, {rows}-row tiles" if rows else "grouped GEMM"
 
 
 def sweep(args, experts, experts_fp8=None):
@@ -544,7 +544,8 @@ def sweep(args, experts, experts_fp8=None):
         s = layer_summary(r)
         hbm, mfma = s["layer_hbm_frac"], s["layer_mfma_frac"]
         points.append({"T": T, "steps": steps, "ms_per_step": round(r["ms_per_step"], 4),
-                       "tokens_per_s": round(T / (r["ms_per_step"] / 1e3), 1), "path": expert_path(wl),
+                       "tokens_per_s": round(T / (r["ms_per_step"] / 1e3), 1),
+                       "path": expert_path(wl, experts_fp8 is not None),
                        "experts_touched": r["n_touched"], "max_rows_per_expert": r["max_count"],
                        "layer_hbm_gbs": s["layer_hbm_gbs"], "layer_hbm_frac": hbm,
                        "layer_expert_tflops": s["layer_expert_tflops"], "layer_mfma_frac": mfma,
@@ -552,7 +553,8 @@ def sweep(args, experts, experts_fp8=None):
         print(f"[bench] sweep T={T}: {r['ms_per_step']:.4f} ms, hbm {hbm:.3f}, mfma {mfma:.3f}",
               file=sys.stderr, flush=True)
     print(json.dumps({"metric": "MoE-layer tokens/s and roofline fractions over batch size T", "unit": "tokens/s",
-                      "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+                      "n_gpus": 1, "dtype": DTYPE_FP8 if experts_fp8 is not None else DTYPE_BF16,
+                      "data": "synthetic",
                       "config": {"workload": "Beam MoE block forward, T swept", "hidden": base.dims.hidden,
                                  "intermediate": base.dims.intermediate, "experts": base.dims.num_experts,
                                  "topk": base.dims.topk,

@@ -29,8 +29,8 @@ SCRATCH_BYTES = 64 << 20       # BEAM_MOE_SCRATCH_BYTES: scratch of beam_moe_for
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route_workspace_bytes", "beam_moe_dispatch_workspace_bytes",
             "beam_moe_route", "beam_moe_select", "beam_moe_dispatch",
             "beam_moe_forward", "beam_moe_forward_noalloc", "beam_moe_forward_fp8", "beam_moe_residual_forward",
-            "beam_moe_residual_forward_fp8", "beam_moe_timing_enable", "beam_moe_timing_read", "beam_moe_stage_name",
-            "beam_moe_status_str")
+            "beam_moe_residual_forward_fp8", "beam_moe_stream_rows", "beam_moe_timing_enable",
+            "beam_moe_timing_read", "beam_moe_stage_name", "beam_moe_status_str")
 
 SIZE_MAX = 2 ** 64 - 1
 
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.beam_moe_residual_forward.restype = ctypes.c_int
     lib.beam_moe_residual_forward_fp8.argtypes = [pd, i32, vp, i32, vp, vp, ctypes.c_float] + [vp] * 16 + [sz, vp]
     lib.beam_moe_residual_forward_fp8.restype = ctypes.c_int
+    lib.beam_moe_stream_rows.argtypes = [pd, i32, ctypes.c_int]
+    lib.beam_moe_stream_rows.restype = ctypes.c_int
     lib.beam_moe_timing_enable.argtypes = [ctypes.c_int]
     lib.beam_moe_timing_enable.restype = ctypes.c_int
     lib.beam_moe_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32),
@@ -392,6 +394,15 @@ def beam_moe_residual_forward_fp8(dims: Dims, stream_in: torch.Tensor, step: int
 # --------------------------------------------------------------------------
 # stage timing diagnostics
 # --------------------------------------------------------------------------
+def beam_moe_stream_rows(dims: Dims, T: int, fp8: bool = False) -> int:
+    """Rows per stream-kernel tile the forward entry points use for T tokens, or 0 for the grouped GEMMs."""
+    cd = _cdims(dims)
+    r = load_library().beam_moe_stream_rows(ctypes.byref(cd), int(T), int(bool(fp8)))
+    if r < 0:
+        raise BeamMoeError(r, "beam_moe_stream_rows")
+    return r
+
+
 def beam_moe_timing_enable(enable: bool = True) -> None:
     _check(load_library().beam_moe_timing_enable(int(bool(enable))), "beam_moe_timing_enable")
 

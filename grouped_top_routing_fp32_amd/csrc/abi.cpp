@@ -23,22 +23,22 @@ int dispatch_units(int n);
 hipError_t launch_dispatch(const int32_t* ids, int n, int E, int32_t* unit_hist, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_slots, Tile* tiles, int mt, int32_t* ntiles, hipStream_t st);
 int scale_cols();
-bool stream_fits(int H, int I);
+bool stream_fits(int H, int I, int R);
 hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
-                                int H, int I, int K, hipStream_t st);
+                                int max_tiles, int R, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
+                                uint8_t* hscale, int H, int I, int K, hipStream_t st);
 hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                              const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16,
+                              const int32_t* ntiles, int max_tiles, int R, const uint16_t* wd, uint16_t* y16,
                               uint8_t* yscale, int H, int I, hipStream_t st);
 hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
                           hipStream_t st);
-bool stream_fp8_fits(int H, int I);
+bool stream_fp8_fits(int H, int I, int R);
 hipError_t launch_gateup_stream_fp8(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                                    int max_tiles, const uint8_t* wg, const uint8_t* wu, const float* sg,
+                                    int max_tiles, int R, const uint8_t* wg, const uint8_t* wu, const float* sg,
                                     const float* su, uint16_t* h, uint8_t* hscale, int H, int I, int K,
                                     hipStream_t st);
 hipError_t launch_down_stream_fp8(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                                  const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd,
+                                  const int32_t* ntiles, int max_tiles, int R, const uint8_t* wd, const float* sd,
                                   uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st);
 hipError_t launch_gateup_grouped_fp8(const uint16_t* x, const int32_t* slots, const Tile* tiles,
                                      const int32_t* ntiles, int max_tiles, const uint8_t* wg, const uint8_t* wu,
@@ -66,7 +66,6 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kTileBytes = 32;          // sizeof(beam::Tile)
-constexpr int kWholeExpert = 1 << 30;   // tile height meaning "all rows of the expert"
 constexpr int64_t kMaxPairs = 1 << 28;  // T * K limit
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -84,16 +83,21 @@ bool dims_ok(const beam_moe_dims* d) {
   return true;
 }
 
-// Expert-path choice: the stream kernels serve batches with at most 4 rows per
-// expert on average, the grouped GEMMs the rest.  The stream kernels read an
-// expert's weights once per pass of 8 rows, the grouped GEMMs once per 256-row
-// tile, so the stream kernels win only while an expert rarely sees more than
-// one pass (measured at Beam dims: T = 128 runs 3.5 ms on the stream kernels,
-// T = 160 .. 1024 run 4.0 .. 4.3 ms on the grouped GEMMs).
-bool use_stream_path(const beam_moe_dims* d, int T, bool fp8 = false) {
-  const bool few_rows = (double)T * d->topk / d->num_experts <= 4.0;
-  return few_rows && (fp8 ? beam::stream_fp8_fits(d->hidden, d->intermediate)
-                          : beam::stream_fits(d->hidden, d->intermediate));
+// Expert-path choice.  The stream kernels take tiles of at most R rows and
+// stream an expert's weights once per tile; R is the smallest of 8, 16, 32 and
+// 64 that is at least twice the average rows per expert, so nearly every expert
+// has one tile.  Above 32 rows per expert on average the grouped GEMMs take the
+// batch: they read an expert's weights once per 256-row tile at MFMA-bound
+// rates.  Returns R, or 0 for the grouped GEMMs.
+int stream_rows(const beam_moe_dims* d, int T, bool fp8 = false) {
+  const double avg = (double)T * d->topk / d->num_experts;
+  for (int R = 8; R <= 64; R *= 2)
+    if (avg * 2.0 <= R)
+      return (fp8 ? beam::stream_fp8_fits(d->hidden, d->intermediate, R)
+                  : beam::stream_fits(d->hidden, d->intermediate, R))
+                 ? R
+                 : 0;
+  return 0;
 }
 
 struct Plan {
@@ -106,6 +110,7 @@ struct Plan {
   size_t off_hist;
   // expert tiles
   bool stream;
+  int rows;  // stream path: rows per tile
   // one tile table serves both projections: whole experts (stream path) or
   // row tiles of the grouped GEMMs, whose down kernel reads the activation
   // scales of the gate/up tile its rows belong to
@@ -136,15 +141,11 @@ void make_plan(const beam_moe_dims* d, int T, Plan* p, bool fp8 = false) {
   p->k_per_split = steps_per * 32;
   p->splits = (ksteps + steps_per - 1) / steps_per;
   p->units = beam::dispatch_units(p->n);
-  p->stream = use_stream_path(d, T, fp8);
+  p->rows = stream_rows(d, T, fp8);
+  p->stream = p->rows > 0;
   const int touched = p->E < p->n ? p->E : p->n;  // most experts with rows
-  if (p->stream) {
-    p->mt = kWholeExpert;
-    p->max_tiles = touched;
-  } else {
-    p->mt = beam::grouped_gemm_rows();
-    p->max_tiles = p->n / p->mt + touched;
-  }
+  p->mt = p->stream ? p->rows : beam::grouped_gemm_rows();
+  p->max_tiles = p->n / p->mt + touched;
   size_t off = 0;
   p->off_part = off;
   off = align_up(off + (size_t)p->splits * T * p->E * sizeof(float));
@@ -320,27 +321,27 @@ int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* w
                                  a.expert_offsets, a.sorted_slots, tiles, p.mt, ntiles, st));
   BEAM_TRY(mark(ev, kStGateUp, st));
   if (a.qg && p.stream)
-    BEAM_TRY(beam::launch_gateup_stream_fp8(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qg, a.qu, a.sg, a.su,
-                                            h, hscale, p.H, p.I, p.K, st));
+    BEAM_TRY(beam::launch_gateup_stream_fp8(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, p.rows, a.qg, a.qu,
+                                            a.sg, a.su, h, hscale, p.H, p.I, p.K, st));
   else if (a.qg)
     BEAM_TRY(beam::launch_gateup_grouped_fp8(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qg, a.qu, a.sg,
                                              a.su, h, hscale, p.H, p.I, p.K, st));
   else if (p.stream)
-    BEAM_TRY(beam::launch_gateup_stream(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wg, a.wu, h, hscale, p.H,
-                                        p.I, p.K, st));
+    BEAM_TRY(beam::launch_gateup_stream(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, p.rows, a.wg, a.wu, h,
+                                        hscale, p.H, p.I, p.K, st));
   else
     BEAM_TRY(beam::launch_gateup_grouped(a.x, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wg, a.wu, h, hscale,
                                          p.H, p.I, p.K, st));
   BEAM_TRY(mark(ev, kStDown, st));
   if (a.qd && p.stream)
-    BEAM_TRY(beam::launch_down_stream_fp8(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qd, a.sd, y16,
-                                          yscale, p.H, p.I, st));
+    BEAM_TRY(beam::launch_down_stream_fp8(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, p.rows, a.qd, a.sd,
+                                          y16, yscale, p.H, p.I, st));
   else if (a.qd)
     BEAM_TRY(beam::launch_down_grouped_fp8(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qd, a.sd, y16,
                                            yscale, p.H, p.I, st));
   else if (p.stream)
-    BEAM_TRY(beam::launch_down_stream(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wd, y16, yscale, p.H,
-                                      p.I, st));
+    BEAM_TRY(beam::launch_down_stream(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, p.rows, a.wd, y16,
+                                      yscale, p.H, p.I, st));
   else
     BEAM_TRY(beam::launch_down_grouped(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wd, y16, yscale,
                                        p.H, p.I, st));
@@ -588,7 +589,7 @@ int beam_moe_forward_fp8(const beam_moe_dims* d, int32_t T, const void* x_bf16, 
                          void* ws, size_t ws_bytes, void* stream) {
   int rc = check_common(d, T);
   if (rc != BEAM_MOE_OK) return rc;
-  if (!beam::stream_fp8_fits(d->hidden, d->intermediate)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (!beam::stream_fp8_fits(d->hidden, d->intermediate, 8)) return BEAM_MOE_ERR_UNSUPPORTED;
   if (T == 0) return BEAM_MOE_OK;
   if ((rc = check_ptrs({x_bf16, w_router, w_gate_fp8, gate_scale, w_up_fp8, up_scale, w_down_fp8, down_scale, out,
                         topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots})) != BEAM_MOE_OK)
@@ -633,7 +634,7 @@ int beam_moe_residual_forward_fp8(const beam_moe_dims* d, int32_t T, const float
                                   void* stream) {
   int rc = check_common(d, T);
   if (rc != BEAM_MOE_OK) return rc;
-  if (!beam::stream_fp8_fits(d->hidden, d->intermediate)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (!beam::stream_fp8_fits(d->hidden, d->intermediate, 8)) return BEAM_MOE_ERR_UNSUPPORTED;
   if (T > 0 &&
       (rc = check_ptrs({w_gate_fp8, gate_scale, w_up_fp8, up_scale, w_down_fp8, down_scale})) != BEAM_MOE_OK)
     return rc;
@@ -641,6 +642,12 @@ int beam_moe_residual_forward_fp8(const beam_moe_dims* d, int32_t T, const float
                           w_down_fp8, down_scale, topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots);
   return residual_block(d, T, stream_in, step, norm_in_weight, norm_out_weight, norm_eps, a, true, stream_out, ws,
                         ws_bytes, stream);
+}
+
+int beam_moe_stream_rows(const beam_moe_dims* d, int32_t T, int fp8) {
+  const int rc = check_common(d, T);
+  if (rc != BEAM_MOE_OK) return rc;
+  return stream_rows(d, T, fp8 != 0);
 }
 
 int beam_moe_timing_enable(int enable) {

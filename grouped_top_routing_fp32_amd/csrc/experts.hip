@@ -35,48 +35,118 @@
 namespace beam {
 
 // ---------------------------------------------------------------------------
-// stream kernels (few rows per expert)
+// stream kernels (up to R rows per expert tile)
 // ---------------------------------------------------------------------------
-// Destination slots of this lane's rows (4 (lane / 16) + r) of a pass, read
-// when the pass starts so that the loads complete under its main loop; rows
-// past the pass's end read its last row and are never stored.
-__device__ __forceinline__ void load_y_slots(const int32_t* __restrict__ slot_of, int nrows, int32_t (&yslot)[4]) {
+// The dispatch cuts each expert's rows into tiles of at most R rows; one
+// workgroup takes one tile and 64 output columns and streams those columns'
+// weights once over the whole K, against all the tile's rows.  R follows the
+// batch (twice the average rows per expert, 8 .. 64), so an expert's weights
+// are read once per tile and nearly every expert has one tile.
+
+// Destination slots of this lane's rows (16 f + 4 (lane / 16) + r) of a tile,
+// read when the tile starts so that the loads complete under its main loop;
+// rows past the tile's end read its last row and are never stored.
+template <int NF>
+__device__ __forceinline__ void load_y_slots(const int32_t* __restrict__ slot_of, int nrows,
+                                             int32_t (&yslot)[NF][4]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) yslot[r] = slot_of[min((lane >> 4) * 4 + r, nrows - 1)];
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yslot[f][r] = slot_of[min(16 * f + (lane >> 4) * 4 + r, nrows - 1)];
 }
 
-// Writes one pass of y: fp16 bits of acc * 2^-s, s from the largest magnitude
-// of the pass's rows in the workgroup's 64 columns, and s per (row, block).
-__device__ __forceinline__ void store_y_pass(const f32x4& acc, int nrows, const int32_t (&yslot)[4],
+// Writes one tile of y: fp16 bits of acc * 2^-s, s from the largest magnitude
+// of the tile's rows in each 64-column block, and s per (row, block).  Each wave
+// holds NB column fragments (columns col + 16 j); the workgroup's 64 NB columns
+// start at block cb * NB, and wave w's columns lie in block cb * NB + w * NB / 4.
+template <int NF, int NB>
+__device__ __forceinline__ void store_y_tile(const f32x4 (&acc)[NB][NF], int nrows, const int32_t (&yslot)[NF][4],
                                              uint16_t* __restrict__ y16, uint8_t* __restrict__ yscale, int H,
-                                             int col, float* smax) {
+                                             int cb, int col, float* smax) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   float mx = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if ((lane >> 4) * 4 + r < nrows) mx = fmaxf(mx, fabsf(acc[r]));
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * f + (lane >> 4) * 4 + r < nrows) mx = fmaxf(mx, fabsf(acc[j][f][r]));
+  mx = wave_max(mx);
+  if (lane == 0) smax[wave] = mx;
+  __syncthreads();
+  constexpr int kGroup = 4 / NB;  // waves sharing a 64-column block
+  const int g0 = wave / kGroup * kGroup;
+  float bm = smax[g0];
+#pragma unroll
+  for (int i = 1; i < kGroup; ++i) bm = fmaxf(bm, smax[g0 + i]);
+  const int sexp = act_scale_exp(bm);
+  const int blk = cb * NB + wave / kGroup;
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * f + (lane >> 4) * 4 + r;
+      if (row < nrows) {
+        const size_t slot = (size_t)yslot[f][r];
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          y16[slot * H + col + 16 * j] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[j][f][r], -sexp));
+        if (wave == g0 && (lane & 15) == 0) yscale[slot * (H / kScaleCols) + blk] = (uint8_t)sexp;
+      }
+    }
+}
+
+// Writes one tile of h: SwiGLU values v (FP32, zero past the tile's end) as fp16
+// times 2^-s, s from the tile's largest magnitude in the workgroup's 64 columns.
+template <int NF>
+__device__ __forceinline__ void store_h_tile(const float (&v)[NF][4], float mx, const Tile& tl,
+                                             uint16_t* __restrict__ h, uint8_t* __restrict__ hscale, int I, int cb,
+                                             int col, float* smax) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   mx = wave_max(mx);
   if (lane == 0) smax[wave] = mx;
   __syncthreads();
   const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
+  const int nsb = I / kScaleCols;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = (lane >> 4) * 4 + r;
-    if (row < nrows) {
-      const size_t slot = (size_t)yslot[r];
-      y16[slot * H + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(acc[r], -sexp));
-      if (wave == 0 && (lane & 15) == 0) yscale[slot * (H / kScaleCols) + blockIdx.y] = (uint8_t)sexp;
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * f + (lane >> 4) * 4 + r;
+      if (row < tl.rows) {
+        const size_t gr = (size_t)(tl.row_start + row);
+        h[gr * I + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(v[f][r], -sexp));
+        if (wave == 0 && (lane & 15) == 0) hscale[gr * nsb + cb] = (uint8_t)sexp;
+      }
     }
-  }
 }
 
 int scale_cols() { return kScaleCols; }
 
-// One expert per workgroup, 64 output columns, each wave 16 columns over the
-// whole K; weights and the pass's activation rows (at most kLdsRows) reach the
-// MFMAs through LDS.
+// Placement of a stream workgroup: (tile, 64-column block).  The grid is 1-D,
+// sized for the most tiles a batch can have times ncb column blocks; the order
+// spans the tiles this batch has (read on the device), and each XCD (block b runs
+// on XCD b % 8) takes a contiguous range of the tile-major order, so the column
+// blocks of one tile run side by side on one XCD and share its activation rows
+// in that XCD's L2.  Returns false for the surplus blocks, which exit.
+__device__ __forceinline__ bool stream_block(const int32_t* __restrict__ ntiles, int ncb, int& tile, int& cb) {
+  const int real = ntiles[0] * ncb;
+  const int b = blockIdx.x;
+  if (b >= real) return false;
+  const int full = real & ~7;
+  const int lin = b >= full ? b : (b & 7) * (full >> 3) + (b >> 3);
+  tile = lin / ncb;
+  cb = lin - tile * ncb;
+  return true;
+}
+
+// One tile of at most R rows per workgroup, 64 output columns, each wave 16
+// columns over the whole K and all the tile's rows (R / 16 row fragments, one
+// for R = 8); weights and the tile's activation rows reach the MFMAs through LDS.
 // Per stage of kSk = 128 of K, the load unit copies the workgroup's weight rows
 // and the activation rows into a ring slot (global_load_lds), each copy taking
 // 4 rows x 256 contiguous bytes: register operand loads touch 16 rows x 64
@@ -85,9 +155,7 @@ int scale_cols() { return kScaleCols; }
 // its 16-byte chunk c sits at position c ^ (r & 15), so the 16 rows read by one
 // MFMA operand load fall on distinct banks.  A copy of row r fetches, for its
 // lane at position p, the chunk p ^ (r & 15).
-constexpr int kLdsRows = 8;  // activation rows per pass
-constexpr int kSk = 128;     // K per stage
-constexpr int kSSlots = 3;   // ring depth
+constexpr int kSk = 128;  // K per stage
 
 // Stage geometry for SK elements of K per stage: rows of SK * 2 bytes; one copy
 // (1 KB) covers RPI rows with LPR lanes per row.
@@ -100,6 +168,17 @@ struct StageGeom {
   // the swizzle XORs a chunk index with (row & 15): rows need at least 16 chunks
   // of 16 bytes so that every swizzled chunk stays inside its row's segment
   static_assert(kRowBytes >= 256, "stage rows of at least 16 chunks");
+};
+
+// Activation rows of a tile of R rows: each of the 4 waves copies R / 4 of them,
+// kRPI rows per copy; at R = 8 a wave's two rows take half of one copy's lanes.
+template <int SK, int R>
+struct ActCopies {
+  using G = StageGeom<SK>;
+  static constexpr int kPer = R / 4;                               // rows per wave
+  static constexpr int kCopies = (kPer + G::kRPI - 1) / G::kRPI;  // copy instructions per wave and stage
+  static constexpr int kLanes = kPer < G::kRPI ? kPer * G::kLPR : 64;
+  static_assert(R % 8 == 0 && (kPer < G::kRPI || kPer % G::kRPI == 0), "whole copies or one partial one");
 };
 
 // Source of lane `lane` for a copy whose lanes cover row r at positions
@@ -116,10 +195,23 @@ __device__ __forceinline__ int stage_off(int row, int chunk) {
   return row * StageGeom<SK>::kRowBytes + ((chunk ^ (row & 15)) << 4);
 }
 
-// grid: (max_tiles, I / 64); block 256; dynamic LDS kSSlots * 136 * 256 bytes.
+// Waits until this wave's copies of stage st have landed, `later` stages (at most
+// two) having been requested after it, each with COPIES copy instructions.
+template <int COPIES>
+__device__ __forceinline__ void wait_stage(int later) {
+  if (later >= 2)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * COPIES));
+  else if (later == 1)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(COPIES));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+}
+
+// grid: max_tiles * I / 64 (see stream_block); block 256; dynamic LDS SLOTS * (128 + R) * 256 bytes.
 // Slot rows: 0..63 gate rows of the workgroup's columns, 64..127 the up rows,
-// 128..135 the activation rows of the pass.
-template <int SLOTS, int SK>
+// 128 .. 128 + R - 1 the activation rows of the tile.
+template <int SLOTS, int SK, int R>
 __global__ __launch_bounds__(256) void gateup_stream_lds_kernel(const uint16_t* __restrict__ x,
                                                                 const int32_t* __restrict__ sorted_slots,
                                                                 const Tile* __restrict__ tiles,
@@ -129,104 +221,104 @@ __global__ __launch_bounds__(256) void gateup_stream_lds_kernel(const uint16_t* 
                                                                 uint16_t* __restrict__ h,
                                                                 uint8_t* __restrict__ hscale, int H, int I, int K) {
   using G = StageGeom<SK>;
-  constexpr int kRows = 128 + kLdsRows;
+  using AC = ActCopies<SK, R>;
+  constexpr int kRows = 128 + R;
   constexpr int kSlot = kRows * G::kRowBytes;
   constexpr int kWCopies = 32 / G::kRPI;  // weight copies per wave per stage (32 rows)
-  constexpr int kCopies = kWCopies + 1;   // plus one copy (or part of one) of activation rows
+  constexpr int kCopies = kWCopies + AC::kCopies;
+  constexpr int kNF = (R + 15) / 16;      // row fragments
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   __shared__ float smax[4];
-  if ((int)blockIdx.x >= ntiles[0]) return;
-  const Tile tl = tiles[blockIdx.x];
+  int ti, cb;
+  if (!stream_block(ntiles, I / 64, ti, cb)) return;
+  const Tile tl = tiles[ti];  // at most R rows
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m = lane & 15;
-  const int col = blockIdx.y * 64 + wave * 16 + m;
-  const int nsb = I / kScaleCols;
+  const int col = cb * 64 + wave * 16 + m;
   const int nst = H / SK;
   const size_t ebase = (size_t)tl.expert * I * H;
+  const int nrows = tl.rows;
 
   // weight copies: wave w fills slot rows 32w .. 32w+31 (w < 2: gate, else up)
   const uint16_t* wsrc[kWCopies];
 #pragma unroll
   for (int q = 0; q < kWCopies; ++q) {
     const int r = 32 * wave + G::kRPI * q + lane / G::kLPR;
-    const uint16_t* base = (r < 64 ? wg : wu) + ebase + (size_t)(blockIdx.y * 64 + (r & 63)) * H;
+    const uint16_t* base = (r < 64 ? wg : wu) + ebase + (size_t)(cb * 64 + (r & 63)) * H;
     wsrc[q] = stage_src<SK>(base, r, lane);
   }
-
-  for (int p = 0; p < tl.rows; p += kLdsRows) {
-    const int nrows = min(kLdsRows, tl.rows - p);
-    // activation copies: wave w fills activation rows 2w, 2w+1 (lanes 0 .. 2 LPR - 1)
-    const int xr = 2 * wave + min(1, lane / G::kLPR);
-    const int tok = sorted_slots[tl.row_start + p + min(xr, nrows - 1)] / K;
-    const uint16_t* xsrc = stage_src<SK>(x + (size_t)tok * H, 128 + xr, lane);
-    auto issue = [&](int st, int slot) {
-      unsigned char* sl = ring + slot * kSlot;
-      const int k = st * SK;
+  // activation copies: wave w fills activation rows AC::kPer w .. AC::kPer (w + 1) - 1;
+  // rows past the tile's end repeat its last row
+  const uint16_t* xsrc[AC::kCopies];
 #pragma unroll
-      for (int q = 0; q < kWCopies; ++q) lds_copy16(wsrc[q] + k, lds_addr(sl + (32 * wave + G::kRPI * q) * G::kRowBytes));
-      if (lane < 2 * G::kLPR) lds_copy16(xsrc + k, lds_addr(sl + (128 + 2 * wave) * G::kRowBytes));
-    };
-    f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
-    const bool rv = m < nrows;
-    const int arow = 128 + (rv ? m : 0);
-    const int grow = wave * 16 + m, urow = 64 + wave * 16 + m;
-#pragma unroll
-    for (int s = 0; s < SLOTS - 1; ++s)
-      if (s < nst) issue(s, s);
-    for (int st = 0; st < nst; ++st) {
-      const int later = min(SLOTS - 2, nst - 1 - st);  // stages requested after stage st
-      if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
-      else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_barrier();  // stage st complete for all waves; stage st - 1's slot is free
-      if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
-      const unsigned char* sl = ring + (st % SLOTS) * kSlot;
-#pragma unroll
-      for (int s = 0; s < SK / 32; ++s) {
-        const int c = 4 * s + (lane >> 4);
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(arow, c));
-        const u32x4 g = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(grow, c));
-        const u32x4 u = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(urow, c));
-        const u32x4 az = rv ? a : u32x4{0u, 0u, 0u, 0u};
-        ag = mfma16x16x32(az, g, ag);
-        au = mfma16x16x32(az, u, au);
-      }
-    }
-    // SwiGLU in FP32; one power-of-two scale per (pass, 64 columns)
-    float v[4];
-    float mx = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      v[r] = (row < nrows) ? silu_f32(ag[r]) * au[r] : 0.f;
-      mx = fmaxf(mx, fabsf(v[r]));
-    }
-    mx = wave_max(mx);
-    if (lane == 0) smax[wave] = mx;
-    __syncthreads();  // also: every wave is done with the ring before the next pass refills it
-    const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      if (row < nrows) {
-        const size_t gr = (size_t)(tl.row_start + p + row);
-        h[gr * I + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(v[r], -sexp));
-        if (wave == 0 && m == 0) hscale[gr * nsb + blockIdx.y] = (uint8_t)sexp;
-      }
-    }
-    __syncthreads();  // smax is rewritten by the next pass
+  for (int q = 0; q < AC::kCopies; ++q) {
+    const int xr = AC::kPer * wave + G::kRPI * q + lane / G::kLPR;
+    const int tok = sorted_slots[tl.row_start + min(xr, nrows - 1)] / K;
+    xsrc[q] = stage_src<SK>(x + (size_t)tok * H, 128 + xr, lane);
   }
+  auto issue = [&](int st, int slot) {
+    unsigned char* sl = ring + slot * kSlot;
+    const int k = st * SK;
+#pragma unroll
+    for (int q = 0; q < kWCopies; ++q) lds_copy16(wsrc[q] + k, lds_addr(sl + (32 * wave + G::kRPI * q) * G::kRowBytes));
+#pragma unroll
+    for (int q = 0; q < AC::kCopies; ++q)
+      if (lane < AC::kLanes)
+        lds_copy16(xsrc[q] + k, lds_addr(sl + (128 + AC::kPer * wave + G::kRPI * q) * G::kRowBytes));
+  };
+  f32x4 ag[kNF], au[kNF];
+  int arow[kNF];
+#pragma unroll
+  for (int f = 0; f < kNF; ++f) {
+    ag[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    au[f] = ag[f];
+    const int ar = 16 * f + m;  // at R = 8, operand rows 8..15 read row 0: never stored
+    arow[f] = 128 + (ar < R ? ar : 0);
+  }
+  const int grow = wave * 16 + m, urow = 64 + wave * 16 + m;
+#pragma unroll
+  for (int s = 0; s < SLOTS - 1; ++s)
+    if (s < nst) issue(s, s);
+  for (int st = 0; st < nst; ++st) {
+    wait_stage<kCopies>(min(SLOTS - 2, nst - 1 - st));
+    __builtin_amdgcn_s_barrier();  // stage st complete for all waves; stage st - 1's slot is free
+    if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+    const unsigned char* sl = ring + (st % SLOTS) * kSlot;
+#pragma unroll
+    for (int s = 0; s < SK / 32; ++s) {
+      const int c = 4 * s + (lane >> 4);
+      const u32x4 g = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(grow, c));
+      const u32x4 u = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(urow, c));
+#pragma unroll
+      for (int f = 0; f < kNF; ++f) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(arow[f], c));
+        ag[f] = mfma16x16x32(a, g, ag[f]);
+        au[f] = mfma16x16x32(a, u, au[f]);
+      }
+    }
+  }
+  // SwiGLU in FP32; one power-of-two scale per (tile, 64 columns)
+  float v[kNF][4];
+  float mx = 0.f;
+#pragma unroll
+  for (int f = 0; f < kNF; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * f + (lane >> 4) * 4 + r;
+      v[f][r] = (row < nrows) ? silu_f32(ag[f][r]) * au[f][r] : 0.f;
+      mx = fmaxf(mx, fabsf(v[f][r]));
+    }
+  store_h_tile<kNF>(v, mx, tl, h, hscale, I, cb, col, smax);
 }
 
-// grid: (max_tiles, H / 64); block 256; dynamic LDS SLOTS * 72 * 256 bytes + the
-// pass's scales.  y leaves through store_y_pass.  Slot rows: 0..63 W_down rows of the workgroup's columns,
-// 64..71 the activation rows (h, fp16) of the pass.
-template <int SLOTS, int SK>
+// grid: max_tiles * H / (64 NB) (see stream_block); block 256; dynamic LDS
+// SLOTS * (64 NB + R) * 256 bytes + the tile's scales.  y leaves through
+// store_y_tile.  Each wave owns NB fragments of 16 output columns: the workgroup
+// covers 64 NB columns, so wide tiles (NB = 2) read their activation rows half as
+// often per weight byte, in LDS and from L2.  Slot rows: 0 .. 64 NB - 1 W_down
+// rows of the workgroup's columns, then the R activation rows (h, fp16) of the tile.
+template <int SLOTS, int SK, int R, int NB>
 __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __restrict__ h,
                                                               const uint8_t* __restrict__ hscale,
                                                               const int32_t* __restrict__ sorted_slots,
@@ -236,93 +328,113 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
                                                               uint16_t* __restrict__ y16,
                                                               uint8_t* __restrict__ yscale, int H, int I) {
   using G = StageGeom<SK>;
-  constexpr int kRows = 64 + kLdsRows;
+  using AC = ActCopies<SK, R>;
+  constexpr int kWRows = 64 * NB;
+  constexpr int kRows = kWRows + R;
   constexpr int kSlot = kRows * G::kRowBytes;
-  constexpr int kWCopies = 16 / G::kRPI;  // weight copies per wave per stage (16 rows)
-  constexpr int kCopies = kWCopies + 1;   // plus one copy (or part of one) of activation rows
+  constexpr int kWCopies = 16 * NB / G::kRPI;  // weight copies per wave per stage (16 NB rows)
+  constexpr int kCopies = kWCopies + AC::kCopies;
+  constexpr int kNF = (R + 15) / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   __shared__ int sany;
   __shared__ float smax[4];
-  uint8_t* ssc = ring + SLOTS * kSlot;  // the pass's activation scales
-  if ((int)blockIdx.x >= ntiles[0]) return;
-  const Tile tl = tiles[blockIdx.x];
+  uint8_t* ssc = ring + SLOTS * kSlot;  // the tile's activation scales
+  int ti, cb;
+  if (!stream_block(ntiles, H / kWRows, ti, cb)) return;
+  const Tile tl = tiles[ti];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int m = lane & 15;
-  const int col = blockIdx.y * 64 + wave * 16 + m;
+  const int col = cb * kWRows + wave * 16 * NB + m;  // + 16 j for fragment j
   const int nsb = I / kScaleCols;
   const int nst = I / SK;
+  const int nrows = tl.rows;
 
   const uint16_t* wsrc[kWCopies];
 #pragma unroll
   for (int q = 0; q < kWCopies; ++q) {
-    const int r = 16 * wave + G::kRPI * q + lane / G::kLPR;
-    const uint16_t* base = wd + (size_t)tl.expert * H * I + (size_t)(blockIdx.y * 64 + r) * I;
+    const int r = 16 * NB * wave + G::kRPI * q + lane / G::kLPR;
+    const uint16_t* base = wd + (size_t)tl.expert * H * I + (size_t)(cb * kWRows + r) * I;
     wsrc[q] = stage_src<SK>(base, r, lane);
   }
-
-  for (int p = 0; p < tl.rows; p += kLdsRows) {
-    const int nrows = min(kLdsRows, tl.rows - p);
-    int32_t yslot[4];
-    load_y_slots(sorted_slots + tl.row_start + p, nrows, yslot);
-    const int xr = 2 * wave + min(1, lane / G::kLPR);
-    const uint16_t* xsrc = stage_src<SK>(h + (size_t)(tl.row_start + p + min(xr, nrows - 1)) * I, 64 + xr, lane);
-    auto issue = [&](int st, int slot) {
-      unsigned char* sl = ring + slot * kSlot;
-      const int k = st * SK;
+  int32_t yslot[kNF][4];
+  load_y_slots<kNF>(sorted_slots + tl.row_start, nrows, yslot);
+  const uint16_t* xsrc[AC::kCopies];
 #pragma unroll
-      for (int q = 0; q < kWCopies; ++q) lds_copy16(wsrc[q] + k, lds_addr(sl + (16 * wave + G::kRPI * q) * G::kRowBytes));
-      if (lane < 2 * G::kLPR) lds_copy16(xsrc + k, lds_addr(sl + (64 + 2 * wave) * G::kRowBytes));
-    };
+  for (int q = 0; q < AC::kCopies; ++q) {
+    const int xr = AC::kPer * wave + G::kRPI * q + lane / G::kLPR;
+    xsrc[q] = stage_src<SK>(h + (size_t)(tl.row_start + min(xr, nrows - 1)) * I, kWRows + xr, lane);
+  }
+  auto issue = [&](int st, int slot) {
+    unsigned char* sl = ring + slot * kSlot;
+    const int k = st * SK;
 #pragma unroll
-    for (int s = 0; s < SLOTS - 1; ++s)
-      if (s < nst) issue(s, s);
-    if (tid == 0) sany = 0;
-    __syncthreads();
-    for (int i = tid; i < nsb; i += 256) {
-      const uint8_t sv = hscale[(size_t)(tl.row_start + p) * nsb + i];
-      ssc[i] = sv;
-      if (sv) sany = 1;
-    }
-    __syncthreads();
-    const bool scaled = sany != 0;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool rv = m < nrows;
-    const int arow = 64 + (rv ? m : 0);
-    const int brow = wave * 16 + m;
-    int s_acc = 0;  // acc holds y * 2^-s_acc (the activation block consumed last)
-    for (int st = 0; st < nst; ++st) {
-      const int later = min(SLOTS - 2, nst - 1 - st);
-      if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
-      else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_barrier();
-      if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
-      const unsigned char* sl = ring + (st % SLOTS) * kSlot;
+    for (int q = 0; q < kWCopies; ++q)
+      lds_copy16(wsrc[q] + k, lds_addr(sl + (16 * NB * wave + G::kRPI * q) * G::kRowBytes));
 #pragma unroll
-      for (int s = 0; s < SK / 32; ++s) {
-        const int c = 4 * s + (lane >> 4);
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(arow, c));
-        const u32x4 b = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(brow, c));
-        if (scaled) {
-          const int sk = __builtin_amdgcn_readfirstlane(ssc[(st * SK + 32 * s) / kScaleCols]);
-          if (sk != s_acc) {
-            acc = ldexp4(acc, s_acc - sk);
-            s_acc = sk;
-          }
+    for (int q = 0; q < AC::kCopies; ++q)
+      if (lane < AC::kLanes)
+        lds_copy16(xsrc[q] + k, lds_addr(sl + (kWRows + AC::kPer * wave + G::kRPI * q) * G::kRowBytes));
+  };
+#pragma unroll
+  for (int s = 0; s < SLOTS - 1; ++s)
+    if (s < nst) issue(s, s);
+  if (tid == 0) sany = 0;
+  __syncthreads();
+  for (int i = tid; i < nsb; i += 256) {
+    const uint8_t sv = hscale[(size_t)tl.row_start * nsb + i];  // one scale per (tile, 64 columns)
+    ssc[i] = sv;
+    if (sv) sany = 1;
+  }
+  __syncthreads();
+  const bool scaled = sany != 0;
+  f32x4 acc[NB][kNF];
+  int arow[kNF];
+#pragma unroll
+  for (int f = 0; f < kNF; ++f) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ar = 16 * f + m;
+    arow[f] = kWRows + (ar < R ? ar : 0);
+  }
+  const int brow = wave * 16 * NB + m;  // + 16 j
+  int s_acc = 0;  // acc holds y * 2^-s_acc (the activation block consumed last)
+  for (int st = 0; st < nst; ++st) {
+    wait_stage<kCopies>(min(SLOTS - 2, nst - 1 - st));
+    __builtin_amdgcn_s_barrier();
+    if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+    const unsigned char* sl = ring + (st % SLOTS) * kSlot;
+#pragma unroll
+    for (int s = 0; s < SK / 32; ++s) {
+      const int c = 4 * s + (lane >> 4);
+      u32x4 b[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        b[j] = bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(sl + stage_off<SK>(brow + 16 * j, c)));
+      if (scaled) {
+        const int sk = __builtin_amdgcn_readfirstlane(ssc[(st * SK + 32 * s) / kScaleCols]);
+        if (sk != s_acc) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int f = 0; f < kNF; ++f) acc[j][f] = ldexp4(acc[j][f], s_acc - sk);
+          s_acc = sk;
         }
-        acc = mfma16x16x32_f16(rv ? a : u32x4{0u, 0u, 0u, 0u}, bf16x8_to_f16x8(b), acc);
+      }
+#pragma unroll
+      for (int f = 0; f < kNF; ++f) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(arow[f], c));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[j][f] = mfma16x16x32_f16(a, b[j], acc[j][f]);
       }
     }
-    acc = ldexp4(acc, s_acc);
-    store_y_pass(acc, nrows, yslot, y16, yscale, H, col, smax);
-    __syncthreads();  // every wave is done with the ring and the scales before the next pass
   }
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) acc[j][f] = ldexp4(acc[j][f], s_acc);
+  store_y_tile<kNF, NB>(acc, nrows, yslot, y16, yscale, H, cb, col, smax);
 }
 
 // ---------------------------------------------------------------------------
@@ -334,24 +446,30 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
 // per output row.  W[r, :] = decode(q[r, :]) * scale[r]: the codes are decoded
 // exactly to bf16 (gate/up, against bf16 activations) or fp16 (down, against
 // the fp16 activations, whose 2^s the accumulator carries) in registers, the
-// MFMAs accumulate in FP32 and the row scale multiplies the accumulator.  Half the
-// bytes of the bf16 weights for the same arithmetic.
+// MFMAs accumulate in FP32 and the row scale multiplies the accumulator.  Half
+// the bytes of the bf16 weights for the same arithmetic.
 //
 // Stage of kF8Sk = 256 of K: weight rows of 256 bytes (256 codes) and
 // activation rows of 512 bytes (256 bf16 / fp16 values), both with 16-byte
-// chunk c of row r at position c ^ (r & 15) (activation rows keyed by their
-// index 0..7).  Per 64 of K a lane reads one 16-byte chunk of codes (16 K
-// values) and the two matching 16-byte chunks of its activation row: two
-// MFMAs of K = 32, the first on the chunk's 8 low codes, the second on its
-// 8 high ones.  A and B agree on which K each operand slot holds, which is
-// all a contraction needs.
+// chunk c of row r at position c ^ (r & 15).  Per 64 of K a lane reads one
+// 16-byte chunk of codes (16 K values) and the two matching 16-byte chunks of
+// its activation row: two MFMAs of K = 32, the first on the chunk's 8 low
+// codes, the second on its 8 high ones.  A and B agree on which K each operand
+// slot holds, which is all a contraction needs.
 constexpr int kF8Sk = 256;     // K per stage
 constexpr int kF8WRow = 256;   // bytes of a staged weight row
 constexpr int kF8ARow = 512;   // bytes of a staged activation row
-constexpr int kF8Slots = 3;    // ring depth
 
 __device__ __forceinline__ int f8_woff(int row, int chunk) { return row * kF8WRow + ((chunk ^ (row & 15)) << 4); }
 __device__ __forceinline__ int f8_aoff(int row, int chunk) { return row * kF8ARow + ((chunk ^ (row & 15)) << 4); }
+
+// Activation rows of 512 bytes: each wave copies R / 4 of them, two per copy.
+template <int R>
+struct F8ActCopies {
+  static constexpr int kPer = R / 4;
+  static constexpr int kCopies = kPer / 2;
+  static_assert(R % 8 == 0, "whole copies");
+};
 
 // 16 E4M3 codes -> two operands of 8 bf16 (exact: E4M3 values are bf16 values).
 __device__ __forceinline__ void fp8x16_to_bf16(u32x4 q, u32x4& lo, u32x4& hi) {
@@ -376,10 +494,10 @@ __device__ __forceinline__ void fp8x16_to_f16(u32x4 q, u32x4& lo, u32x4& hi) {
   }
 }
 
-// grid: (max_tiles, I / 64); block 256; dynamic LDS SLOTS * (128 * 256 + 8 * 512) bytes.
+// grid: max_tiles * I / 64 (see stream_block); block 256; dynamic LDS SLOTS * (128 * 256 + R * 512) bytes.
 // Slot: 128 weight rows (0..63 gate, 64..127 up, of the workgroup's columns), then
-// the pass's 8 activation rows.
-template <int SLOTS>
+// the tile's R activation rows.
+template <int SLOTS, int R>
 __global__ __launch_bounds__(256) void gateup_stream_fp8_kernel(const uint16_t* __restrict__ x,
                                                                 const int32_t* __restrict__ sorted_slots,
                                                                 const Tile* __restrict__ tiles,
@@ -390,114 +508,107 @@ __global__ __launch_bounds__(256) void gateup_stream_fp8_kernel(const uint16_t* 
                                                                 const float* __restrict__ su,
                                                                 uint16_t* __restrict__ h,
                                                                 uint8_t* __restrict__ hscale, int H, int I, int K) {
+  using AC = F8ActCopies<R>;
   constexpr int kWBytes = 128 * kF8WRow;
-  constexpr int kSlot = kWBytes + kLdsRows * kF8ARow;
-  constexpr int kWCopies = 8;            // 32 weight rows of 256 bytes per wave: 4 rows per copy
-  constexpr int kCopies = kWCopies + 1;  // plus two activation rows of 512 bytes
+  constexpr int kSlot = kWBytes + R * kF8ARow;
+  constexpr int kWCopies = 8;  // 32 weight rows of 256 bytes per wave: 4 rows per copy
+  constexpr int kCopies = kWCopies + AC::kCopies;
+  constexpr int kNF = (R + 15) / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   __shared__ float smax[4];
-  if ((int)blockIdx.x >= ntiles[0]) return;
-  const Tile tl = tiles[blockIdx.x];
+  int ti, cb;
+  if (!stream_block(ntiles, I / 64, ti, cb)) return;
+  const Tile tl = tiles[ti];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m = lane & 15;
-  const int col = blockIdx.y * 64 + wave * 16 + m;
-  const int nsb = I / kScaleCols;
+  const int col = cb * 64 + wave * 16 + m;
   const int nst = H / kF8Sk;
   const size_t ebase = (size_t)tl.expert * I * H;
+  const int nrows = tl.rows;
 
   // weight copies: wave w fills slot rows 32w .. 32w+31 (w < 2: gate, else up), 16 lanes a row
   const uint8_t* wsrc[kWCopies];
 #pragma unroll
   for (int q = 0; q < kWCopies; ++q) {
     const int r = 32 * wave + 4 * q + (lane >> 4);
-    const uint8_t* base = (r < 64 ? wg : wu) + ebase + (size_t)(blockIdx.y * 64 + (r & 63)) * H;
+    const uint8_t* base = (r < 64 ? wg : wu) + ebase + (size_t)(cb * 64 + (r & 63)) * H;
     wsrc[q] = base + (((lane & 15) ^ (r & 15)) << 4);
   }
   const float scale_g = sg[(size_t)tl.expert * I + col];
   const float scale_u = su[(size_t)tl.expert * I + col];
-
-  for (int p = 0; p < tl.rows; p += kLdsRows) {
-    const int nrows = min(kLdsRows, tl.rows - p);
-    // activation copy: wave w fills activation rows 2w, 2w+1, 32 lanes a row
-    const int xr = 2 * wave + (lane >> 5);
-    const int tok = sorted_slots[tl.row_start + p + min(xr, nrows - 1)] / K;
-    const unsigned char* xsrc =
-        reinterpret_cast<const unsigned char*>(x + (size_t)tok * H) + (((lane & 31) ^ (xr & 15)) << 4);
-    auto issue = [&](int st, int slot) {
-      unsigned char* sl = ring + slot * kSlot;
+  // activation copies: wave w fills rows AC::kPer w .., two rows of 32 lanes per copy
+  const unsigned char* xsrc[AC::kCopies];
 #pragma unroll
-      for (int q = 0; q < kWCopies; ++q)
-        lds_copy16(wsrc[q] + (size_t)st * kF8Sk, lds_addr(sl + (32 * wave + 4 * q) * kF8WRow));
-      lds_copy16(xsrc + (size_t)st * kF8Sk * 2, lds_addr(sl + kWBytes + 2 * wave * kF8ARow));
-    };
-    f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
-    const bool rv = m < nrows;
-    const int arow = rv ? m : 0;
-    const int grow = wave * 16 + m, urow = 64 + wave * 16 + m;
-    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int s = 0; s < SLOTS - 1; ++s)
-      if (s < nst) issue(s, s);
-    for (int st = 0; st < nst; ++st) {
-      const int later = min(SLOTS - 2, nst - 1 - st);  // stages requested after stage st
-      if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
-      else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_barrier();  // stage st complete for all waves; stage st - 1's slot is free
-      if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
-      const unsigned char* sl = ring + (st % SLOTS) * kSlot;
-      const unsigned char* sa = sl + kWBytes;
-#pragma unroll
-      for (int j = 0; j < kF8Sk / 64; ++j) {
-        const int cw = 4 * j + (lane >> 4);
-        const u32x4 gq = *reinterpret_cast<const u32x4*>(sl + f8_woff(grow, cw));
-        const u32x4 uq = *reinterpret_cast<const u32x4*>(sl + f8_woff(urow, cw));
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw));
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw + 1));
-        u32x4 g0, g1, u0, u1;
-        fp8x16_to_bf16(gq, g0, g1);
-        fp8x16_to_bf16(uq, u0, u1);
-        const u32x4 az0 = rv ? a0 : zero, az1 = rv ? a1 : zero;
-        ag = mfma16x16x32(az0, g0, ag);
-        au = mfma16x16x32(az0, u0, au);
-        ag = mfma16x16x32(az1, g1, ag);
-        au = mfma16x16x32(az1, u1, au);
-      }
-    }
-    // row scales, then SwiGLU in FP32; one power-of-two scale per (pass, 64 columns)
-    float v[4];
-    float mx = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      v[r] = (row < nrows) ? silu_f32(ag[r] * scale_g) * (au[r] * scale_u) : 0.f;
-      mx = fmaxf(mx, fabsf(v[r]));
-    }
-    mx = wave_max(mx);
-    if (lane == 0) smax[wave] = mx;
-    __syncthreads();  // also: every wave is done with the ring before the next pass refills it
-    const int sexp = act_scale_exp(fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3])));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      if (row < nrows) {
-        const size_t gr = (size_t)(tl.row_start + p + row);
-        h[gr * I + col] = f32_to_f16_bits(__builtin_amdgcn_ldexpf(v[r], -sexp));
-        if (wave == 0 && m == 0) hscale[gr * nsb + blockIdx.y] = (uint8_t)sexp;
-      }
-    }
-    __syncthreads();  // smax is rewritten by the next pass
+  for (int q = 0; q < AC::kCopies; ++q) {
+    const int xr = AC::kPer * wave + 2 * q + (lane >> 5);
+    const int tok = sorted_slots[tl.row_start + min(xr, nrows - 1)] / K;
+    xsrc[q] = reinterpret_cast<const unsigned char*>(x + (size_t)tok * H) + (((lane & 31) ^ (xr & 15)) << 4);
   }
+  auto issue = [&](int st, int slot) {
+    unsigned char* sl = ring + slot * kSlot;
+#pragma unroll
+    for (int q = 0; q < kWCopies; ++q)
+      lds_copy16(wsrc[q] + (size_t)st * kF8Sk, lds_addr(sl + (32 * wave + 4 * q) * kF8WRow));
+#pragma unroll
+    for (int q = 0; q < AC::kCopies; ++q)
+      lds_copy16(xsrc[q] + (size_t)st * kF8Sk * 2, lds_addr(sl + kWBytes + (AC::kPer * wave + 2 * q) * kF8ARow));
+  };
+  f32x4 ag[kNF], au[kNF];
+  int arow[kNF];
+#pragma unroll
+  for (int f = 0; f < kNF; ++f) {
+    ag[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    au[f] = ag[f];
+    const int ar = 16 * f + m;
+    arow[f] = ar < R ? ar : 0;
+  }
+  const int grow = wave * 16 + m, urow = 64 + wave * 16 + m;
+#pragma unroll
+  for (int s = 0; s < SLOTS - 1; ++s)
+    if (s < nst) issue(s, s);
+  for (int st = 0; st < nst; ++st) {
+    wait_stage<kCopies>(min(SLOTS - 2, nst - 1 - st));
+    __builtin_amdgcn_s_barrier();  // stage st complete for all waves; stage st - 1's slot is free
+    if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+    const unsigned char* sl = ring + (st % SLOTS) * kSlot;
+    const unsigned char* sa = sl + kWBytes;
+#pragma unroll
+    for (int j = 0; j < kF8Sk / 64; ++j) {
+      const int cw = 4 * j + (lane >> 4);
+      u32x4 g0, g1, u0, u1;
+      fp8x16_to_bf16(*reinterpret_cast<const u32x4*>(sl + f8_woff(grow, cw)), g0, g1);
+      fp8x16_to_bf16(*reinterpret_cast<const u32x4*>(sl + f8_woff(urow, cw)), u0, u1);
+#pragma unroll
+      for (int f = 0; f < kNF; ++f) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow[f], 2 * cw));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow[f], 2 * cw + 1));
+        ag[f] = mfma16x16x32(a0, g0, ag[f]);
+        au[f] = mfma16x16x32(a0, u0, au[f]);
+        ag[f] = mfma16x16x32(a1, g1, ag[f]);
+        au[f] = mfma16x16x32(a1, u1, au[f]);
+      }
+    }
+  }
+  // row scales, then SwiGLU in FP32; one power-of-two scale per (tile, 64 columns)
+  float v[kNF][4];
+  float mx = 0.f;
+#pragma unroll
+  for (int f = 0; f < kNF; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * f + (lane >> 4) * 4 + r;
+      v[f][r] = (row < nrows) ? silu_f32(ag[f][r] * scale_g) * (au[f][r] * scale_u) : 0.f;
+      mx = fmaxf(mx, fabsf(v[f][r]));
+    }
+  store_h_tile<kNF>(v, mx, tl, h, hscale, I, cb, col, smax);
 }
 
-// grid: (max_tiles, H / 64); block 256; dynamic LDS SLOTS * (64 * 256 + 8 * 512) bytes + the
-// pass's scales.  Slot: 64 W_down rows of the workgroup's columns, then the pass's 8 h rows.
-template <int SLOTS>
+// grid: max_tiles * H / (64 NB) (see stream_block); block 256; dynamic LDS
+// SLOTS * (64 NB * 256 + R * 512) bytes + the tile's scales.  Slot: 64 NB W_down rows
+// of the workgroup's columns (NB fragments of 16 per wave, as the bf16 kernel), then
+// the tile's R h rows.
+template <int SLOTS, int R, int NB>
 __global__ __launch_bounds__(256) void down_stream_fp8_kernel(const uint16_t* __restrict__ h,
                                                               const uint8_t* __restrict__ hscale,
                                                               const int32_t* __restrict__ sorted_slots,
@@ -507,110 +618,130 @@ __global__ __launch_bounds__(256) void down_stream_fp8_kernel(const uint16_t* __
                                                               const float* __restrict__ sd,
                                                               uint16_t* __restrict__ y16,
                                                               uint8_t* __restrict__ yscale, int H, int I) {
-  constexpr int kWBytes = 64 * kF8WRow;
-  constexpr int kSlot = kWBytes + kLdsRows * kF8ARow;
-  constexpr int kWCopies = 4;            // 16 weight rows of 256 bytes per wave
-  constexpr int kCopies = kWCopies + 1;  // plus two activation rows of 512 bytes
+  using AC = F8ActCopies<R>;
+  constexpr int kWRows = 64 * NB;
+  constexpr int kWBytes = kWRows * kF8WRow;
+  constexpr int kSlot = kWBytes + R * kF8ARow;
+  constexpr int kWCopies = 4 * NB;  // 16 NB weight rows of 256 bytes per wave, 4 rows per copy
+  constexpr int kCopies = kWCopies + AC::kCopies;
+  constexpr int kNF = (R + 15) / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   __shared__ int sany;
   __shared__ float smax[4];
-  uint8_t* ssc = ring + SLOTS * kSlot;  // the pass's activation scales
-  if ((int)blockIdx.x >= ntiles[0]) return;
-  const Tile tl = tiles[blockIdx.x];
+  uint8_t* ssc = ring + SLOTS * kSlot;  // the tile's activation scales
+  int ti, cb;
+  if (!stream_block(ntiles, H / kWRows, ti, cb)) return;
+  const Tile tl = tiles[ti];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int m = lane & 15;
-  const int col = blockIdx.y * 64 + wave * 16 + m;
+  const int col = cb * kWRows + wave * 16 * NB + m;  // + 16 j for fragment j
   const int nsb = I / kScaleCols;
   const int nst = I / kF8Sk;
+  const int nrows = tl.rows;
 
   const uint8_t* wsrc[kWCopies];
 #pragma unroll
   for (int q = 0; q < kWCopies; ++q) {
-    const int r = 16 * wave + 4 * q + (lane >> 4);
-    const uint8_t* base = wd + (size_t)tl.expert * H * I + (size_t)(blockIdx.y * 64 + r) * I;
+    const int r = 16 * NB * wave + 4 * q + (lane >> 4);
+    const uint8_t* base = wd + (size_t)tl.expert * H * I + (size_t)(cb * kWRows + r) * I;
     wsrc[q] = base + (((lane & 15) ^ (r & 15)) << 4);
   }
-  const float scale_d = sd[(size_t)tl.expert * H + col];
-
-  for (int p = 0; p < tl.rows; p += kLdsRows) {
-    const int nrows = min(kLdsRows, tl.rows - p);
-    int32_t yslot[4];
-    load_y_slots(sorted_slots + tl.row_start + p, nrows, yslot);
-    const int xr = 2 * wave + (lane >> 5);
-    const unsigned char* xsrc =
-        reinterpret_cast<const unsigned char*>(h + (size_t)(tl.row_start + p + min(xr, nrows - 1)) * I) +
-        (((lane & 31) ^ (xr & 15)) << 4);
-    auto issue = [&](int st, int slot) {
-      unsigned char* sl = ring + slot * kSlot;
+  float scale_d[NB];
 #pragma unroll
-      for (int q = 0; q < kWCopies; ++q)
-        lds_copy16(wsrc[q] + (size_t)st * kF8Sk, lds_addr(sl + (16 * wave + 4 * q) * kF8WRow));
-      lds_copy16(xsrc + (size_t)st * kF8Sk * 2, lds_addr(sl + kWBytes + 2 * wave * kF8ARow));
-    };
+  for (int j = 0; j < NB; ++j) scale_d[j] = sd[(size_t)tl.expert * H + col + 16 * j];
+  int32_t yslot[kNF][4];
+  load_y_slots<kNF>(sorted_slots + tl.row_start, nrows, yslot);
+  const unsigned char* xsrc[AC::kCopies];
 #pragma unroll
-    for (int s = 0; s < SLOTS - 1; ++s)
-      if (s < nst) issue(s, s);
-    if (tid == 0) sany = 0;
-    __syncthreads();
-    for (int i = tid; i < nsb; i += 256) {
-      const uint8_t sv = hscale[(size_t)(tl.row_start + p) * nsb + i];
-      ssc[i] = sv;
-      if (sv) sany = 1;
-    }
-    __syncthreads();
-    const bool scaled = sany != 0;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool rv = m < nrows;
-    const int arow = rv ? m : 0;
-    const int brow = wave * 16 + m;
-    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-    int s_acc = 0;  // acc holds y * 2^-s_acc (the activation block consumed last)
-    for (int st = 0; st < nst; ++st) {
-      const int later = min(SLOTS - 2, nst - 1 - st);
-      if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
-      else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopies));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_barrier();
-      if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
-      const unsigned char* sl = ring + (st % SLOTS) * kSlot;
-      const unsigned char* sa = sl + kWBytes;
+  for (int q = 0; q < AC::kCopies; ++q) {
+    const int xr = AC::kPer * wave + 2 * q + (lane >> 5);
+    xsrc[q] = reinterpret_cast<const unsigned char*>(h + (size_t)(tl.row_start + min(xr, nrows - 1)) * I) +
+              (((lane & 31) ^ (xr & 15)) << 4);
+  }
+  auto issue = [&](int st, int slot) {
+    unsigned char* sl = ring + slot * kSlot;
 #pragma unroll
-      for (int j = 0; j < kF8Sk / 64; ++j) {
-        const int cw = 4 * j + (lane >> 4);
-        const u32x4 bq = *reinterpret_cast<const u32x4*>(sl + f8_woff(brow, cw));
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw));
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow, 2 * cw + 1));
-        // the 64 K values of step j share one activation scale block
-        if (scaled) {
-          const int sk = __builtin_amdgcn_readfirstlane(ssc[(st * kF8Sk) / kScaleCols + j]);
-          if (sk != s_acc) {
-            acc = ldexp4(acc, s_acc - sk);
-            s_acc = sk;
-          }
+    for (int q = 0; q < kWCopies; ++q)
+      lds_copy16(wsrc[q] + (size_t)st * kF8Sk, lds_addr(sl + (16 * NB * wave + 4 * q) * kF8WRow));
+#pragma unroll
+    for (int q = 0; q < AC::kCopies; ++q)
+      lds_copy16(xsrc[q] + (size_t)st * kF8Sk * 2, lds_addr(sl + kWBytes + (AC::kPer * wave + 2 * q) * kF8ARow));
+  };
+#pragma unroll
+  for (int s = 0; s < SLOTS - 1; ++s)
+    if (s < nst) issue(s, s);
+  if (tid == 0) sany = 0;
+  __syncthreads();
+  for (int i = tid; i < nsb; i += 256) {
+    const uint8_t sv = hscale[(size_t)tl.row_start * nsb + i];
+    ssc[i] = sv;
+    if (sv) sany = 1;
+  }
+  __syncthreads();
+  const bool scaled = sany != 0;
+  f32x4 acc[NB][kNF];
+  int arow[kNF];
+#pragma unroll
+  for (int f = 0; f < kNF; ++f) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ar = 16 * f + m;
+    arow[f] = ar < R ? ar : 0;
+  }
+  const int brow = wave * 16 * NB + m;  // + 16 j
+  int s_acc = 0;  // acc holds y * 2^-s_acc (the activation block consumed last)
+  for (int st = 0; st < nst; ++st) {
+    wait_stage<kCopies>(min(SLOTS - 2, nst - 1 - st));
+    __builtin_amdgcn_s_barrier();
+    if (st + SLOTS - 1 < nst) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+    const unsigned char* sl = ring + (st % SLOTS) * kSlot;
+    const unsigned char* sa = sl + kWBytes;
+#pragma unroll
+    for (int jk = 0; jk < kF8Sk / 64; ++jk) {
+      const int cw = 4 * jk + (lane >> 4);
+      u32x4 b0[NB], b1[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        fp8x16_to_f16(*reinterpret_cast<const u32x4*>(sl + f8_woff(brow + 16 * j, cw)), b0[j], b1[j]);
+      // the 64 K values of step jk share one activation scale block
+      if (scaled) {
+        const int sk = __builtin_amdgcn_readfirstlane(ssc[(st * kF8Sk) / kScaleCols + jk]);
+        if (sk != s_acc) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int f = 0; f < kNF; ++f) acc[j][f] = ldexp4(acc[j][f], s_acc - sk);
+          s_acc = sk;
         }
-        u32x4 b0, b1;
-        fp8x16_to_f16(bq, b0, b1);
-        acc = mfma16x16x32_f16(rv ? a0 : zero, b0, acc);
-        acc = mfma16x16x32_f16(rv ? a1 : zero, b1, acc);
+      }
+#pragma unroll
+      for (int f = 0; f < kNF; ++f) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow[f], 2 * cw));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sa + f8_aoff(arow[f], 2 * cw + 1));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          acc[j][f] = mfma16x16x32_f16(a0, b0[j], acc[j][f]);
+          acc[j][f] = mfma16x16x32_f16(a1, b1[j], acc[j][f]);
+        }
       }
     }
-    acc = ldexp4(acc, s_acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] *= scale_d;
-    store_y_pass(acc, nrows, yslot, y16, yscale, H, col, smax);
-    __syncthreads();  // every wave is done with the ring and the scales before the next pass
   }
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) {
+      acc[j][f] = ldexp4(acc[j][f], s_acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[j][f][r] *= scale_d[j];
+    }
+  store_y_tile<kNF, NB>(acc, nrows, yslot, y16, yscale, H, cb, col, smax);
 }
 
-// Dynamic LDS the stream kernels may take: 128 KB of a gfx950 CU's 160 KB,
+// Dynamic LDS the stream kernels may take: 152 KB of a gfx950 CU's 160 KB,
 // leaving room for their small static arrays.
-constexpr size_t kStreamLdsMax = 128 * 1024;
+constexpr size_t kStreamLdsMax = 152 * 1024;
 
 // Raises `fn`'s dynamic-LDS limit to kStreamLdsMax, once per device (the
 // attribute is per device; later launches, graph captures included, only launch).
@@ -625,84 +756,144 @@ static hipError_t allow_full_lds(const void* fn, std::atomic<uint64_t>& done) {
   return e;
 }
 
-size_t gateup_stream_lds_bytes() { return (size_t)kSSlots * (128 + kLdsRows) * StageGeom<kSk>::kRowBytes; }
-size_t down_stream_lds_bytes(int I) {
-  return (size_t)kSSlots * (64 + kLdsRows) * StageGeom<kSk>::kRowBytes + I / kScaleCols;
+// Ring depth per tile height: three slots while they fit, else two.
+constexpr int gateup_slots(int R) { return (128 + R) * 256 * 3 <= 144 * 1024 ? 3 : 2; }
+// down workgroups take 128 output columns from 32-row tiles: their activation rows
+// are then read half as often per weight byte
+constexpr int down_nb(int R) { return R >= 32 ? 2 : 1; }
+constexpr int down_slots(int R) { return (64 * down_nb(R) + R) * 256 * 3 <= 144 * 1024 ? 3 : 2; }
+constexpr int gateup_f8_slots(int R) { return R >= 64 ? 2 : 3; }
+constexpr int down_f8_slots(int R) { return (64 * down_nb(R) * kF8WRow + R * kF8ARow) * 3 <= 144 * 1024 ? 3 : 2; }
+
+size_t gateup_stream_lds_bytes(int R) { return (size_t)gateup_slots(R) * (128 + R) * StageGeom<kSk>::kRowBytes; }
+size_t down_stream_lds_bytes(int R, int I) {
+  return (size_t)down_slots(R) * (64 * down_nb(R) + R) * StageGeom<kSk>::kRowBytes + I / kScaleCols;
+}
+size_t gateup_stream_fp8_lds_bytes(int R) { return (size_t)gateup_f8_slots(R) * (128 * kF8WRow + R * kF8ARow); }
+size_t down_stream_fp8_lds_bytes(int R, int I) {
+  return (size_t)down_f8_slots(R) * (64 * down_nb(R) * kF8WRow + R * kF8ARow) + I / kScaleCols;
 }
 
-// Whether the stream kernels can run at this shape: K of both projections in
-// whole stages, and the staged rows and the down kernel's scales fit in LDS.
-bool stream_fits(int H, int I) {
-  return H % kSk == 0 && I % kSk == 0 && gateup_stream_lds_bytes() <= kStreamLdsMax &&
-         down_stream_lds_bytes(I) <= kStreamLdsMax;
+// Tile heights the stream kernels are built for.  Wider tiles (128 rows) were
+// measured slower than the grouped GEMMs at the batches that would use them
+// (T = 2048 at Beam dims: 5.1 against 4.4 ms).
+bool stream_rows_ok(int R, bool) { return R == 8 || R == 16 || R == 32 || R == 64; }
+
+// Whether the stream kernels with tiles of R rows can run at this shape: K of
+// both projections in whole stages, and the staged rows and the down kernel's
+// scales fit in LDS.
+bool stream_fits(int H, int I, int R) {
+  return stream_rows_ok(R, false) && H % kSk == 0 && I % kSk == 0 && H % (64 * down_nb(R)) == 0 &&
+         gateup_stream_lds_bytes(R) <= kStreamLdsMax && down_stream_lds_bytes(R, I) <= kStreamLdsMax;
 }
 
-size_t gateup_stream_fp8_lds_bytes() { return (size_t)kF8Slots * (128 * kF8WRow + kLdsRows * kF8ARow); }
-size_t down_stream_fp8_lds_bytes(int I) {
-  return (size_t)kF8Slots * (64 * kF8WRow + kLdsRows * kF8ARow) + I / kScaleCols;
+bool stream_fp8_fits(int H, int I, int R) {
+  return stream_rows_ok(R, true) && H % kF8Sk == 0 && I % kF8Sk == 0 && H % (64 * down_nb(R)) == 0 &&
+         gateup_stream_fp8_lds_bytes(R) <= kStreamLdsMax && down_stream_fp8_lds_bytes(R, I) <= kStreamLdsMax;
 }
 
-// Whether the FP8 stream kernels can run at this shape: K of both projections
-// in whole 256-value stages, and the staged rows and scales fit in LDS.
-bool stream_fp8_fits(int H, int I) {
-  return H % kF8Sk == 0 && I % kF8Sk == 0 && gateup_stream_fp8_lds_bytes() <= kStreamLdsMax &&
-         down_stream_fp8_lds_bytes(I) <= kStreamLdsMax;
+template <int R>
+static hipError_t gateup_fp8_r(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                               int max_tiles, const uint8_t* wg, const uint8_t* wu, const float* sg, const float* su,
+                               uint16_t* h, uint8_t* hscale, int H, int I, int K, hipStream_t st) {
+  constexpr int S = gateup_f8_slots(R);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<S, R>), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gateup_stream_fp8_kernel<S, R>), dim3(max_tiles * (I / 64)), dim3(256),
+                     gateup_stream_fp8_lds_bytes(R), st, x, slots, tiles, ntiles, wg, wu, sg, su, h, hscale, H, I, K);
+  return hipGetLastError();
 }
 
+template <int R>
+static hipError_t down_fp8_r(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                             const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd, uint16_t* y16,
+                             uint8_t* yscale, int H, int I, hipStream_t st) {
+  constexpr int S = down_f8_slots(R), NB = down_nb(R);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_fp8_kernel<S, R, NB>), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((down_stream_fp8_kernel<S, R, NB>), dim3(max_tiles * (H / (64 * NB))), dim3(256),
+                     down_stream_fp8_lds_bytes(R, I), st, h, hscale, slots, tiles, ntiles, wd, sd, y16, yscale, H, I);
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t gateup_r(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                           int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale, int H,
+                           int I, int K, hipStream_t st) {
+  constexpr int S = gateup_slots(R);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<S, kSk, R>), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gateup_stream_lds_kernel<S, kSk, R>), dim3(max_tiles * (I / 64)), dim3(256),
+                     gateup_stream_lds_bytes(R), st, x, slots, tiles, ntiles, wg, wu, h, hscale, H, I, K);
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t down_r(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                         const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16, uint8_t* yscale,
+                         int H, int I, hipStream_t st) {
+  constexpr int S = down_slots(R), NB = down_nb(R);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_lds_kernel<S, kSk, R, NB>), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((down_stream_lds_kernel<S, kSk, R, NB>), dim3(max_tiles * (H / (64 * NB))), dim3(256),
+                     down_stream_lds_bytes(R, I), st, h, hscale, slots, tiles, ntiles, wd, y16, yscale, H, I);
+  return hipGetLastError();
+}
+
+// Launchers of the stream path (tiles of at most R rows from the dispatch; require
+// stream_fits / stream_fp8_fits).  Gate/up and down run on the same tile table: the
+// down kernel reads one activation scale per (tile, 64 columns).
 hipError_t launch_gateup_stream_fp8(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                                    int max_tiles, const uint8_t* wg, const uint8_t* wu, const float* sg,
+                                    int max_tiles, int R, const uint8_t* wg, const uint8_t* wu, const float* sg,
                                     const float* su, uint16_t* h, uint8_t* hscale, int H, int I, int K,
                                     hipStream_t st) {
-  dim3 grid(max_tiles, I / 64);
-  const size_t bytes = gateup_stream_fp8_lds_bytes();
-  static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<kF8Slots>), lds_set);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gateup_stream_fp8_kernel<kF8Slots>), grid, dim3(256), bytes, st, x, slots, tiles, ntiles, wg,
-                     wu, sg, su, h, hscale, H, I, K);
-  return hipGetLastError();
+  switch (R) {
+    case 8: return gateup_fp8_r<8>(x, slots, tiles, ntiles, max_tiles, wg, wu, sg, su, h, hscale, H, I, K, st);
+    case 16: return gateup_fp8_r<16>(x, slots, tiles, ntiles, max_tiles, wg, wu, sg, su, h, hscale, H, I, K, st);
+    case 32: return gateup_fp8_r<32>(x, slots, tiles, ntiles, max_tiles, wg, wu, sg, su, h, hscale, H, I, K, st);
+    case 64: return gateup_fp8_r<64>(x, slots, tiles, ntiles, max_tiles, wg, wu, sg, su, h, hscale, H, I, K, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_down_stream_fp8(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                                  const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd,
+                                  const int32_t* ntiles, int max_tiles, int R, const uint8_t* wd, const float* sd,
                                   uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st) {
-  dim3 grid(max_tiles, H / 64);
-  const size_t bytes = down_stream_fp8_lds_bytes(I);
-  static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_fp8_kernel<kF8Slots>), lds_set);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_stream_fp8_kernel<kF8Slots>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
-                     ntiles, wd, sd, y16, yscale, H, I);
-  return hipGetLastError();
+  switch (R) {
+    case 8: return down_fp8_r<8>(h, hscale, slots, tiles, ntiles, max_tiles, wd, sd, y16, yscale, H, I, st);
+    case 16: return down_fp8_r<16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, sd, y16, yscale, H, I, st);
+    case 32: return down_fp8_r<32>(h, hscale, slots, tiles, ntiles, max_tiles, wd, sd, y16, yscale, H, I, st);
+    case 64: return down_fp8_r<64>(h, hscale, slots, tiles, ntiles, max_tiles, wd, sd, y16, yscale, H, I, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-// Launchers of the stream path (passes of kLdsRows rows; requires stream_fits).
-// Gate/up and down run together: the down kernel reads one activation scale per
-// pass of gate/up.
 hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
-                                int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
-                                int H, int I, int K, hipStream_t st) {
-  dim3 grid(max_tiles, I / 64);  // I % 64 == 0
-  const size_t bytes = gateup_stream_lds_bytes();
-  static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<kSSlots, kSk>), lds_set);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gateup_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, x, slots, tiles, ntiles,
-                     wg, wu, h, hscale, H, I, K);
-  return hipGetLastError();
+                                int max_tiles, int R, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
+                                uint8_t* hscale, int H, int I, int K, hipStream_t st) {
+  switch (R) {
+    case 8: return gateup_r<8>(x, slots, tiles, ntiles, max_tiles, wg, wu, h, hscale, H, I, K, st);
+    case 16: return gateup_r<16>(x, slots, tiles, ntiles, max_tiles, wg, wu, h, hscale, H, I, K, st);
+    case 32: return gateup_r<32>(x, slots, tiles, ntiles, max_tiles, wg, wu, h, hscale, H, I, K, st);
+    case 64: return gateup_r<64>(x, slots, tiles, ntiles, max_tiles, wg, wu, h, hscale, H, I, K, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                              const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16,
+                              const int32_t* ntiles, int max_tiles, int R, const uint16_t* wd, uint16_t* y16,
                               uint8_t* yscale, int H, int I, hipStream_t st) {
-  dim3 grid(max_tiles, H / 64);  // H % 64 == 0
-  const size_t bytes = down_stream_lds_bytes(I);
-  static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_lds_kernel<kSSlots, kSk>), lds_set);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_stream_lds_kernel<kSSlots, kSk>), grid, dim3(256), bytes, st, h, hscale, slots, tiles,
-                     ntiles, wd, y16, yscale, H, I);
-  return hipGetLastError();
+  switch (R) {
+    case 8: return down_r<8>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+    case 16: return down_r<16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+    case 32: return down_r<32>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+    case 64: return down_r<64>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // ---------------------------------------------------------------------------

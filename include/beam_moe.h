@@ -271,6 +271,15 @@ int beam_moe_timing_enable(int enable);
 int beam_moe_timing_read(float* stage_ms, int32_t max_stages, int32_t* n_stages, int32_t* calls);
 const char* beam_moe_stage_name(int32_t stage);
 
+/* Diagnostics: which expert kernels the forward entry points run for T tokens.
+ * Returns R > 0 when they take the stream kernels on tiles of at most R rows of
+ * one expert (8, 16, 32 or 64: the smallest at least twice the average rows per
+ * expert, T * topk / num_experts), 0 when they take the grouped GEMMs (256-row
+ * tiles; from 32 average rows per expert, or where the stream kernels do not
+ * fit the shape), or a negative status for invalid or unsupported dims.
+ * fp8 != 0 asks about beam_moe_forward_fp8. */
+int beam_moe_stream_rows(const beam_moe_dims* dims, int32_t T, int fp8);
+
 /* Static string for a status code. */
 const char* beam_moe_status_str(int status);
 

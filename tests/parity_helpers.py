@@ -265,52 +265,57 @@ def residual_parity(p: Problem, stream: torch.Tensor, step: int, bufs, tokens=No
 # token samples at large batch sizes, chosen from the dispatch result
 # --------------------------------------------------------------------------
 TILE_ROWS = 256     # rows of a grouped-GEMM tile
-LEVEL_ROWS = 64     # rows of one row level of a tile
-MERGE_ROWS = 64     # a last tile of at most this many rows joins the tile before it
+LEVEL_ROWS = 64     # rows of one row level of a grouped-GEMM tile
+MERGE_ROWS = 64     # a last grouped-GEMM tile of at most this many rows joins the tile before it
 
 
-def tile_samples(counts, offsets, slots, topk, per_kind=2):
-    """Tokens whose routed rows fall in each part of the grouped GEMMs' tiling.
+def tile_samples(counts, offsets, slots, topk, per_kind=2, stream_rows=0):
+    """Tokens whose routed rows fall in each part of the expert kernels' tiling.
 
-    An expert's rows (expert-sorted order) are cut into tiles of 256 rows; a
-    last tile of at most 64 rows is merged into the tile before it as a fifth
-    64-row level.  Returns [(label, token)]: rows in each of the four row levels
-    of a full tile, the fifth level of merged tiles (its first and last row),
-    the last row of partial tiles, the first and last row of the hottest
-    expert and of its last tile, and the last row of a one-level expert."""
+    Grouped GEMMs (stream_rows = 0): an expert's rows (expert-sorted order) are
+    cut into tiles of 256 rows, and a last tile of at most 64 rows is merged into
+    the tile before it as a fifth 64-row level.  Stream kernels (stream_rows = R):
+    tiles of at most R rows, in 16-row fragments, nothing merged.  Returns
+    [(label, token)]: rows in each level (fragment) of a full tile, the fifth
+    level of merged tiles (its first and last row), the last row of partial
+    tiles, the first and last row of the hottest expert and of its last tile, and
+    the last row of an expert with very few rows."""
     counts = np.asarray(counts)
     offsets = np.asarray(offsets)
     slots = np.asarray(slots)
+    tile = stream_rows or TILE_ROWS
+    level = 16 if stream_rows else LEVEL_ROWS
+    merge = 0 if stream_rows else MERGE_ROWS
     out = []
 
     def add(label, e, r):
         out.append((label, int(slots[offsets[e] + r]) // topk))
 
     order = np.argsort(-counts, kind="stable")
-    full = [e for e in order if counts[e] >= TILE_ROWS]
+    full = [e for e in order if counts[e] >= tile]
     for e in full[:1]:
-        for lev in range(TILE_ROWS // LEVEL_ROWS):
-            add(f"expert {e} ({counts[e]} rows) tile 0 level {lev}", e, lev * LEVEL_ROWS + (17 * lev + 5) % 64)
-    merged = [e for e in order if counts[e] > TILE_ROWS and 0 < counts[e] % TILE_ROWS <= MERGE_ROWS]
+        for lev in range(tile // level):
+            add(f"expert {e} ({counts[e]} rows) tile 0 level {lev}", e, lev * level + (17 * lev + 5) % level)
+    merged = [e for e in order if merge and counts[e] > tile and 0 < counts[e] % tile <= merge]
     for e in merged[:per_kind]:
         c = int(counts[e])
-        first5 = c - c % TILE_ROWS
+        first5 = c - c % tile
         add(f"expert {e} ({c} rows) merged fifth level, first row", e, first5)
         add(f"expert {e} ({c} rows) merged fifth level, last row", e, c - 1)
-    partial = [e for e in order if counts[e] % TILE_ROWS > MERGE_ROWS]
+    partial = [e for e in order if counts[e] % tile > merge]
     for e in partial[:per_kind]:
         c = int(counts[e])
-        add(f"expert {e} ({c} rows) partial last tile ({c % TILE_ROWS} rows), last row", e, c - 1)
+        add(f"expert {e} ({c} rows) partial last tile ({c % tile} rows), last row", e, c - 1)
     if counts.max() > 0:
         e = int(order[0])
         c = int(counts[e])
         add(f"hottest expert {e} ({c} rows), first row", e, 0)
-        last_tile = (c - 1) // TILE_ROWS * TILE_ROWS
-        if c > TILE_ROWS and c % TILE_ROWS and c % TILE_ROWS <= MERGE_ROWS:
-            last_tile -= TILE_ROWS
+        last_tile = (c - 1) // tile * tile
+        if merge and c > tile and c % tile and c % tile <= merge:
+            last_tile -= tile
         add(f"hottest expert {e} ({c} rows), first row of its last tile", e, last_tile)
         add(f"hottest expert {e} ({c} rows), last row", e, c - 1)
-    small = [e for e in order[::-1] if 0 < counts[e] <= LEVEL_ROWS]
+    small = [e for e in order[::-1] if 0 < counts[e] <= min(level, tile)]
     for e in small[:1]:
         add(f"expert {e} ({counts[e]} rows, one level), last row", e, int(counts[e]) - 1)
     return out

@@ -75,6 +75,19 @@ def test_route_and_dispatch_workspace_sizes(T):
         assert route == T * E * 4 and route * 100 < full
 
 
+def test_stream_rows_rule():
+    """The expert path the library reports: stream tiles of R rows (the smallest of 8 .. 64 at
+    least twice the average rows per expert), else 0."""
+    got = {T: (binding.beam_moe_stream_rows(BEAM, T), binding.beam_moe_stream_rows(BEAM, T, True))
+           for T in (1, 64, 128, 129, 256, 257, 512, 1024, 1025, 2048, 2049, 16384)}
+    assert got == {1: (8, 8), 64: (8, 8), 128: (8, 8), 129: (16, 16), 256: (16, 16), 257: (32, 32), 512: (32, 32),
+                   1024: (64, 64), 1025: (0, 0), 2048: (0, 0), 2049: (0, 0), 16384: (0, 0)}
+    lib = binding.load_library()
+    bad = binding._cdims(Dims(5120, 2560, 256, 7, 4, 8))
+    assert lib.beam_moe_stream_rows(ctypes.byref(bad), 64, 0) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert lib.beam_moe_stream_rows(ctypes.byref(binding._cdims(BEAM)), -1, 0) == binding.BEAM_MOE_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("K", [1, 8])
 def test_routed_pair_limit(K):
     """T * K <= 2^28 is accepted; one token more is UNSUPPORTED before any pointer is read."""

@@ -201,40 +201,65 @@ def test_route_end_to_end(name, T):
 # --------------------------------------------------------------------------
 # whole block
 # --------------------------------------------------------------------------
+# Each case names the expert path it covers: R > 0 for the stream kernels on tiles of at most R
+# rows (the smallest of 8 .. 128 at least twice the average rows per expert), 0 for the grouped
+# GEMMs (more than 64 average rows per expert); the library's choice is asserted first.
 MID = {
-    # stream path (at most 4 rows per expert on average), several column blocks,
-    # experts with more than one 8-row pass
-    "mid_stream": (synth.Workload("mid_stream", 40, synth.Dims(512, 384, 64, 8, 4, 6), router_sigma=0.06), None),
+    # stream path, 8-row tiles, several column blocks; experts with more than one tile
+    "mid_stream": (synth.Workload("mid_stream", 40, synth.Dims(512, 384, 64, 8, 4, 6), router_sigma=0.06), 8),
     # grouped path, 16 experts, ~225 rows each: full and ragged 256-row tiles
-    "mid_tiled": (synth.Workload("mid_tiled", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06), None),
-    # grouped path with Beam's expert count: one partial tile per expert
-    "mid_tiled_e256": (synth.Workload("mid_tiled_e256", 1100, synth.Dims(768, 256, 256, 8, 4, 8), router_sigma=0.04),
-                       None),
-    # stream path with skewed bias: some experts get more than 16 rows (several passes)
+    "mid_tiled": (synth.Workload("mid_tiled", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06), 0),
+    # grouped path with Beam's expert count: one partial tile (about 69 rows, two levels) per expert
+    "mid_tiled_e256": (synth.Workload("mid_tiled_e256", 2200, synth.Dims(768, 256, 256, 8, 4, 8), router_sigma=0.04),
+                       0),
+    # stream path with skewed bias: some experts get several 8-row tiles
     "mid_stream_skew": (synth.Workload("mid_stream_skew", 60, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
-                                       zipf_s=1.2), None),
+                                       zipf_s=1.2), 8),
     # stream path, I/32 not a multiple of 8
     "mid_stream_i384": (synth.Workload("mid_stream_i384", 40, synth.Dims(512, 384, 64, 8, 4, 4),
-                                       router_sigma=0.06), None),
+                                       router_sigma=0.06), 8),
     # large activations (expert weights N(0, 10^2)): the SwiGLU activations and the expert
     # outputs exceed 2^15 and travel to the next step with a power-of-two scale
     "mid_stream_big": (synth.Workload("mid_stream_big", 40, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
-                                      expert_sigma=10.0), None),
+                                      expert_sigma=10.0), 8),
     "mid_tiled_big": (synth.Workload("mid_tiled_big", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06,
-                                     expert_sigma=10.0), None),
+                                     expert_sigma=10.0), 0),
     # huge activations (expert weights N(0, 200^2)): SwiGLU activations near 2^24 and expert
     # outputs near 2^36, so h and y carry scales 2^-s with s >= 9.  The down projection keeps
     # its accumulators in units of 2^s and never scales its weights: weights times 2^s would
     # pass fp16's 65504 here
     "mid_stream_huge": (synth.Workload("mid_stream_huge", 40, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
-                                       expert_sigma=200.0), None),
+                                       expert_sigma=200.0), 8),
     "mid_tiled_huge": (synth.Workload("mid_tiled_huge", 900, synth.Dims(512, 384, 16, 4, 2, 4), router_sigma=0.06,
-                                      expert_sigma=200.0), None),
-    # grouped path just above the stream threshold (about 9 rows per expert) with skew:
-    # mostly near-empty tiles, whose idle waves copy no activations
-    "mid_grouped_skew": (synth.Workload("mid_grouped_skew", 150, synth.Dims(512, 256, 64, 8, 4, 4),
-                                        router_sigma=0.06, zipf_s=1.2), None),
+                                      expert_sigma=200.0), 0),
+    # grouped path with skew (75 rows per expert on average): hot experts with several tiles,
+    # many nearly empty tiles, whose idle waves copy no activations
+    "mid_grouped_skew": (synth.Workload("mid_grouped_skew", 1200, synth.Dims(512, 256, 64, 8, 4, 4),
+                                        router_sigma=0.06, zipf_s=1.2), 0),
+    # stream path on every wider tile: 16, 32 and 64 rows (one to four row fragments per wave;
+    # the down kernel with two column fragments per wave from 32 rows), partial tiles, and skewed
+    # batches whose hot experts take several tiles
+    "mid_stream_r16": (synth.Workload("mid_stream_r16", 100, synth.Dims(512, 384, 64, 8, 4, 4), router_sigma=0.06),
+                       16),
+    "mid_stream_r32": (synth.Workload("mid_stream_r32", 200, synth.Dims(512, 384, 64, 8, 4, 4), router_sigma=0.06),
+                       32),
+    "mid_stream_r32_skew": (synth.Workload("mid_stream_r32_skew", 200, synth.Dims(512, 384, 64, 8, 4, 4),
+                                           router_sigma=0.06, zipf_s=1.2), 32),
+    "mid_stream_r64": (synth.Workload("mid_stream_r64", 400, synth.Dims(512, 384, 64, 8, 4, 4), router_sigma=0.06),
+                       64),
+    "mid_stream_r64_skew": (synth.Workload("mid_stream_r64_skew", 400, synth.Dims(512, 384, 64, 8, 4, 4),
+                                           router_sigma=0.06, zipf_s=1.2), 64),
+    # just past the stream path (50 rows per expert on average): grouped GEMMs, one partial tile each
+    "mid_grouped_r50": (synth.Workload("mid_grouped_r50", 800, synth.Dims(512, 384, 64, 8, 4, 4),
+                                       router_sigma=0.06), 0),
+    "mid_stream_r64_big": (synth.Workload("mid_stream_r64_big", 400, synth.Dims(512, 256, 64, 8, 4, 4),
+                                          router_sigma=0.06, expert_sigma=10.0), 64),
 }
+
+
+def _expect_path(wl, rows, fp8=False):
+    got = binding.beam_moe_stream_rows(wl.dims, wl.tokens, fp8)
+    assert got == rows, f"{wl.name}: the library takes {got} (0 = grouped GEMMs), the case covers {rows}"
 
 
 def test_forward_tiny():
@@ -248,7 +273,8 @@ def test_forward_tiny():
 @pytest.mark.parametrize("name", list(MID))
 def test_forward_mid(name):
     _announce(f"forward {name} (all tokens)")
-    wl, _ = MID[name]
+    wl, rows = MID[name]
+    _expect_path(wl, rows)
     p = Problem(wl, DEV)
     bufs = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
     excluded, worst = forward_parity(p, bufs)
@@ -262,11 +288,14 @@ def _beam_forward(name, beam_experts, sample):
     return _beam_forward_wl(synth.WORKLOADS[name], beam_experts, sample)
 
 
-def _samples(bufs, K, fixed):
-    """Fixed tokens plus tokens whose routed rows land in each part of the grouped GEMMs'
+def _samples(p, bufs, fixed):
+    """Fixed tokens plus tokens whose routed rows land in each part of the expert kernels'
     tiling (row levels, merged fifth levels, partial tiles, the hottest expert), chosen
-    from this run's dispatch; prints which."""
-    picks = tile_samples(bufs.counts.cpu().numpy(), bufs.offsets.cpu().numpy(), bufs.slots.cpu().numpy(), K)
+    from this run's dispatch and the path the library takes; prints which."""
+    rows = binding.beam_moe_stream_rows(p.dims, p.x.shape[0], p.fp8)
+    print(f"    expert path: {'stream kernels, tiles of %d rows' % rows if rows else 'grouped GEMMs'}", flush=True)
+    picks = tile_samples(bufs.counts.cpu().numpy(), bufs.offsets.cpu().numpy(), bufs.slots.cpu().numpy(),
+                         p.dims.topk, stream_rows=rows)
     print_samples(picks)
     return sorted(set(int(t) for t in fixed) | {t for _, t in picks})
 
@@ -278,7 +307,7 @@ def _beam_forward_wl(wl, beam_experts, sample):
     torch.cuda.synchronize()
     T = wl.tokens
     if isinstance(sample, str):
-        sample = _samples(bufs, p.dims.topk, (0, T // 2, T - 1))
+        sample = _samples(p, bufs, (0, T // 2, T - 1))
     excluded, worst = forward_parity(p, bufs, sample)
     print(f"  worst error / tolerance {worst:.3f}")
     out1 = bufs.out.clone()
@@ -310,7 +339,7 @@ def test_forward_skewed(beam_experts):
 # stream kernels (T = 128: several experts with more than one 8-row pass); from
 # T = 160 the grouped GEMMs, first with nearly empty tiles, then partial ones;
 # T = 32768, twice the prefill batch: about 1024 rows, four tiles, per expert.
-@pytest.mark.parametrize("T", [1, 8, 128, 160, 256, 512, 1024, 2048, 32768])
+@pytest.mark.parametrize("T", [1, 8, 128, 160, 256, 512, 1024, 2048, 4096, 32768])
 def test_forward_beam_sizes(beam_experts, T):
     _announce(f"forward Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
@@ -342,7 +371,7 @@ EDGE = {
                                        expert_sigma=10.0),
     # the largest top-k, on both paths
     "topk16_stream": synth.Workload("topk16_stream", 16, synth.Dims(256, 128, 64, 8, 8, 16), router_sigma=0.06),
-    "topk16_grouped": synth.Workload("topk16_grouped", 200, synth.Dims(256, 128, 64, 8, 8, 16), router_sigma=0.06),
+    "topk16_grouped": synth.Workload("topk16_grouped", 300, synth.Dims(256, 128, 64, 8, 8, 16), router_sigma=0.06),
     # no grouping (one group), every group kept (plain top-k), one expert per group
     "one_group": synth.Workload("one_group", 24, synth.Dims(256, 128, 64, 1, 1, 8), router_sigma=0.06),
     "all_groups": synth.Workload("all_groups", 24, synth.Dims(256, 128, 64, 8, 8, 8), router_sigma=0.06),
@@ -472,10 +501,11 @@ def test_residual_tiny(step, weights):
     print(f"  worst error / tolerance {worst:.3f}")
 
 
-@pytest.mark.parametrize("name", ["mid_stream", "mid_tiled", "mid_stream_skew"])
+@pytest.mark.parametrize("name", ["mid_stream", "mid_tiled", "mid_stream_skew", "mid_stream_r64"])
 def test_residual_mid(name):
     _announce(f"residual {name} (all tokens)")
-    wl, _ = MID[name]
+    wl, rows = MID[name]
+    _expect_path(wl, rows)
     p, stream, g_in, g_out, bufs = _residual_case(wl, 4, True)
     excluded, worst = residual_parity(p, stream, 4, bufs, g_in=g_in, g_out=g_out)
     print(f"  worst error / tolerance {worst:.3f}")
@@ -509,7 +539,7 @@ def test_residual_beam(beam_experts, name, T):
     wl = synth.with_tokens(synth.WORKLOADS[name], T)
     p, stream, g_in, g_out, bufs = _residual_case(wl, 3, True, experts=beam_experts)
     fixed = [t for t in (0, 1, 2, 3, T // 2, T - 1) if t < T]
-    sample = None if T <= 64 else _samples(bufs, p.dims.topk, fixed)
+    sample = None if T <= 64 else _samples(p, bufs, fixed)
     excluded, worst = residual_parity(p, stream, 3, bufs, sample, g_in=g_in, g_out=g_out)
     print(f"  worst error / tolerance {worst:.3f}")
 
@@ -540,8 +570,18 @@ FP8 = {
     "f8_grouped": synth.Workload("f8_grouped", 300, synth.Dims(512, 256, 16, 4, 2, 4), router_sigma=0.06),
     "f8_grouped_e256": synth.Workload("f8_grouped_e256", 1100, synth.Dims(768, 256, 256, 8, 4, 8),
                                       router_sigma=0.04),
-    "f8_grouped_skew": synth.Workload("f8_grouped_skew", 150, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
+    "f8_grouped_skew": synth.Workload("f8_grouped_skew", 1200, synth.Dims(512, 256, 64, 8, 4, 4), router_sigma=0.06,
                                       zipf_s=1.2),
+    # FP8 stream kernels on wider tiles (16, 32, 64 rows), with skew at 32 and 64
+    "f8_stream_r16": synth.Workload("f8_stream_r16", 100, synth.Dims(512, 512, 64, 8, 4, 4), router_sigma=0.06),
+    "f8_stream_r32": synth.Workload("f8_stream_r32", 200, synth.Dims(512, 512, 64, 8, 4, 4), router_sigma=0.06),
+    "f8_stream_r32_skew": synth.Workload("f8_stream_r32_skew", 200, synth.Dims(512, 512, 64, 8, 4, 4),
+                                         router_sigma=0.06, zipf_s=1.2),
+    "f8_stream_r64": synth.Workload("f8_stream_r64", 400, synth.Dims(512, 512, 64, 8, 4, 4), router_sigma=0.06),
+    "f8_stream_r64_skew": synth.Workload("f8_stream_r64_skew", 400, synth.Dims(512, 512, 64, 8, 4, 4),
+                                         router_sigma=0.06, zipf_s=1.2),
+    "f8_stream_r64_huge": synth.Workload("f8_stream_r64_huge", 400, synth.Dims(512, 512, 64, 8, 4, 4),
+                                         router_sigma=0.06, expert_sigma=200.0),
     "f8_grouped_big": synth.Workload("f8_grouped_big", 900, synth.Dims(512, 512, 16, 4, 2, 4), router_sigma=0.06,
                                      expert_sigma=10.0),
     # huge activations (near 2^24, scales 2^-s with s >= 9): E4M3 values up to 448 times 2^s would
@@ -558,9 +598,17 @@ FP8 = {
 }
 
 
+# the expert path each FP8 case covers (R of the stream tiles, or 0 for the grouped GEMMs)
+FP8_PATH = {"f8_small": 8, "f8_stream": 8, "f8_skew": 8, "f8_big": 8, "f8_huge": 8, "f8_grouped": 0,
+            "f8_grouped_e256": 0, "f8_grouped_skew": 0, "f8_grouped_big": 0, "f8_grouped_huge": 0,
+            "f8_stream_r16": 16, "f8_stream_r32": 32, "f8_stream_r32_skew": 32, "f8_stream_r64": 64,
+            "f8_stream_r64_skew": 64, "f8_stream_r64_huge": 64, "f8_dense_merged_big": 0, "f8_merged_tails_big": 0}
+
+
 @pytest.mark.parametrize("name", list(FP8))
 def test_forward_fp8(name):
     _announce(f"forward fp8 {name} (all tokens)")
+    _expect_path(FP8[name], FP8_PATH[name], fp8=True)
     p = Problem(FP8[name], DEV, fp8=True)
     bufs = binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q)
     excluded, worst = forward_parity(p, bufs)
@@ -596,7 +644,7 @@ def test_forward_fp8_rejects_unsupported_intermediate():
     assert ei.value.status == binding.BEAM_MOE_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("T", [1, 64, 512, 2048, 16384])
+@pytest.mark.parametrize("T", [1, 64, 256, 512, 1024, 2048, 16384])
 def test_forward_fp8_beam(beam_experts_fp8, T):
     _announce(f"forward fp8 Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
@@ -604,7 +652,7 @@ def test_forward_fp8_beam(beam_experts_fp8, T):
     bufs = binding.beam_moe_forward_fp8(p.dims, p.x, p.wr, p.bias, *p.q)
     torch.cuda.synchronize()
     # every token of the decode batch and below; tile-aware samples of larger batches
-    sample = None if T <= 64 else _samples(bufs, p.dims.topk, (0, 1, T // 3, T // 2, T - 1))
+    sample = None if T <= 64 else _samples(p, bufs, (0, 1, T // 3, T // 2, T - 1))
     excluded, worst = forward_parity(p, bufs, sample)
     print(f"  worst error / tolerance {worst:.3f}")
     out1 = bufs.out.clone()
@@ -645,8 +693,8 @@ def test_residual_fp8_beam(beam_experts_fp8):
 # graph capture: every call is stream-ordered and allocation-free, so a captured
 # forward replays to the eager bits (outputs overwritten by eager work in between)
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("name,fp8", [("mid_stream", False), ("mid_tiled", False), ("f8_stream", True),
-                                      ("f8_grouped", True)])
+@pytest.mark.parametrize("name,fp8", [("mid_stream", False), ("mid_tiled", False), ("mid_stream_r64", False),
+                                      ("f8_stream", True), ("f8_grouped", True), ("f8_stream_r32", True)])
 def test_forward_graph_replay(name, fp8):
     _announce(f"graph replay {name}")
     wl = FP8[name] if fp8 else MID[name][0]

@@ -152,3 +152,16 @@ def test_fp8_lookup_equals_the_oracle_decode():
     args[0][0, :4] = [0x7E, 0xFE, 0x01, 0x80]  # 448, -448, the smallest subnormal, -0
     for a, b in zip(fp8_expert_lookup(*args), orc.fp8_expert(*args)):
         assert np.array_equal(a, b)
+
+
+def test_tile_samples_on_stream_tiles():
+    K, R = 8, 32
+    counts = np.array([100, 7, 64, 0, 33], dtype=np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    slots = np.arange(int(offsets[-1]), dtype=np.int32)   # token of row r of expert e: (offsets[e] + r) // K
+    got = dict((lab, t) for lab, t in tile_samples(counts, offsets, slots, K, stream_rows=R))
+    assert not any("merged" in lab for lab in got)        # the stream path merges nothing
+    assert got["hottest expert 0 (100 rows), first row of its last tile"] == (0 + 96) // K
+    assert got["expert 0 (100 rows) partial last tile (4 rows), last row"] == 99 // K
+    assert sum("tile 0 level" in lab for lab in got) == R // 16
+    assert got["expert 1 (7 rows, one level), last row"] == (100 + 6) // K
