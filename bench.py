@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import os
 import sys
 import time
@@ -47,8 +48,10 @@ KERNEL_SOURCES = ["grouped_top_routing_fp32_amd/csrc/" + f
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read, 1 GiB written
 # Workloads of the counter runs behind TRAFFIC_FILE: one per gate/up kernel.
 TRAFFIC_WORKLOADS = "decode,prefill,decode_fp8,prefill_fp8"
-GATE_UP_KERNELS = {"decode": "gateup_stream_lds_kernel", "prefill": "grouped_gemm_kernel<true, false>",
-                   "decode_fp8": "gateup_stream_fp8_kernel", "prefill_fp8": "grouped_gemm_kernel<true, true>"}
+# Workloads of the kernel-trace run behind the kernel-time profile.
+TRACE_WORKLOADS = "decode,prefill,prefill_packed,decode_fp8,prefill_fp8"
+GATE_UP_KERNELS = {"decode": "gateup_stream_lds_kernel", "prefill": "grouped_gemm_kernel<true, false",
+                   "decode_fp8": "gateup_stream_fp8_kernel", "prefill_fp8": "grouped_gemm_kernel<true, true"}
 
 
 def parse():
@@ -56,7 +59,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode,prefill,decode_fp8,prefill_fp8,skewed,router_dispatch")
+    ap.add_argument("--workloads",
+                    default="decode,prefill,prefill_packed,decode_fp8,prefill_fp8,skewed,router_dispatch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-residual", action="store_true",
                     help="skip timing the residual-sublayer entry point on the same batches")
@@ -208,8 +212,11 @@ def summarize_trace(trace_dir, out_md):
 
     def kind(c):
         names = " ".join(r["Kernel_Name"] for r in c)
-        fp8 = "_fp8_kernel" in names or ", true>" in names
-        wl = ("prefill" if "grouped_gemm" in names else "decode") + ("_fp8" if fp8 else "")
+        fp8 = "_fp8_kernel" in names or "grouped_gemm_kernel<true, true" in names
+        # W_down packed to fp16: the down kernels' last template argument is true
+        packed = bool(re.search(r"(grouped_gemm_kernel<false, false|down_stream_lds_kernel<[^>]*), true>", names))
+        wl = ("prefill" if "grouped_gemm" in names else "decode") + ("_fp8" if fp8 else "") + \
+            ("_packed" if packed else "")
         return wl + (", residual sublayer" if "prenorm_kernel" in names else "")
 
     per = {}
@@ -222,13 +229,14 @@ def summarize_trace(trace_dir, out_md):
            "", "Command (repository root on the GPU host):", "", "```",
            "cd /tmp && export TMPDIR=/tmp",
            "rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- \\",
-           f"    python3 $REPO/bench.py --workloads {TRAFFIC_WORKLOADS} --steps 10 --warmup 2 --no-cpu-baseline",
+           f"    python3 $REPO/bench.py --workloads {TRACE_WORKLOADS} --steps 10 --warmup 2 --no-cpu-baseline",
            "python3 bench.py --summarize-trace <TRACE_DIR> <this file>", "```", "",
            "Calls are cut before each router_logits_kernel dispatch (before the prenorm_kernel of a",
            "residual-sublayer call); calls that ran the grouped GEMM are prefill, the others decode, with",
-           "the suffix _fp8 where the FP8 kernels ran.  Warmup and timed calls, with and without the stage",
+           "the suffix _fp8 where the FP8 kernels ran and _packed where the down kernel took W_down packed",
+           "to fp16 (beam_moe_forward_packed).  Warmup and timed calls, with and without the stage",
            "markers, are all counted.  Durations are the dispatch end minus start timestamps.", ""]
-    order = ["decode", "prefill", "decode_fp8", "prefill_fp8", "decode, residual sublayer",
+    order = ["decode", "prefill", "prefill_packed", "decode_fp8", "prefill_fp8", "decode, residual sublayer",
              "prefill, residual sublayer"]
     for wl in order + sorted(k for k in per if k not in order):
         if wl not in per:
@@ -264,12 +272,21 @@ def measured_traffic(workload):
     return None
 
 
+_PACKED = {}   # W_down packed to fp16 once per run (a weight-load step, outside every timed region)
+
+
 def time_workload(name, experts, steps, warmup, experts_fp8=None):
     """`name` is a workload of synth.WORKLOADS, or one with the suffix "_fp8": the same batch
-    through the FP8-weight entry point."""
-    from grouped_top_routing_fp32_amd import synth
+    through the FP8-weight entry point, or "_packed": the same batch through
+    beam_moe_forward_packed, with W_down converted to fp16 once beforehand."""
+    from grouped_top_routing_fp32_amd import binding, synth
     if name.endswith("_fp8"):
         return time_wl(synth.WORKLOADS[name[:-4]], experts, steps, warmup, fp8=experts_fp8)
+    if name.endswith("_packed"):
+        wl = synth.WORKLOADS[name[:-7]]
+        if "wd" not in _PACKED:
+            _PACKED["wd"] = binding.beam_moe_pack_weights(wl.dims, experts[2])
+        return time_wl(wl, experts, steps, warmup, packed_down=_PACKED["wd"])
     return time_wl(synth.WORKLOADS[name], experts, steps, warmup)
 
 
@@ -339,7 +356,7 @@ def timed_loops(call, steps, warmup, stream):
     return total_ms, stage_ms
 
 
-def time_wl(wl, experts, steps, warmup, fp8=None):
+def time_wl(wl, experts, steps, warmup, fp8=None, packed_down=None):
     import torch
     from grouped_top_routing_fp32_amd import binding, synth
 
@@ -352,6 +369,9 @@ def time_wl(wl, experts, steps, warmup, fp8=None):
     stream = torch.cuda.current_stream()
     if fp8 is not None:
         call = lambda: binding.beam_moe_forward_fp8(d, x, wr, bias, *fp8, bufs=bufs, stream=stream)  # noqa: E731
+    elif packed_down is not None:
+        call = lambda: binding.beam_moe_forward_packed(d, x, wr, bias, wg, wu, packed_down,  # noqa: E731
+                                                       bufs=bufs, stream=stream)
     else:
         call = lambda: binding.beam_moe_forward(d, x, wr, bias, wg, wu, wd, bufs=bufs, stream=stream)  # noqa: E731
     total_ms, stage_ms = timed_loops(call, steps, warmup, stream)
@@ -727,9 +747,10 @@ def main():
         r["experts"] = experts
         r["experts_fp8"] = experts_fp8
         r["fp8"] = name.endswith("_fp8")
+        r["packed"] = name.endswith("_packed")
         results[name] = r
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step; stages {r['stage_ms']}", file=sys.stderr, flush=True)
-        if not args.no_residual and not r["fp8"]:
+        if not args.no_residual and not r["fp8"] and not r["packed"]:
             r["residual"] = time_residual(r, args.steps, args.warmup)
             print(f"[bench] {name} as a residual sublayer: {r['residual']['ms_per_step']:.4f} ms/step",
                   file=sys.stderr, flush=True)
@@ -741,7 +762,8 @@ def main():
         wl = r["wl"]
         d = wl.dims
         bound = "hbm" if wl.tokens * d.topk / d.num_experts < 32 else "mfma"
-        what = "Beam MoE block forward" + (" with FP8 E4M3 expert weights" if r["fp8"] else "")
+        what = "Beam MoE block forward" + (" with FP8 E4M3 expert weights" if r["fp8"] else "") + \
+            (" with W_down packed to fp16 once (beam_moe_pack_weights; bf16 gate/up)" if r["packed"] else "")
         cfg = {"workload": f"{name}: {what}, T={wl.tokens}", "tokens": wl.tokens,
                "hidden": d.hidden, "intermediate": d.intermediate, "experts": d.num_experts,
                "groups": d.num_groups, "topk_groups": d.topk_groups, "topk": d.topk,
@@ -752,7 +774,7 @@ def main():
         out["dtype"] = DTYPE_FP8 if r["fp8"] else DTYPE_BF16
         if "residual" in r:
             out["residual_sublayer"] = r["residual"]
-        if not args.no_cpu_baseline and name != head:
+        if not args.no_cpu_baseline and name != head and not r["packed"]:
             print(f"[bench] cpu baseline (oracle) on {name}", file=sys.stderr, flush=True)
             out["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds / 2)
         return out

@@ -28,7 +28,8 @@ SCRATCH_BYTES = 64 << 20       # BEAM_MOE_SCRATCH_BYTES: scratch of beam_moe_for
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route_workspace_bytes", "beam_moe_dispatch_workspace_bytes",
             "beam_moe_route", "beam_moe_select", "beam_moe_dispatch",
-            "beam_moe_forward", "beam_moe_forward_noalloc", "beam_moe_forward_fp8", "beam_moe_residual_forward",
+            "beam_moe_forward", "beam_moe_forward_noalloc", "beam_moe_pack_weights", "beam_moe_forward_packed",
+            "beam_moe_forward_fp8", "beam_moe_residual_forward",
             "beam_moe_residual_forward_fp8", "beam_moe_stream_rows", "beam_moe_timing_enable",
             "beam_moe_timing_read", "beam_moe_stage_name", "beam_moe_status_str")
 
@@ -73,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.beam_moe_dispatch.restype = ctypes.c_int
     lib.beam_moe_forward.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.beam_moe_forward.restype = ctypes.c_int
+    lib.beam_moe_pack_weights.argtypes = [pd, vp, vp, vp]
+    lib.beam_moe_pack_weights.restype = ctypes.c_int
+    lib.beam_moe_forward_packed.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.beam_moe_forward_packed.restype = ctypes.c_int
     lib.beam_moe_forward_noalloc.argtypes = [pd, i32] + [vp] * 13 + [vp]
     lib.beam_moe_forward_noalloc.restype = ctypes.c_int
     lib.beam_moe_forward_fp8.argtypes = [pd, i32] + [vp] * 17 + [sz, vp]
@@ -294,6 +299,41 @@ def beam_moe_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor, logit_
         ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), *_outputs(bufs, bufs.out), _stream(stream))
     _check(st, "beam_moe_forward")
+    return bufs
+
+
+def beam_moe_pack_weights(dims: Dims, w_down: torch.Tensor, out: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """W_down [E, H, I] bf16 -> fp16 (the form beam_moe_forward_packed takes)."""
+    E, I, H = dims.num_experts, dims.intermediate, dims.hidden
+    _req(w_down, "w_down", torch.bfloat16, (E, H, I))
+    if out is None:
+        out = torch.empty((E, H, I), dtype=torch.float16, device=w_down.device)
+    _req(out, "w_down_packed", torch.float16, (E, H, I))
+    cd = _cdims(dims)
+    _check(load_library().beam_moe_pack_weights(ctypes.byref(cd), _ptr(w_down), _ptr(out), _stream(stream)),
+           "beam_moe_pack_weights")
+    return out
+
+
+def beam_moe_forward_packed(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
+                            logit_bias: Optional[torch.Tensor], w_gate: torch.Tensor, w_up: torch.Tensor,
+                            w_down_packed: torch.Tensor, *, select_bias: Optional[torch.Tensor] = None,
+                            bufs: Optional[ForwardBuffers] = None, stream=None) -> ForwardBuffers:
+    """beam_moe_forward with W_down from beam_moe_pack_weights (fp16)."""
+    T = x.shape[0]
+    E, I, H = dims.num_experts, dims.intermediate, dims.hidden
+    _req(x, "x", torch.bfloat16, (T, H))
+    _req_router(dims, w_router, logit_bias, select_bias)
+    _req(w_gate, "w_gate", torch.bfloat16, (E, I, H))
+    _req(w_up, "w_up", torch.bfloat16, (E, I, H))
+    _req(w_down_packed, "w_down_packed", torch.float16, (E, H, I))
+    bufs = _buffers(dims, T, x.device, bufs)
+    cd = _cdims(dims)
+    st = load_library().beam_moe_forward_packed(
+        ctypes.byref(cd), T, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down_packed), *_outputs(bufs, bufs.out), _stream(stream))
+    _check(st, "beam_moe_forward_packed")
     return bufs
 
 

@@ -28,8 +28,9 @@ hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const T
                                 int max_tiles, int R, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                                 uint8_t* hscale, int H, int I, int K, hipStream_t st);
 hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                              const int32_t* ntiles, int max_tiles, int R, const uint16_t* wd, uint16_t* y16,
-                              uint8_t* yscale, int H, int I, hipStream_t st);
+                              const int32_t* ntiles, int max_tiles, int R, const uint16_t* wd, bool wd_f16,
+                              uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st);
+hipError_t launch_pack_f16(const uint16_t* src, uint16_t* dst, size_t n, hipStream_t st);
 hipError_t launch_combine(const uint16_t* y16, const uint8_t* yscale, const float* w, float* out, int T, int H, int K,
                           hipStream_t st);
 bool stream_fp8_fits(int H, int I, int R);
@@ -58,7 +59,7 @@ hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const 
                                  int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale,
                                  int H, int I, int K, hipStream_t st);
 hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16,
+                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, bool wd_f16, uint16_t* y16,
                                uint8_t* yscale, int H, int I, hipStream_t st);
 }  // namespace beam
 
@@ -240,6 +241,7 @@ struct BlockArgs {
   const uint16_t* wg;  // bf16 experts (null for FP8 ones)
   const uint16_t* wu;
   const uint16_t* wd;
+  bool wd_f16;  // wd holds fp16 weights (beam_moe_pack_weights), not bf16
   const uint8_t* qg;  // FP8 experts: E4M3 codes and per-row scales (null for bf16 ones)
   const uint8_t* qu;
   const uint8_t* qd;
@@ -340,11 +342,11 @@ int run_block(const beam_moe_dims* d, const Plan& p, const BlockArgs& a, void* w
     BEAM_TRY(beam::launch_down_grouped_fp8(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.qd, a.sd, y16,
                                            yscale, p.H, p.I, st));
   else if (p.stream)
-    BEAM_TRY(beam::launch_down_stream(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, p.rows, a.wd, y16,
-                                      yscale, p.H, p.I, st));
+    BEAM_TRY(beam::launch_down_stream(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, p.rows, a.wd,
+                                      a.wd_f16, y16, yscale, p.H, p.I, st));
   else
-    BEAM_TRY(beam::launch_down_grouped(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wd, y16, yscale,
-                                       p.H, p.I, st));
+    BEAM_TRY(beam::launch_down_grouped(h, hscale, a.sorted_slots, tiles, ntiles, p.max_tiles, a.wd, a.wd_f16, y16,
+                                       yscale, p.H, p.I, st));
   BEAM_TRY(mark(ev, kStCombine, st));
   BEAM_TRY(combine(y16, yscale));
   BEAM_TRY(mark(ev, kNumStages, st));
@@ -402,9 +404,11 @@ int check_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, const f
 int forward_bf16(const beam_moe_dims* d, const Plan& p, const void* x_bf16, const float* w_router,
                  const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
                  const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
-                 int32_t* expert_offsets, int32_t* sorted_slots, void* ws, hipStream_t st, bool timed) {
+                 int32_t* expert_offsets, int32_t* sorted_slots, void* ws, hipStream_t st, bool timed,
+                 bool wd_f16 = false) {
   BlockArgs a = bf16_block(x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, topk_ids, topk_w,
                            expert_counts, expert_offsets, sorted_slots);
+  a.wd_f16 = wd_f16;
   return run_block(
       d, p, a, ws, st, [] { return hipSuccess; },
       [&](const uint16_t* y16, const uint8_t* yscale) {
@@ -561,6 +565,33 @@ int beam_moe_forward(const beam_moe_dims* d, int32_t T, const void* x_bf16, cons
   if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
   return forward_bf16(d, p, x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down, out, topk_ids, topk_w,
                       expert_counts, expert_offsets, sorted_slots, ws, static_cast<hipStream_t>(stream), true);
+}
+
+int beam_moe_pack_weights(const beam_moe_dims* d, const void* w_down_bf16, void* w_down_packed, void* stream) {
+  if (!d) return BEAM_MOE_ERR_INVALID_ARG;
+  if (!dims_ok(d)) return BEAM_MOE_ERR_UNSUPPORTED;
+  int rc;
+  if ((rc = check_ptrs({w_down_bf16, w_down_packed})) != BEAM_MOE_OK) return rc;
+  if (w_down_bf16 == w_down_packed) return BEAM_MOE_ERR_INVALID_ARG;
+  const size_t n = (size_t)d->num_experts * d->hidden * d->intermediate;
+  return hip_status(beam::launch_pack_f16(static_cast<const uint16_t*>(w_down_bf16),
+                                          static_cast<uint16_t*>(w_down_packed), n,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int beam_moe_forward_packed(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,
+                            const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
+                            const void* w_down_packed, float* out, int32_t* topk_ids, float* topk_w,
+                            int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots, void* ws,
+                            size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = check_forward(d, T, x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down_packed, out,
+                         topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots, &p);
+  if (rc != BEAM_MOE_OK || T == 0) return rc;
+  if (!ws || !aligned16(ws) || ws_bytes < p.total) return BEAM_MOE_ERR_WORKSPACE;
+  return forward_bf16(d, p, x_bf16, w_router, logit_bias, select_bias, w_gate, w_up, w_down_packed, out, topk_ids,
+                      topk_w, expert_counts, expert_offsets, sorted_slots, ws, static_cast<hipStream_t>(stream), true,
+                      true);
 }
 
 int beam_moe_forward_noalloc(const beam_moe_dims* d, int32_t T, const void* x_bf16, const float* w_router,

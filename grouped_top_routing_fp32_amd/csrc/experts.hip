@@ -318,7 +318,8 @@ __global__ __launch_bounds__(256) void gateup_stream_lds_kernel(const uint16_t* 
 // covers 64 NB columns, so wide tiles (NB = 2) read their activation rows half as
 // often per weight byte, in LDS and from L2.  Slot rows: 0 .. 64 NB - 1 W_down
 // rows of the workgroup's columns, then the R activation rows (h, fp16) of the tile.
-template <int SLOTS, int SK, int R, int NB>
+// WF16: W_down given in fp16 (beam_moe_pack_weights), used as read.
+template <int SLOTS, int SK, int R, int NB, bool WF16>
 __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __restrict__ h,
                                                               const uint8_t* __restrict__ hscale,
                                                               const int32_t* __restrict__ sorted_slots,
@@ -411,7 +412,10 @@ __global__ __launch_bounds__(256) void down_stream_lds_kernel(const uint16_t* __
       u32x4 b[NB];
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        b[j] = bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(sl + stage_off<SK>(brow + 16 * j, c)));
+      {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(sl + stage_off<SK>(brow + 16 * j, c));
+        b[j] = WF16 ? raw : bf16x8_to_f16x8(raw);  // WF16: the weights are fp16 already
+      }
       if (scaled) {
         const int sk = __builtin_amdgcn_readfirstlane(ssc[(st * SK + 32 * s) / kScaleCols]);
         if (sk != s_acc) {
@@ -831,15 +835,16 @@ static hipError_t gateup_r(const uint16_t* x, const int32_t* slots, const Tile* 
   return hipGetLastError();
 }
 
-template <int R>
+template <int R, bool WF16>
 static hipError_t down_r(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
                          const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16, uint8_t* yscale,
                          int H, int I, hipStream_t st) {
   constexpr int S = down_slots(R), NB = down_nb(R);
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_lds_kernel<S, kSk, R, NB>), lds_set);
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(&down_stream_lds_kernel<S, kSk, R, NB, WF16>), lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_stream_lds_kernel<S, kSk, R, NB>), dim3(max_tiles * (H / (64 * NB))), dim3(256),
+  hipLaunchKernelGGL((down_stream_lds_kernel<S, kSk, R, NB, WF16>), dim3(max_tiles * (H / (64 * NB))), dim3(256),
                      down_stream_lds_bytes(R, I), st, h, hscale, slots, tiles, ntiles, wd, y16, yscale, H, I);
   return hipGetLastError();
 }
@@ -884,16 +889,49 @@ hipError_t launch_gateup_stream(const uint16_t* x, const int32_t* slots, const T
   }
 }
 
-hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                              const int32_t* ntiles, int max_tiles, int R, const uint16_t* wd, uint16_t* y16,
-                              uint8_t* yscale, int H, int I, hipStream_t st) {
+template <bool WF16>
+static hipError_t down_stream_any(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                                  const int32_t* ntiles, int max_tiles, int R, const uint16_t* wd, uint16_t* y16,
+                                  uint8_t* yscale, int H, int I, hipStream_t st) {
   switch (R) {
-    case 8: return down_r<8>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
-    case 16: return down_r<16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
-    case 32: return down_r<32>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
-    case 64: return down_r<64>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+    case 8: return down_r<8, WF16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+    case 16: return down_r<16, WF16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+    case 32: return down_r<32, WF16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+    case 64: return down_r<64, WF16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+// wd_f16: W_down given in fp16 (beam_moe_pack_weights) rather than bf16.
+hipError_t launch_down_stream(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                              const int32_t* ntiles, int max_tiles, int R, const uint16_t* wd, bool wd_f16,
+                              uint16_t* y16, uint8_t* yscale, int H, int I, hipStream_t st) {
+  return wd_f16 ? down_stream_any<true>(h, hscale, slots, tiles, ntiles, max_tiles, R, wd, y16, yscale, H, I, st)
+                : down_stream_any<false>(h, hscale, slots, tiles, ntiles, max_tiles, R, wd, y16, yscale, H, I, st);
+}
+
+// ---------------------------------------------------------------------------
+// weight packing: bf16 -> fp16, once, for the down projection
+// ---------------------------------------------------------------------------
+// Each 16-byte group of 8 bf16 values becomes 8 fp16 values by exactly the
+// conversion the down kernels apply as they read bf16 weights (bf16x8_to_f16x8),
+// so a forward on the packed weights gives the same bits as one on the bf16
+// weights.  Grid-stride over n8 groups of 8 elements.
+__global__ __launch_bounds__(256) void pack_f16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                       size_t n8) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride)
+    dst[i] = bf16x8_to_f16x8(src[i]);
+}
+
+hipError_t launch_pack_f16(const uint16_t* src, uint16_t* dst, size_t n, hipStream_t st) {
+  const size_t n8 = n / 8;  // n % 8 == 0: whole rows of I % 128 == 0 elements
+  if (n8 == 0) return hipSuccess;
+  const size_t want = (n8 + 255) / 256;
+  const unsigned blocks = (unsigned)std::min<size_t>(want, 16384);
+  hipLaunchKernelGGL(pack_f16_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<const u32x4*>(src),
+                     reinterpret_cast<u32x4*>(dst), n8);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -80,7 +80,7 @@ __device__ __forceinline__ int xcd_lin(int b, int total) {
 
 // One block of a tile of at most 64 kLev rows (kLev row levels) against one
 // column block; ring holds two A stages of 64 kLev rows, then two B stages.
-template <bool GATEUP, bool FP8, int kLev>
+template <bool GATEUP, bool FP8, int kLev, bool WF16>
 __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t* srow, const Tile tl, int nblk,
                                            const uint16_t* __restrict__ act,
                                            const int32_t* __restrict__ sorted_slots, const void* __restrict__ w0v,
@@ -92,7 +92,9 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
   using WT = std::conditional_t<FP8, uint8_t, uint16_t>;  // weight element
   const WT* w0 = static_cast<const WT*>(w0v);
   const WT* w1 = static_cast<const WT*>(w1v);
-  constexpr bool kRegB = FP8 || !GATEUP;  // weights through registers
+  // weights through registers (FP8 codes, bf16 down weights to convert), or copied by the
+  // load unit (bf16 gate/up weights, and down weights already in fp16: WF16)
+  constexpr bool kRegB = FP8 || (!GATEUP && !WF16);
   constexpr int BM = 64 * kLev;           // rows per A stage
   constexpr int kAPer = BM / 8;           // A rows copied per wave
   uint16_t(*sA)[BM * kBK] = reinterpret_cast<uint16_t(*)[BM * kBK]>(ring);
@@ -272,11 +274,12 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
   if constexpr (kRegB) {
     load_b(0);
     store_b(0);
-    s_next = bsexp;
-    s_acc = bsexp;
   } else {
     issue_b(0, 0);
+    if constexpr (!GATEUP) bsexp = tscale[0];
   }
+  s_next = bsexp;
+  s_acc = bsexp;
   auto main_loop = [&](auto full) {
     for (int st = 0; st < nk; ++st) {
       const int slot = st & 1;
@@ -287,10 +290,12 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
       const int s_st = s_next;
       if (more) {
         issue_a(st + 1, slot ^ 1);
-        if constexpr (kRegB)
+        if constexpr (kRegB) {
           load_b(st + 1);
-        else
+        } else {
           issue_b(st + 1, slot ^ 1);
+          if constexpr (!GATEUP) bsexp = tscale[st + 1];
+        }
       }
       if constexpr (!GATEUP) {
         if (s_st != s_acc) {  // uniform: one exponent per tile and stage
@@ -307,8 +312,8 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
         math(slot, 0, full);
         math(slot, 1, full);
       }
-      if (kRegB && more) {
-        store_b(slot ^ 1);
+      if (more) {
+        if constexpr (kRegB) store_b(slot ^ 1);
         s_next = bsexp;
       }
     }
@@ -435,7 +440,7 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
 //      w1, [E, Ndim]); every copy of them passes through registers, where the codes are decoded
 //      exactly (to bf16 for gate/up, to fp16 for down), and the row scales multiply the
 //      accumulators before the epilogue.
-template <bool GATEUP, bool FP8>
+template <bool GATEUP, bool FP8, bool WF16 = false>
 __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_slots, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, const void* __restrict__ w0v, const void* __restrict__ w1v,
@@ -475,13 +480,13 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     if (idx > 0 && prev.expert == tl.expert && tl.rows <= kMergeRows) return;  // merged into the tile before
     if (idx + 1 < nt && next.expert == tl.expert && next.rows <= kMergeRows) {
       tl.rows += next.rows;
-      gemm_block<GATEUP, FP8, (kBM + kMergeRows) / 64>(ring, smax, srow, tl, nblk, act, sorted_slots, w0v, w1v, s0,
-                                                       s1, out, hscale, oscale, Kdim, Ndim, topk);
+      gemm_block<GATEUP, FP8, (kBM + kMergeRows) / 64, WF16>(ring, smax, srow, tl, nblk, act, sorted_slots, w0v,
+                                                             w1v, s0, s1, out, hscale, oscale, Kdim, Ndim, topk);
       return;
     }
   }
-  gemm_block<GATEUP, FP8, kBM / 64>(ring, smax, srow, tl, nblk, act, sorted_slots, w0v, w1v, s0, s1, out, hscale,
-                                    oscale, Kdim, Ndim, topk);
+  gemm_block<GATEUP, FP8, kBM / 64, WF16>(ring, smax, srow, tl, nblk, act, sorted_slots, w0v, w1v, s0, s1, out,
+                                          hscale, oscale, Kdim, Ndim, topk);
 }
 
 int grouped_gemm_rows() { return gg::kBM; }
@@ -498,14 +503,21 @@ hipError_t launch_gateup_grouped(const uint16_t* x, const int32_t* slots, const 
   return hipGetLastError();
 }
 
+// wd_f16: W_down already converted to fp16 (beam_moe_pack_weights): copied into LDS by
+// the load unit like the gate/up weights, with no conversion.
 hipError_t launch_down_grouped(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
-                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16,
+                               const int32_t* ntiles, int max_tiles, const uint16_t* wd, bool wd_f16, uint16_t* y16,
                                uint8_t* yscale, int H, int I, hipStream_t st) {
   const int nbn = H / gg::kBN;  // H % 256 == 0
   const int total = gemm_blocks(max_tiles, nbn);
-  hipLaunchKernelGGL((grouped_gemm_kernel<false, false>), dim3(total), dim3(gg::kThreads), 0, st, h, slots, tiles,
-                     ntiles, wd, nullptr, nullptr, nullptr, (void*)y16, const_cast<uint8_t*>(hscale), yscale, I, H, 0,
-                     nbn, total);
+  if (wd_f16)
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, false, true>), dim3(total), dim3(gg::kThreads), 0, st, h, slots,
+                       tiles, ntiles, wd, nullptr, nullptr, nullptr, (void*)y16, const_cast<uint8_t*>(hscale), yscale,
+                       I, H, 0, nbn, total);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, false>), dim3(total), dim3(gg::kThreads), 0, st, h, slots, tiles,
+                       ntiles, wd, nullptr, nullptr, nullptr, (void*)y16, const_cast<uint8_t*>(hscale), yscale, I, H,
+                       0, nbn, total);
   return hipGetLastError();
 }
 

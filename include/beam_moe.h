@@ -169,6 +169,30 @@ int beam_moe_forward(const beam_moe_dims* dims, int32_t T, const void* x_bf16, c
                      const void* w_down, float* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
                      int32_t* expert_offsets, int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
+/* Converts W_down [E, H, I] from bf16 to fp16 once, for beam_moe_forward_packed
+ * (a weight-load step, like quantising to FP8: the forward never repeats it).
+ * Each value is converted exactly as the down kernels convert bf16 weights as
+ * they read them: exactly for magnitudes in fp16's normal range [2^-14, 65504],
+ * toward zero below it (subnormals), so beam_moe_forward_packed on the result
+ * gives the same bits as beam_moe_forward on the bf16 weights.  Magnitudes
+ * above 65504 do not fit fp16 (far outside any weight range); the result is
+ * then undefined.
+ *   w_down_bf16    [E, H, I] bf16
+ *   w_down_packed  [E, H, I] fp16 out (caller-owned, not aliasing w_down_bf16)
+ * Asynchronous on `stream`, like every call. */
+int beam_moe_pack_weights(const beam_moe_dims* dims, const void* w_down_bf16, void* w_down_packed, void* stream);
+
+/* beam_moe_forward with W_down given as beam_moe_pack_weights made it (fp16
+ * [E, H, I]); all other arguments, outputs and results as beam_moe_forward, bit
+ * for bit.  The down projection then copies its weights into LDS unconverted,
+ * as the gate/up projection does, instead of converting each stage in
+ * registers. */
+int beam_moe_forward_packed(const beam_moe_dims* dims, int32_t T, const void* x_bf16, const float* w_router,
+                            const float* logit_bias, const float* select_bias, const void* w_gate, const void* w_up,
+                            const void* w_down_packed, float* out, int32_t* topk_ids, float* topk_w,
+                            int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* beam_moe_forward without the workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  It allocates nothing: the scratch that

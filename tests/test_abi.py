@@ -306,3 +306,27 @@ def test_forward_noalloc_validation():
     bad = binding._cdims(Dims(5120, 2560, 256, 7, 4, 8))
     assert lib.beam_moe_forward_noalloc(ctypes.byref(bad), 64, *ok, None) == binding.BEAM_MOE_ERR_UNSUPPORTED
     assert lib.beam_moe_forward_noalloc(ctypes.byref(cd), 0, *([None] * 13), None) == binding.BEAM_MOE_OK
+
+
+def test_pack_and_forward_packed_validation():
+    """Rejections of the packed entry points return before any device call."""
+    lib = binding.load_library()
+    cd = binding._cdims(BEAM)
+    other = ctypes.c_void_p(2 << 20)
+    assert lib.beam_moe_pack_weights(ctypes.byref(cd), None, FAKE, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert lib.beam_moe_pack_weights(ctypes.byref(cd), FAKE, None, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    assert lib.beam_moe_pack_weights(ctypes.byref(cd), FAKE, ctypes.c_void_p((2 << 20) + 8), None) == \
+        binding.BEAM_MOE_ERR_INVALID_ARG
+    assert lib.beam_moe_pack_weights(ctypes.byref(cd), FAKE, FAKE, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    bad = binding._cdims(Dims(5120, 2560, 256, 7, 4, 8))
+    assert lib.beam_moe_pack_weights(ctypes.byref(bad), FAKE, other, None) == binding.BEAM_MOE_ERR_UNSUPPORTED
+    assert lib.beam_moe_pack_weights(None, FAKE, other, None) == binding.BEAM_MOE_ERR_INVALID_ARG
+    ok = [FAKE] * 14
+    for i in (0, 1, 4, 5, 6, 7, 8, 9, 10, 11, 12):
+        args = list(ok)
+        args[i] = None
+        assert lib.beam_moe_forward_packed(ctypes.byref(cd), 64, *args, 1 << 40, None) == \
+            binding.BEAM_MOE_ERR_INVALID_ARG
+    need = lib.beam_moe_workspace_bytes(ctypes.byref(cd), 64)
+    assert lib.beam_moe_forward_packed(ctypes.byref(cd), 64, *ok, need - 1, None) == binding.BEAM_MOE_ERR_WORKSPACE
+    assert lib.beam_moe_forward_packed(ctypes.byref(cd), 0, *([None] * 14), 0, None) == binding.BEAM_MOE_OK

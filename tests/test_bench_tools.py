@@ -35,8 +35,8 @@ def test_source_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
 def test_traffic_summary_and_reader(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.txt"))
     copy_kib = bench.COPY_BYTES / 1024
-    gate_up = "void beam::gateup_stream_lds_kernel<3, 128>(int)"
-    grouped = "void beam::grouped_gemm_kernel<true, false>(int)"
+    gate_up = "void beam::gateup_stream_lds_kernel<3, 128, 8>(int)"
+    grouped = "void beam::grouped_gemm_kernel<true, false, false>(int)"
     calib = "void at::native::neg_kernel(int)"
     # FETCH_SIZE reads half the calibration copy's bytes (scale 2), WRITE_SIZE all of them (scale 1)
     _write_counters(tmp_path / "fetch" / "sub", "FETCH_SIZE",
@@ -54,7 +54,7 @@ def test_traffic_summary_and_reader(tmp_path, monkeypatch):
 
 
 def test_counter_summary_keeps_passes_apart(tmp_path):
-    grouped = "void beam::grouped_gemm_kernel<true, false>(int)"
+    grouped = "void beam::grouped_gemm_kernel<true, false, false>(int)"
     for label, busy in (("prefill", 0.5), ("skewed", 0.25)):
         d = tmp_path / label
         os.makedirs(d)
@@ -70,27 +70,31 @@ def test_counter_summary_keeps_passes_apart(tmp_path):
     out = tmp_path / "summary.md"
     bench.summarize_counters(str(out), f"prefill={tmp_path / 'prefill'}", f"skewed={tmp_path / 'skewed'}")
     text = out.read_text()
-    prefill = text[text.index("## prefill: `beam::grouped_gemm_kernel<true, false>` (1 dispatches)"):
+    prefill = text[text.index("## prefill: `beam::grouped_gemm_kernel<true, false, false>` (1 dispatches)"):
                    text.index("## skewed:")]
-    skewed = text[text.index("## skewed: `beam::grouped_gemm_kernel<true, false>` (1 dispatches)"):]
+    skewed = text[text.index("## skewed: `beam::grouped_gemm_kernel<true, false, false>` (1 dispatches)"):]
     assert "| MFMA busy (derived) | 0.500 |" in prefill and "| MFMA busy (derived) | 0.250 |" in skewed
     assert "| wave wait (derived) | 0.300 |" in prefill
     assert "--workloads prefill " in text and "--workloads skewed " in text
 
 
 def test_trace_summary_cuts_and_classifies_calls(tmp_path):
-    """Four calls in a row (decode, prefill, FP8 decode, a residual-sublayer decode): each is cut at
+    """Five calls in a row (decode, prefill, FP8 decode, a residual-sublayer decode, prefill with
+    packed down weights): each is cut at
     its router (or its prenorm) and filed under its workload; other kernels are ignored."""
     calls = [
-        ["router_logits_kernel<64>", "select_kernel", "dispatch_small_kernel", "gateup_stream_lds_kernel<3, 128>",
-         "down_stream_lds_kernel<3, 128>", "combine_kernel"],
+        ["router_logits_kernel<64>", "select_kernel", "dispatch_small_kernel", "gateup_stream_lds_kernel<3, 128, 8>",
+         "down_stream_lds_kernel<3, 128, 8, 1, false>", "combine_kernel"],
         ["router_logits_kernel<128>", "select_kernel", "dispatch_hist_kernel", "dispatch_scan_kernel",
-         "dispatch_scatter_kernel", "grouped_gemm_kernel<true, false>", "grouped_gemm_kernel<false, false>",
+         "dispatch_scatter_kernel", "grouped_gemm_kernel<true, false, false>", "grouped_gemm_kernel<false, false, false>",
          "combine_kernel"],
-        ["router_logits_kernel<64>", "select_kernel", "dispatch_small_kernel", "gateup_stream_fp8_kernel<3>",
-         "down_stream_fp8_kernel<3>", "combine_kernel"],
+        ["router_logits_kernel<64>", "select_kernel", "dispatch_small_kernel", "gateup_stream_fp8_kernel<3, 8>",
+         "down_stream_fp8_kernel<3, 8, 1>", "combine_kernel"],
         ["prenorm_kernel", "router_logits_kernel<64>", "select_kernel", "dispatch_small_kernel",
-         "gateup_stream_lds_kernel<3, 128>", "down_stream_lds_kernel<3, 128>", "combine_residual_kernel"],
+         "gateup_stream_lds_kernel<3, 128, 8>", "down_stream_lds_kernel<3, 128, 8, 1, false>", "combine_residual_kernel"],
+        ["router_logits_kernel<128>", "select_kernel", "dispatch_hist_kernel", "dispatch_scan_kernel",
+         "dispatch_scatter_kernel", "grouped_gemm_kernel<true, false, false>", "grouped_gemm_kernel<false, false, true>",
+         "combine_kernel"],
     ]
     os.makedirs(tmp_path / "trace" / "host")
     t = 1000
@@ -108,11 +112,12 @@ def test_trace_summary_cuts_and_classifies_calls(tmp_path):
     bench.summarize_trace(str(tmp_path / "trace"), str(out))
     text = out.read_text()
     sections = {s.split("\n", 1)[0]: s for s in text.split("\n## ")[1:]}
-    assert set(sections) == {"decode", "prefill", "decode_fp8", "decode, residual sublayer"}
+    assert set(sections) == {"decode", "prefill", "decode_fp8", "decode, residual sublayer", "prefill_packed"}
+    assert "`beam::grouped_gemm_kernel<false, false, true>` | 1 | 5.6 |" in sections["prefill_packed"]
     # each call's kernels are filed under its own workload, with its own durations (1 us per call
     # index, plus 0.1 us per position in the call)
-    assert "`beam::grouped_gemm_kernel<true, false>` | 1 | 2.5 |" in sections["prefill"]
-    assert "`beam::gateup_stream_fp8_kernel<3>` | 1 | 3.3 |" in sections["decode_fp8"]
+    assert "`beam::grouped_gemm_kernel<true, false, false>` | 1 | 2.5 |" in sections["prefill"]
+    assert "`beam::gateup_stream_fp8_kernel<3, 8>` | 1 | 3.3 |" in sections["decode_fp8"]
     assert "`beam::prenorm_kernel` | 1 | 4.0 |" in sections["decode, residual sublayer"]
     assert "`beam::router_logits_kernel<64>` | 1 | 4.1 |" in sections["decode, residual sublayer"]
     assert "`beam::combine_kernel` | 1 | 1.5 |" in sections["decode"]

@@ -727,3 +727,45 @@ def test_forward_graph_replay(name, fp8):
         torch.cuda.synchronize()
         for k in names:
             assert torch.equal(getattr(bufs, k), ref[k]), (i, k)
+
+
+# --------------------------------------------------------------------------
+# W_down packed to fp16 once (beam_moe_pack_weights): the same conversion the down kernels apply
+# to bf16 weights as they read them, so the packed forward gives the bf16 forward's bits
+# --------------------------------------------------------------------------
+PACKED = {
+    "mid_stream": MID["mid_stream"][0],           # stream kernels, 8-row tiles
+    "mid_stream_r64": MID["mid_stream_r64"][0],   # stream kernels, 64-row tiles, two column fragments per wave
+    "mid_tiled": MID["mid_tiled"][0],             # grouped GEMMs, full and ragged tiles
+    "mid_tiled_huge": MID["mid_tiled_huge"][0],   # accumulator rescaling between activation blocks
+    "dense_merged_big": EDGE["dense_merged_big"],  # a merged five-level tile with non-zero scales
+}
+
+
+def _packed_equals_bf16(p):
+    wdp = binding.beam_moe_pack_weights(p.dims, p.wd)
+    ref = binding.beam_moe_forward(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, p.wd)
+    got = binding.beam_moe_forward_packed(p.dims, p.x, p.wr, p.bias, p.wg, p.wu, wdp)
+    torch.cuda.synchronize()
+    for k in ("out", "ids", "w", "counts", "offsets", "slots"):
+        assert torch.equal(getattr(ref, k), getattr(got, k)), k
+    return wdp
+
+
+@pytest.mark.parametrize("name", list(PACKED))
+def test_forward_packed_matches_bf16_bits(name):
+    _announce(f"forward packed {name}")
+    p = Problem(PACKED[name], DEV)
+    wdp = _packed_equals_bf16(p)
+    # the packed weights are the bf16 ones, exactly where fp16 represents them
+    w32 = p.wd.float()
+    normal = w32.abs() >= 2.0 ** -14
+    assert torch.equal(wdp.float()[normal], w32[normal])
+
+
+@pytest.mark.parametrize("T", [64, 16384])
+def test_forward_packed_beam(beam_experts, T):
+    _announce(f"forward packed Beam T={T}")
+    wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
+    p = Problem(wl, DEV, experts=beam_experts)
+    _packed_equals_bf16(p)
