@@ -129,10 +129,12 @@ def summarize_pmc(fetch_dir, write_dir):
     f_scale = COPY_BYTES / 1024.0 / copy_kib(fetch)
     w_scale = COPY_BYTES / 1024.0 / copy_kib(write)
     lines = ["# HBM traffic per launch of the gate/up kernel (decode and prefill, bf16 and FP8 weights), from rocprofv3 counters",
-             "# fetch:  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- "
+             "# fetch:  rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'beam::|neg' --output-format csv "
+             "-d <FETCH_DIR> -o run -- "
              f"python3 bench.py --workloads {TRAFFIC_WORKLOADS} --steps 3 --warmup 1 --no-cpu-baseline --no-residual "
              "--copy-calibration",
-             "# write:  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- "
+             "# write:  rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'beam::|neg' --output-format csv "
+             "-d <WRITE_DIR> -o run -- "
              f"python3 bench.py --workloads {TRAFFIC_WORKLOADS} --steps 3 --warmup 1 --no-cpu-baseline --no-residual "
              "--copy-calibration",
              "# (one workload per gate/up kernel: dispatches are told apart by kernel name)",
@@ -597,7 +599,8 @@ def summarize_counters(out_md, *passes):
     sections, cmds = [], []
     for spec in passes:
         workloads, counter_dir = spec.split("=", 1)
-        cmds.append(f"rocprofv3 --pmc {COUNTER_SET} --output-format csv -d <COUNTER_DIR_{len(cmds) + 1}> -o run "
+        cmds.append(f"rocprofv3 --pmc {COUNTER_SET} --kernel-include-regex 'beam::' --output-format csv "
+                    f"-d <COUNTER_DIR_{len(cmds) + 1}> -o run "
                     f"-- python3 bench.py --workloads {workloads} --steps 2 --warmup 1 --no-cpu-baseline --no-residual")
         per, order = {}, []
         for path in sorted(glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True)):
