@@ -762,12 +762,22 @@ static hipError_t allow_full_lds(const void* fn, std::atomic<uint64_t>& done) {
 
 // Ring depth per tile height: three slots while they fit, else two.
 constexpr int gateup_slots(int R) { return (128 + R) * 256 * 3 <= 144 * 1024 ? 3 : 2; }
-// down workgroups take 128 output columns from 32-row tiles: their activation rows
-// are then read half as often per weight byte
-constexpr int down_nb(int R) { return R >= 32 ? 2 : 1; }
-constexpr int down_slots(int R) { return (64 * down_nb(R) + R) * 256 * 3 <= 144 * 1024 ? 3 : 2; }
+// The down kernels' shape per tile height, chosen by measurement (T = 256 .. 1024 at
+// Beam dims, identical output in every variant): a ring that fits half the LDS lets
+// two workgroups share a CU, so one's start-up and tail overlap the other's
+// streaming, which beat 128-column workgroups (which read their activation rows
+// half as often per weight byte) for bf16 weights at every tile height: 64-row
+// tiles 1.35 against 1.50 ms, 32-row 1.17 against 1.20.  With FP8 weights, whose
+// 512-byte activation rows outweigh the codes from 64-row tiles, 128 columns win
+// there (0.92 ms, against 1.11 with 64 columns and one workgroup per CU).
+constexpr int kHalfLds = 78 * 1024;
+constexpr int down_nb(int R) { return 1; }
+constexpr int down_slots(int R) { return (64 * down_nb(R) + R) * 256 * 3 <= kHalfLds ? 3 : 2; }
+constexpr int down_f8_nb(int R) { return R >= 64 ? 2 : 1; }
 constexpr int gateup_f8_slots(int R) { return R >= 64 ? 2 : 3; }
-constexpr int down_f8_slots(int R) { return (64 * down_nb(R) * kF8WRow + R * kF8ARow) * 3 <= 144 * 1024 ? 3 : 2; }
+constexpr int down_f8_slots(int R) {
+  return (64 * down_f8_nb(R) * kF8WRow + R * kF8ARow) * 3 <= kHalfLds ? 3 : 2;
+}
 
 size_t gateup_stream_lds_bytes(int R) { return (size_t)gateup_slots(R) * (128 + R) * StageGeom<kSk>::kRowBytes; }
 size_t down_stream_lds_bytes(int R, int I) {
@@ -775,7 +785,7 @@ size_t down_stream_lds_bytes(int R, int I) {
 }
 size_t gateup_stream_fp8_lds_bytes(int R) { return (size_t)gateup_f8_slots(R) * (128 * kF8WRow + R * kF8ARow); }
 size_t down_stream_fp8_lds_bytes(int R, int I) {
-  return (size_t)down_f8_slots(R) * (64 * down_nb(R) * kF8WRow + R * kF8ARow) + I / kScaleCols;
+  return (size_t)down_f8_slots(R) * (64 * down_f8_nb(R) * kF8WRow + R * kF8ARow) + I / kScaleCols;
 }
 
 // Tile heights the stream kernels are built for.  Wider tiles (128 rows) were
@@ -792,7 +802,7 @@ bool stream_fits(int H, int I, int R) {
 }
 
 bool stream_fp8_fits(int H, int I, int R) {
-  return stream_rows_ok(R, true) && H % kF8Sk == 0 && I % kF8Sk == 0 && H % (64 * down_nb(R)) == 0 &&
+  return stream_rows_ok(R, true) && H % kF8Sk == 0 && I % kF8Sk == 0 && H % (64 * down_f8_nb(R)) == 0 &&
          gateup_stream_fp8_lds_bytes(R) <= kStreamLdsMax && down_stream_fp8_lds_bytes(R, I) <= kStreamLdsMax;
 }
 
@@ -813,7 +823,7 @@ template <int R>
 static hipError_t down_fp8_r(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
                              const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd, uint16_t* y16,
                              uint8_t* yscale, int H, int I, hipStream_t st) {
-  constexpr int S = down_f8_slots(R), NB = down_nb(R);
+  constexpr int S = down_f8_slots(R), NB = down_f8_nb(R);
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_fp8_kernel<S, R, NB>), lds_set);
   if (e != hipSuccess) return e;
