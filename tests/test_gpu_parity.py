@@ -660,7 +660,7 @@ def test_forward_fp8_beam(beam_experts_fp8, T):
     assert torch.equal(out1, bufs.out)
 
 
-@pytest.mark.parametrize("name", ["f8_stream", "f8_grouped"])
+@pytest.mark.parametrize("name", ["f8_stream", "f8_stream_r32", "f8_grouped"])
 def test_residual_fp8(name):
     _announce(f"residual fp8 {name} (all tokens)")
     wl = FP8[name]
