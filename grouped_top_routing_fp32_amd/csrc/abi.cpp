@@ -112,9 +112,9 @@ struct Plan {
   // expert tiles
   bool stream;
   int rows;  // stream path: rows per tile
-  // one tile table serves both projections: whole experts (stream path) or
-  // row tiles of the grouped GEMMs, whose down kernel reads the activation
-  // scales of the gate/up tile its rows belong to
+  // one tile table serves both projections: tiles of at most `rows` rows
+  // (stream path) or the grouped GEMMs' 256-row tiles; each down kernel reads
+  // the activation scales of the gate/up tile its rows belong to
   int mt, max_tiles;
   size_t off_tiles, off_ntiles;
   // activations

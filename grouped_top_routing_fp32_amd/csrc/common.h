@@ -115,8 +115,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
-// One row tile of the grouped expert GEMMs (or one whole expert on the stream
-// path), written by the dispatch: rows [row_start, row_start + rows) of the
+// One row tile of the expert kernels (256 rows for the grouped GEMMs, at most
+// R for the stream kernels), written by the dispatch: rows [row_start, row_start + rows) of the
 // expert-sorted order, all belonging to `expert`.  An expert's consecutive
 // tiles are cut into groups of at most kTileGroupMax; each tile carries its
 // group's first index and size, which the GEMM block order uses to run a

@@ -9,23 +9,26 @@
 //   h[r] = silu(W_gate[e] x[r]) * (W_up[e] x[r])   bf16 MFMA, SwiGLU in FP32
 //   y[r] = W_down[e] h[r]                           fp16 MFMA, FP32 accumulation
 // h is handed to the down projection as fp16 (11 significant bits against
-// bf16's 8) with a power-of-two scale 2^-s per block of 64 columns of a pass
-// of rows, s chosen so the block's largest magnitude stays below 2^15; W_down
-// is converted from bf16 to fp16 exactly as it is read, and the FP32
-// accumulators are kept in units of 2^s of the activation block they consume
-// (rescaled exactly when s changes), so the weights never carry the scale.  y
-// goes to the combine the same way: fp16 scaled by 2^-s per (row group, 64
-// columns).
+// bf16's 8) with a power-of-two scale 2^-s per block of 64 columns of a row
+// tile, s chosen so the block's largest magnitude stays below 2^15; W_down is
+// converted from bf16 to fp16 exactly as it is read (or given in fp16 once
+// packed), and the FP32 accumulators are kept in units of 2^s of the
+// activation block they consume (rescaled exactly when s changes), so the
+// weights never carry the scale.  y goes to the combine the same way: fp16
+// scaled by 2^-s per (row tile, 64 columns).
 // Rows are processed in expert-sorted order (the dispatch permutation); a
-// tile table produced by the dispatch maps workgroups to experts.
+// tile table produced by the dispatch maps workgroups to row tiles of one
+// expert each.
 //
 // With few rows per expert the step is bound by streaming each touched
-// expert's weights from HBM once: a workgroup owns one expert and 64 output
+// expert's weights from HBM: a workgroup owns one tile of at most R rows
+// (the smallest of 8, 16, 32, 64 that holds twice the batch's average rows
+// per expert) and 64 output
 // columns, each wave 16 columns over the whole K, so no cross-wave reduction
-// is needed; weights and the pass's activation rows (up to 8) are copied into
-// LDS in whole 256-byte row segments.  Batches with more rows per expert use
-// the grouped GEMMs (grouped_gemm.hip), which read an expert's weights once
-// per 256-row tile rather than once per pass.
+// is needed; weights and the tile's activation rows are copied into LDS in
+// whole 256-byte row segments.  Batches with more rows per expert use the
+// grouped GEMMs (grouped_gemm.hip), which read an expert's weights once per
+// 256-row tile.
 #include <atomic>
 
 #include <algorithm>
