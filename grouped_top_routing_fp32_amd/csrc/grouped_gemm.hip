@@ -27,9 +27,13 @@
 // load unit (global_load_lds_dwordx4, no registers), each copy fetching 8 rows
 // x 128 contiguous bytes (one cache line per row: half-line requests measured
 // about 15% slower); two stages fit in LDS and stage t + 1 is requested at
-// the start of step t.  The copies are issued with inline assembly and waited
-// for explicitly (s_waitcnt vmcnt, then s_barrier for the other waves): the
-// compiler's own tracking of LDS copies adds a full drain at each loop head.
+// the start of step t.  Tiles of at most three levels keep three weight stages
+// (and, at two levels, three activation stages) in the same 144 KB, with stage
+// t + 2's weights requested at the start of step t: an expert with few rows
+// streams its weights at a rate one stage of lead cannot sustain.  The copies
+// are issued with inline assembly and waited for explicitly (s_waitcnt vmcnt,
+// then s_barrier for the other waves): the compiler's own tracking of LDS
+// copies adds a full drain at each loop head.
 // Down: the weight stage is loaded into registers, converted to fp16 and
 // written to LDS by the threads themselves, in the same layout the copies
 // produce; the accumulators are kept in units of 2^s of the stage's 64-column
@@ -79,10 +83,16 @@ __device__ __forceinline__ int xcd_lin(int b, int total) {
 }  // namespace gg
 
 // One block of a tile of at most 64 kLev rows (kLev row levels) against one
-// column block; ring holds two A stages of 64 kLev rows, then two B stages.
-template <bool GATEUP, bool FP8, int kLev, bool WF16>
-__device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t* srow, const Tile tl, int nblk,
-                                           const uint16_t* __restrict__ act,
+// column block; ring holds NA A stages of 64 kLev rows, then NB B stages.
+// NB = 3 (tiles of at most three levels, operands copied by the load unit): the
+// weights of two stages are in flight while the MFMAs consume a third.  Such
+// tiles have few rows per weight byte and are bound by the weight stream, which
+// one stage of lead leaves short of bytes in flight.  The activation rows (from
+// L2, mostly) keep the same lead where a third A slot fits (NA = 3, two levels),
+// else one stage (NA = 2).
+template <bool GATEUP, bool FP8, int kLev, bool WF16, int NA = 2, int NB = 2>
+__device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t* srow, uint8_t* stab, const Tile tl,
+                                           int nblk, const uint16_t* __restrict__ act,
                                            const int32_t* __restrict__ sorted_slots, const void* __restrict__ w0v,
                                            const void* __restrict__ w1v, const float* __restrict__ s0,
                                            const float* __restrict__ s1, void* __restrict__ out,
@@ -97,8 +107,10 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
   constexpr bool kRegB = FP8 || (!GATEUP && !WF16);
   constexpr int BM = 64 * kLev;           // rows per A stage
   constexpr int kAPer = BM / 8;           // A rows copied per wave
+  static_assert((NA == 2 && NB == 2) || (NB == 3 && NA >= 2 && NA <= 3 && !kRegB), "ring shapes");
+  static_assert((NA * BM + NB * kBN) * kBK <= kRingHalfs, "ring");
   uint16_t(*sA)[BM * kBK] = reinterpret_cast<uint16_t(*)[BM * kBK]>(ring);
-  uint16_t(*sB)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring + 2 * BM * kBK);
+  uint16_t(*sB)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring + NA * BM * kBK);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -206,9 +218,9 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto math = [&](int slot, int sub, auto full) {
-    const uint16_t* A = sA[slot];
-    const uint16_t* B = sB[slot];
+  auto math = [&](int aslot, int bslot, int sub, auto full) {
+    const uint16_t* A = sA[aslot];
+    const uint16_t* B = sB[bslot];
     const int ao = sub ? aoff1 : aoff0;
     const int bo = sub ? boff1 : boff0;
     u32x4 fa[kLev], fb[8];
@@ -270,59 +282,110 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
   // down: the accumulators hold y * 2^-s_acc, s_acc the exponent of the last stage
   // consumed; s_next is the exponent of the stage waiting in the other slot
   int s_acc = 0, s_next = 0;
-  issue_a(0, 0);
-  if constexpr (kRegB) {
-    load_b(0);
-    store_b(0);
-  } else {
-    issue_b(0, 0);
-    if constexpr (!GATEUP) bsexp = tscale[0];
-  }
-  s_next = bsexp;
-  s_acc = bsexp;
-  auto main_loop = [&](auto full) {
-    for (int st = 0; st < nk; ++st) {
-      const int slot = st & 1;
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_barrier();
-      const bool more = st + 1 < nk;
-      const int s_st = s_next;
-      if (more) {
-        issue_a(st + 1, slot ^ 1);
-        if constexpr (kRegB) {
-          load_b(st + 1);
-        } else {
-          issue_b(st + 1, slot ^ 1);
-          if constexpr (!GATEUP) bsexp = tscale[st + 1];
-        }
-      }
-      if constexpr (!GATEUP) {
-        if (s_st != s_acc) {  // uniform: one exponent per tile and stage
-#pragma unroll
-          for (int i = 0; i < kLev; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = ldexp4(acc[i][j], s_acc - s_st);
-          s_acc = s_st;
-        }
-      }
-      if constexpr (GATEUP && !FP8 && kLev == 4) {
-        math2(slot, full);
-      } else {
-        math(slot, 0, full);
-        math(slot, 1, full);
-      }
-      if (more) {
-        if constexpr (kRegB) store_b(slot ^ 1);
-        s_next = bsexp;
-      }
+  if constexpr (NB == 2) {
+    issue_a(0, 0);
+    if constexpr (kRegB) {
+      load_b(0);
+      store_b(0);
+    } else {
+      issue_b(0, 0);
+      if constexpr (!GATEUP) bsexp = tscale[0];
     }
-  };
-  // full tiles (the common case) run without the per-level tests
-  if (tl.rows >= BM)
-    main_loop(std::true_type{});
-  else
-    main_loop(std::false_type{});
+    s_next = bsexp;
+    s_acc = bsexp;
+    auto main_loop = [&](auto full) {
+      for (int st = 0; st < nk; ++st) {
+        const int slot = st & 1;
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        const bool more = st + 1 < nk;
+        const int s_st = s_next;
+        if (more) {
+          issue_a(st + 1, slot ^ 1);
+          if constexpr (kRegB) {
+            load_b(st + 1);
+          } else {
+            issue_b(st + 1, slot ^ 1);
+            if constexpr (!GATEUP) bsexp = tscale[st + 1];
+          }
+        }
+        if constexpr (!GATEUP) {
+          if (s_st != s_acc) {  // uniform: one exponent per tile and stage
+#pragma unroll
+            for (int i = 0; i < kLev; ++i)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) acc[i][j] = ldexp4(acc[i][j], s_acc - s_st);
+            s_acc = s_st;
+          }
+        }
+        if constexpr (GATEUP && !FP8 && kLev == 4) {
+          math2(slot, full);
+        } else {
+          math(slot, slot, 0, full);
+          math(slot, slot, 1, full);
+        }
+        if (more) {
+          if constexpr (kRegB) store_b(slot ^ 1);
+          s_next = bsexp;
+        }
+      }
+    };
+    // full tiles (the common case) run without the per-level tests
+    if (tl.rows >= BM)
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
+  } else {
+    // Stage t's weights live in B slot t % 3 and its activations in A slot t % NA.
+    // Step t: wait for this wave's copies of stage t (the later ones requested so
+    // far, at most stage t + 1's, may still be in flight), barrier (stage t complete
+    // for all waves, and everyone is done with stage t - 1's slots), request the
+    // activations of stage t + NA - 1 and the weights of stage t + 2 into the slots
+    // stage t - 1 held, MFMAs on stage t.  Requests go out in stage order per wave,
+    // so waiting until only the copies issued after stage t's remain is enough: with
+    // NA = 3 those are all of stage t + 1's, with NA = 2 its weight copies (4).
+    // Down reads each stage's activation scale exponent from the tile's table in LDS
+    // (stab, filled before the first barrier).
+    const int ncopies = (copy_a ? kLev : 0) + 4;  // copies per stage issued by this wave
+    if constexpr (!GATEUP)
+      for (int i = tid; i < nk; i += kThreads) stab[i] = tscale[i];
+    issue_a(0, 0);
+    issue_b(0, 0);
+    if constexpr (NA == 3) issue_a(1, 1);
+    issue_b(1, 1);
+    auto main_loop3 = [&](auto full) {
+      for (int st = 0; st < nk; ++st) {
+        const int slot = st % 3;
+        if (st + 1 == nk)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        else if (NA == 3 && ncopies == kLev + 4)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLev + 4));
+        else
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        if (st + NA - 1 < nk) issue_a(st + NA - 1, (st + NA - 1) % NA);
+        if (st + 2 < nk) issue_b(st + 2, (st + 2) % 3);
+        if constexpr (!GATEUP) {
+          const int s_st = stab[st];
+          if (s_st != s_acc) {  // uniform: one exponent per tile and stage
+#pragma unroll
+            for (int i = 0; i < kLev; ++i)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) acc[i][j] = ldexp4(acc[i][j], s_acc - s_st);
+            s_acc = s_st;
+          }
+        }
+        math(st % NA, slot, 0, full);
+        math(st % NA, slot, 1, full);
+      }
+    };
+    if (tl.rows >= BM)
+      main_loop3(std::true_type{});
+    else
+      main_loop3(std::false_type{});
+  }
 
   // ---- epilogue ----------------------------------------------------------
   // lane holds rows 4*(lane/16)+r and column lane%16 of each 16x16 block
@@ -454,6 +517,8 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
   // down: destination slots of the tile's rows, read when the block starts so that the
   // epilogue's stores need no dependent global loads
   __shared__ int32_t srow[GATEUP ? 1 : kBM + kMergeRows];
+  // down, three-stage tiles: the tile's activation scale exponent per stage (Kdim <= 32768)
+  __shared__ uint8_t stab[GATEUP ? 1 : 512];
 
   // The grid is sized for the most tiles a batch can have; the order spans the
   // tiles this batch has, so every XCD gets an equal share and the surplus
@@ -480,12 +545,28 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     if (idx > 0 && prev.expert == tl.expert && tl.rows <= kMergeRows) return;  // merged into the tile before
     if (idx + 1 < nt && next.expert == tl.expert && next.rows <= kMergeRows) {
       tl.rows += next.rows;
-      gemm_block<GATEUP, FP8, (kBM + kMergeRows) / 64, WF16>(ring, smax, srow, tl, nblk, act, sorted_slots, w0v,
-                                                             w1v, s0, s1, out, hscale, oscale, Kdim, Ndim, topk);
+      gemm_block<GATEUP, FP8, (kBM + kMergeRows) / 64, WF16>(ring, smax, srow, stab, tl, nblk, act, sorted_slots,
+                                                             w0v, w1v, s0, s1, out, hscale, oscale, Kdim, Ndim, topk);
       return;
     }
   }
-  gemm_block<GATEUP, FP8, kBM / 64, WF16>(ring, smax, srow, tl, nblk, act, sorted_slots, w0v, w1v, s0, s1, out,
+  // Tiles of at most three levels (experts with few rows) are bound by their
+  // weight stream; where the load unit copies both operands they keep the weights
+  // of two stages in flight.  (Kernels that take their weights through registers
+  // are bound by their LDS traffic at these heights, not by the stream.)
+  if constexpr (!FP8 && (GATEUP || WF16)) {
+    if (tl.rows <= 128) {
+      gemm_block<GATEUP, FP8, 2, WF16, 3, 3>(ring, smax, srow, stab, tl, nblk, act, sorted_slots, w0v, w1v, s0, s1,
+                                             out, hscale, oscale, Kdim, Ndim, topk);
+      return;
+    }
+    if (tl.rows <= 192) {
+      gemm_block<GATEUP, FP8, 3, WF16, 2, 3>(ring, smax, srow, stab, tl, nblk, act, sorted_slots, w0v, w1v, s0, s1,
+                                             out, hscale, oscale, Kdim, Ndim, topk);
+      return;
+    }
+  }
+  gemm_block<GATEUP, FP8, kBM / 64, WF16>(ring, smax, srow, stab, tl, nblk, act, sorted_slots, w0v, w1v, s0, s1, out,
                                           hscale, oscale, Kdim, Ndim, topk);
 }
 
