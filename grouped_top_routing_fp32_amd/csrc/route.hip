@@ -82,19 +82,29 @@ __global__ __launch_bounds__(4 * MR) void router_logits_kernel(const uint16_t* _
     acc_lo[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // operands of step k are loaded during step k - 32 (one step in flight)
-  u32x4 xv = ldg16(xsrc + kbeg);
-  f32x4 wv[kWC];
+  // Operands of step k are loaded during step k - 64 (two steps in flight): a
+  // split has few steps at small T, each bound by the latency of its loads.  The
+  // two register sets take turns (the loop runs two steps per turn so that each
+  // is named at compile time: a register copy would wait for its loads).  Every
+  // step issues its loads, from the split's last step where it runs past it, so
+  // that the compiler's waits count a fixed number of loads in flight.
+  u32x4 xv[2];
+  f32x4 wv[2][kWC];
+  const int klast = kend - kRtK;
+  auto load = [&](u32x4& xr, f32x4(&wr4)[kWC], int k) {
+    k = min(k, klast);
+    xr = ldg16(xsrc + k);
 #pragma unroll
-  for (int i = 0; i < kWC; ++i) wv[i] = *reinterpret_cast<const f32x4*>(wsrc[i] + kbeg);
-  for (int k = kbeg; k < kend; k += kRtK) {
+    for (int i = 0; i < kWC; ++i) wr4[i] = *reinterpret_cast<const f32x4*>(wsrc[i] + k);
+  };
+  auto step = [&](int k, u32x4& xr, f32x4(&wr4)[kWC]) {
     __syncthreads();  // previous step's fragment reads are done
-    *reinterpret_cast<u32x4*>(&sA[xa_row * kRtLd + xa_kc * 8]) = xv;
+    *reinterpret_cast<u32x4*>(&sA[xa_row * kRtLd + xa_kc * 8]) = xr;
 #pragma unroll
     for (int i = 0; i < kWC; ++i) {
       uint16_t hi[4], mid[4], lo[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) split3(wv[i][q], hi[q], mid[q], lo[q]);
+      for (int q = 0; q < 4; ++q) split3(wr4[i][q], hi[q], mid[q], lo[q]);
       const int off = wb_row[i] * kRtLd + wb_kc[i] * 4;
       uint2 ph, pm, pl;
       ph.x = hi[0] | (uint32_t(hi[1]) << 16);
@@ -108,11 +118,7 @@ __global__ __launch_bounds__(4 * MR) void router_logits_kernel(const uint16_t* _
       *reinterpret_cast<uint2*>(&sB[2][off]) = pl;
     }
     __syncthreads();
-    if (k + kRtK < kend) {
-      xv = ldg16(xsrc + k + kRtK);
-#pragma unroll
-      for (int i = 0; i < kWC; ++i) wv[i] = *reinterpret_cast<const f32x4*>(wsrc[i] + k + kRtK);
-    }
+    load(xr, wr4, k + 2 * kRtK);
     const int arow = wave * 16 + (lane & 15);
     const int kk = (lane >> 4) * 8;
     u32x4 a = *reinterpret_cast<const u32x4*>(&sA[arow * kRtLd + kk]);
@@ -126,7 +132,17 @@ __global__ __launch_bounds__(4 * MR) void router_logits_kernel(const uint16_t* _
       acc_lo[j] = mfma16x16x32(a, bl, acc_lo[j]);
       acc_lo[j] = mfma16x16x32(a, bm, acc_lo[j]);
     }
+  };
+  // kend - kbeg is a positive multiple of kRtK (H % 256 == 0, k_per_split % 32 == 0)
+  const int nsteps = (kend - kbeg) / kRtK;
+  load(xv[0], wv[0], kbeg);
+  load(xv[1], wv[1], kbeg + kRtK);
+  int k = kbeg;
+  for (int p = 0; p < nsteps / 2; ++p, k += 2 * kRtK) {
+    step(k, xv[0], wv[0]);
+    step(k + kRtK, xv[1], wv[1]);
   }
+  if (nsteps & 1) step(k, xv[0], wv[0]);
 
   float* dst = part + (size_t)blockIdx.z * T * E;
 #pragma unroll
