@@ -763,7 +763,27 @@ static hipError_t allow_full_lds(const void* fn, std::atomic<uint64_t>& done) {
   return e;
 }
 
-// Ring depth per tile height: three slots while they fit, else two.
+// Workgroups of 256 threads of `fn` that the device holds at once with `lds` bytes
+// of dynamic LDS each (0 if the runtime cannot tell); computed once per kernel (the
+// kernel's dynamic-LDS limit is raised first, as for its launches).
+static int resident_blocks(const void* fn, size_t lds, std::atomic<int>& cached) {
+  int n = cached.load(std::memory_order_acquire);
+  if (n >= 0) return n;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess)
+    return 0;
+  n = cus * per_cu;
+  cached.store(n, std::memory_order_release);
+  return n;
+}
+
+// Ring depth per tile height: three slots while they fit, else two.  A grid that
+// the device cannot hold at once with three slots but can with two (a batch of a
+// token or two: a few experts' column blocks) takes two, so that no workgroup waits
+// for a second round on a quarter of the CUs.
 constexpr int gateup_slots(int R) { return (128 + R) * 256 * 3 <= 144 * 1024 ? 3 : 2; }
 // The down kernels' shape per tile height, chosen by measurement (T = 256 .. 1024 at
 // Beam dims, identical output in every variant): a ring that fits half the LDS lets
@@ -809,16 +829,47 @@ bool stream_fp8_fits(int H, int I, int R) {
          gateup_stream_fp8_lds_bytes(R) <= kStreamLdsMax && down_stream_fp8_lds_bytes(R, I) <= kStreamLdsMax;
 }
 
+template <int S, int R>
+static hipError_t gateup_fp8_s(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                               int max_tiles, const uint8_t* wg, const uint8_t* wu, const float* sg, const float* su,
+                               uint16_t* h, uint8_t* hscale, int H, int I, int K, hipStream_t st) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<S, R>), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gateup_stream_fp8_kernel<S, R>), dim3(max_tiles * (I / 64)), dim3(256),
+                     (size_t)S * (128 * kF8WRow + R * kF8ARow), st, x, slots, tiles, ntiles, wg, wu, sg, su, h, hscale,
+                     H, I, K);
+  return hipGetLastError();
+}
+
 template <int R>
 static hipError_t gateup_fp8_r(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
                                int max_tiles, const uint8_t* wg, const uint8_t* wu, const float* sg, const float* su,
                                uint16_t* h, uint8_t* hscale, int H, int I, int K, hipStream_t st) {
   constexpr int S = gateup_f8_slots(R);
+  if constexpr (S == 3) {
+    static std::atomic<int> fit3{-1}, fit2{-1};
+    const int grid = max_tiles * (I / 64);
+    if (grid > resident_blocks(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<3, R>),
+                               gateup_stream_fp8_lds_bytes(R), fit3) &&
+        grid <= resident_blocks(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<2, R>),
+                                2 * (128 * kF8WRow + R * kF8ARow), fit2))
+      return gateup_fp8_s<2, R>(x, slots, tiles, ntiles, max_tiles, wg, wu, sg, su, h, hscale, H, I, K, st);
+  }
+  return gateup_fp8_s<S, R>(x, slots, tiles, ntiles, max_tiles, wg, wu, sg, su, h, hscale, H, I, K, st);
+}
+
+template <int S, int R>
+static hipError_t down_fp8_s(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                             const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd, uint16_t* y16,
+                             uint8_t* yscale, int H, int I, hipStream_t st) {
+  constexpr int NB = down_f8_nb(R);
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_fp8_kernel<S, R>), lds_set);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_fp8_kernel<S, R, NB>), lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gateup_stream_fp8_kernel<S, R>), dim3(max_tiles * (I / 64)), dim3(256),
-                     gateup_stream_fp8_lds_bytes(R), st, x, slots, tiles, ntiles, wg, wu, sg, su, h, hscale, H, I, K);
+  hipLaunchKernelGGL((down_stream_fp8_kernel<S, R, NB>), dim3(max_tiles * (H / (64 * NB))), dim3(256),
+                     (size_t)S * (64 * NB * kF8WRow + R * kF8ARow) + I / kScaleCols, st, h, hscale, slots, tiles,
+                     ntiles, wd, sd, y16, yscale, H, I);
   return hipGetLastError();
 }
 
@@ -827,11 +878,28 @@ static hipError_t down_fp8_r(const uint16_t* h, const uint8_t* hscale, const int
                              const int32_t* ntiles, int max_tiles, const uint8_t* wd, const float* sd, uint16_t* y16,
                              uint8_t* yscale, int H, int I, hipStream_t st) {
   constexpr int S = down_f8_slots(R), NB = down_f8_nb(R);
+  if constexpr (S == 3) {
+    static std::atomic<int> fit3{-1}, fit2{-1};
+    const int grid = max_tiles * (H / (64 * NB));
+    if (grid > resident_blocks(reinterpret_cast<const void*>(&down_stream_fp8_kernel<3, R, NB>),
+                               down_stream_fp8_lds_bytes(R, I), fit3) &&
+        grid <= resident_blocks(reinterpret_cast<const void*>(&down_stream_fp8_kernel<2, R, NB>),
+                                2 * (64 * NB * kF8WRow + R * kF8ARow) + I / kScaleCols, fit2))
+      return down_fp8_s<2, R>(h, hscale, slots, tiles, ntiles, max_tiles, wd, sd, y16, yscale, H, I, st);
+  }
+  return down_fp8_s<S, R>(h, hscale, slots, tiles, ntiles, max_tiles, wd, sd, y16, yscale, H, I, st);
+}
+
+template <int S, int R>
+static hipError_t gateup_s(const uint16_t* x, const int32_t* slots, const Tile* tiles, const int32_t* ntiles,
+                           int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale, int H,
+                           int I, int K, hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&down_stream_fp8_kernel<S, R, NB>), lds_set);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<S, kSk, R>), lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_stream_fp8_kernel<S, R, NB>), dim3(max_tiles * (H / (64 * NB))), dim3(256),
-                     down_stream_fp8_lds_bytes(R, I), st, h, hscale, slots, tiles, ntiles, wd, sd, y16, yscale, H, I);
+  hipLaunchKernelGGL((gateup_stream_lds_kernel<S, kSk, R>), dim3(max_tiles * (I / 64)), dim3(256),
+                     (size_t)S * (128 + R) * StageGeom<kSk>::kRowBytes, st, x, slots, tiles, ntiles, wg, wu, h, hscale,
+                     H, I, K);
   return hipGetLastError();
 }
 
@@ -840,11 +908,30 @@ static hipError_t gateup_r(const uint16_t* x, const int32_t* slots, const Tile* 
                            int max_tiles, const uint16_t* wg, const uint16_t* wu, uint16_t* h, uint8_t* hscale, int H,
                            int I, int K, hipStream_t st) {
   constexpr int S = gateup_slots(R);
+  if constexpr (S == 3) {
+    static std::atomic<int> fit3{-1}, fit2{-1};
+    const int grid = max_tiles * (I / 64);
+    if (grid > resident_blocks(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<3, kSk, R>),
+                               gateup_stream_lds_bytes(R), fit3) &&
+        grid <= resident_blocks(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<2, kSk, R>),
+                                2 * (128 + R) * StageGeom<kSk>::kRowBytes, fit2))
+      return gateup_s<2, R>(x, slots, tiles, ntiles, max_tiles, wg, wu, h, hscale, H, I, K, st);
+  }
+  return gateup_s<S, R>(x, slots, tiles, ntiles, max_tiles, wg, wu, h, hscale, H, I, K, st);
+}
+
+template <int S, int R, bool WF16>
+static hipError_t down_s(const uint16_t* h, const uint8_t* hscale, const int32_t* slots, const Tile* tiles,
+                         const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16, uint8_t* yscale,
+                         int H, int I, hipStream_t st) {
+  constexpr int NB = down_nb(R);
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&gateup_stream_lds_kernel<S, kSk, R>), lds_set);
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(&down_stream_lds_kernel<S, kSk, R, NB, WF16>), lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gateup_stream_lds_kernel<S, kSk, R>), dim3(max_tiles * (I / 64)), dim3(256),
-                     gateup_stream_lds_bytes(R), st, x, slots, tiles, ntiles, wg, wu, h, hscale, H, I, K);
+  hipLaunchKernelGGL((down_stream_lds_kernel<S, kSk, R, NB, WF16>), dim3(max_tiles * (H / (64 * NB))), dim3(256),
+                     (size_t)S * (64 * NB + R) * StageGeom<kSk>::kRowBytes + I / kScaleCols, st, h, hscale, slots,
+                     tiles, ntiles, wd, y16, yscale, H, I);
   return hipGetLastError();
 }
 
@@ -853,13 +940,16 @@ static hipError_t down_r(const uint16_t* h, const uint8_t* hscale, const int32_t
                          const int32_t* ntiles, int max_tiles, const uint16_t* wd, uint16_t* y16, uint8_t* yscale,
                          int H, int I, hipStream_t st) {
   constexpr int S = down_slots(R), NB = down_nb(R);
-  static std::atomic<uint64_t> lds_set{0};
-  hipError_t e =
-      allow_full_lds(reinterpret_cast<const void*>(&down_stream_lds_kernel<S, kSk, R, NB, WF16>), lds_set);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_stream_lds_kernel<S, kSk, R, NB, WF16>), dim3(max_tiles * (H / (64 * NB))), dim3(256),
-                     down_stream_lds_bytes(R, I), st, h, hscale, slots, tiles, ntiles, wd, y16, yscale, H, I);
-  return hipGetLastError();
+  if constexpr (S == 3) {
+    static std::atomic<int> fit3{-1}, fit2{-1};
+    const int grid = max_tiles * (H / (64 * NB));
+    if (grid > resident_blocks(reinterpret_cast<const void*>(&down_stream_lds_kernel<3, kSk, R, NB, WF16>),
+                               down_stream_lds_bytes(R, I), fit3) &&
+        grid <= resident_blocks(reinterpret_cast<const void*>(&down_stream_lds_kernel<2, kSk, R, NB, WF16>),
+                                2 * (64 * NB + R) * StageGeom<kSk>::kRowBytes + I / kScaleCols, fit2))
+      return down_s<2, R, WF16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
+  }
+  return down_s<S, R, WF16>(h, hscale, slots, tiles, ntiles, max_tiles, wd, y16, yscale, H, I, st);
 }
 
 // Launchers of the stream path (tiles of at most R rows from the dispatch; require
