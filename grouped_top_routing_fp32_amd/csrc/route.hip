@@ -20,6 +20,8 @@
 //       group top-2 sums, the kept groups and K rounds of a wave-wide argmax,
 //       on the scores or, with a selection-only bias, on score + bias (the
 //       weights always from the unbiased scores).
+#include <type_traits>
+
 #include "common.h"
 
 namespace beam {
@@ -247,43 +249,53 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     valid[j] = e < E && ((kept >> (e / gsz)) & 1ull);
   }
 
-  // K rounds of a wave-wide argmax of (c, e); the winner's unbiased score bs
-  // travels with it for the weights
+  // K rounds of a wave-wide argmax of (c, e).  Each candidate is one 64-bit key,
+  // ordered as beats() orders (c, e): the high word maps c to an unsigned integer
+  // of the same order (-0 taken as +0, which beats() ranks equal), the low word is
+  // ~e, so equal values go to the lower index.  A round reduces the lane maxima
+  // inside each row of 16 lanes with DPP moves (quad swaps, then rotations by 4
+  // and 8) and across the four rows with readlanes; the winner's unbiased score
+  // comes from its lane for the weights.
+  uint64_t key[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u = __float_as_uint(c[j] + 0.0f);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    key[j] = ((uint64_t)o << 32) | (uint32_t)~(uint32_t)(lane + 64 * j);
+  }
+  auto kmax = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  auto dpp_max = [&](uint64_t a, auto ctrl) {
+    constexpr int kCtrl = decltype(ctrl)::value;
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)a, kCtrl, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(a >> 32), kCtrl, 0xF, 0xF, false);
+    return kmax(a, ((uint64_t)hi << 32) | lo);
+  };
+  auto read_lane = [](uint64_t a, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)a, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(a >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+  };
   float total = 0.f;
   float my_v = 0.f;
   int my_e = 0;
   for (int k = 0; k < K; ++k) {
-    float bv = 0.f, bs = 0.f;
-    int be = 0x7fffffff;
-    bool bok = false;
+    uint64_t best = 0;  // below every candidate's key
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (valid[j] && (!bok || beats(c[j], e, bv, be))) {
-        bv = c[j];
-        bs = v[j];
-        be = e;
-        bok = true;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const float os = __shfl_xor(bs, off);
-      const int oe = __shfl_xor(be, off);
-      const int ook = __shfl_xor(int(bok), off);
-      if (ook && (!bok || beats(ov, oe, bv, be))) {
-        bv = ov;
-        bs = os;
-        be = oe;
-        bok = true;
-      }
-    }
-    // bv/be are now the same on every lane
-    if ((be & 63) == lane) {
+    for (int j = 0; j < 4; ++j)
+      if (valid[j]) best = kmax(best, key[j]);
+    best = dpp_max(best, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    best = dpp_max(best, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    best = dpp_max(best, std::integral_constant<int, 0x124>{});  // row_ror:4
+    best = dpp_max(best, std::integral_constant<int, 0x128>{});  // row_ror:8
+    best = kmax(kmax(read_lane(best, 0), read_lane(best, 16)), kmax(read_lane(best, 32), read_lane(best, 48)));
+    const int be = (int)~(uint32_t)best;  // the winner (uniform)
+    const int wj = be >> 6, wl = be & 63;
+    const float mine = wj == 0 ? v[0] : wj == 1 ? v[1] : wj == 2 ? v[2] : v[3];
+    const float bs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mine), wl));
+    if (wl == lane) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (be == lane + 64 * j) valid[j] = false;
+        if (j == wj) valid[j] = false;
     }
     total = total + bs;
     if (lane == k) {
