@@ -763,7 +763,9 @@ def test_forward_packed_matches_bf16_bits(name):
     assert torch.equal(wdp.float()[normal], w32[normal])
 
 
-@pytest.mark.parametrize("T", [64, 16384])
+# 4096: every grouped tile has two or three levels, so packed down runs the three-stage ring
+# (three activation stages at two levels, two at three) against bf16 down's two stages
+@pytest.mark.parametrize("T", [64, 4096, 16384])
 def test_forward_packed_beam(beam_experts, T):
     _announce(f"forward packed Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
