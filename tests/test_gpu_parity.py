@@ -366,6 +366,15 @@ EDGE = {
     # both projections; large weights, so h and y carry non-zero power-of-two scales
     "dense_merged_big": synth.Workload("dense_merged_big", 560, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06,
                                        expert_sigma=10.0),
+    # merged fifth levels: a tail of one 16-row fragment (5 rows), of two (17 rows: the second
+    # holds one row), and a full one (64 rows: 320 rows, the kernel's no-level-test loop), with
+    # non-zero scales
+    "dense_tail1": synth.Workload("dense_tail1", 261, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06,
+                                  expert_sigma=10.0),
+    "dense_tail2": synth.Workload("dense_tail2", 273, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06,
+                                  expert_sigma=10.0),
+    "dense_tail_full": synth.Workload("dense_tail_full", 320, synth.Dims(256, 128, 1, 1, 1, 1), router_sigma=0.06,
+                                      expert_sigma=10.0),
     # about 300 rows per expert: some experts' tails are merged (<= 64 rows), others are not
     "merged_tails_big": synth.Workload("merged_tails_big", 1200, synth.Dims(512, 256, 8, 2, 1, 2), router_sigma=0.06,
                                        expert_sigma=10.0),
@@ -595,6 +604,11 @@ FP8 = {
                                           router_sigma=0.06, expert_sigma=10.0),
     "f8_merged_tails_big": synth.Workload("f8_merged_tails_big", 1200, synth.Dims(512, 256, 8, 2, 1, 2),
                                           router_sigma=0.06, expert_sigma=10.0),
+    # merged fifth levels of one fragment and of four (full), on the register-path kernels
+    "f8_dense_tail1": synth.Workload("f8_dense_tail1", 261, synth.Dims(256, 256, 1, 1, 1, 1), router_sigma=0.06,
+                                     expert_sigma=10.0),
+    "f8_dense_tail_full": synth.Workload("f8_dense_tail_full", 320, synth.Dims(256, 256, 1, 1, 1, 1),
+                                         router_sigma=0.06, expert_sigma=10.0),
 }
 
 
@@ -602,7 +616,8 @@ FP8 = {
 FP8_PATH = {"f8_small": 8, "f8_stream": 8, "f8_skew": 8, "f8_big": 8, "f8_huge": 8, "f8_grouped": 0,
             "f8_grouped_e256": 0, "f8_grouped_skew": 0, "f8_grouped_big": 0, "f8_grouped_huge": 0,
             "f8_stream_r16": 16, "f8_stream_r32": 32, "f8_stream_r32_skew": 32, "f8_stream_r64": 64,
-            "f8_stream_r64_skew": 64, "f8_stream_r64_huge": 64, "f8_dense_merged_big": 0, "f8_merged_tails_big": 0}
+            "f8_stream_r64_skew": 64, "f8_stream_r64_huge": 64, "f8_dense_merged_big": 0, "f8_merged_tails_big": 0,
+            "f8_dense_tail1": 0, "f8_dense_tail_full": 0}
 
 
 @pytest.mark.parametrize("name", list(FP8))
@@ -739,6 +754,7 @@ PACKED = {
     "mid_tiled": MID["mid_tiled"][0],             # grouped GEMMs, full and ragged tiles
     "mid_tiled_huge": MID["mid_tiled_huge"][0],   # accumulator rescaling between activation blocks
     "dense_merged_big": EDGE["dense_merged_big"],  # a merged five-level tile with non-zero scales
+    "dense_tail1": EDGE["dense_tail1"],            # a fifth level of one fragment
 }
 
 
