@@ -172,8 +172,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
                                                      int K, float scale, int32_t* __restrict__ ids,
                                                      float* __restrict__ wout) {
 #pragma clang fp contract(off)
-  __shared__ float s_sc[4][256];
-  __shared__ float s_gs[4][64];
+  __shared__ __attribute__((aligned(16))) float s_sc[4][256];
+  __shared__ __attribute__((aligned(16))) float s_gs[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -216,17 +216,27 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
   }
   __syncthreads();
 
-  // group score: sum of the two largest selection values of the group (one lane per group)
+  // group score: sum of the two largest selection values of the group (one lane per group),
+  // the values taken in index order; read four at a time where the groups allow it
   if (active && lane < G) {
     float m1 = -INFINITY, m2 = -INFINITY;
     const float* g = &s_sc[wave][lane * gsz];
-    for (int i = 0; i < gsz; ++i) {
-      const float s = g[i];
-      if (s > m1) {
-        m2 = m1;
-        m1 = s;
-      } else if (s > m2) {
-        m2 = s;
+    if (gsz % 4 == 0) {
+#pragma unroll 4
+      for (int i = 0; i < gsz; i += 4) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(g + i);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float v = q[u];
+          m2 = v > m1 ? m1 : (v > m2 ? v : m2);
+          m1 = v > m1 ? v : m1;
+        }
+      }
+    } else {
+      for (int i = 0; i < gsz; ++i) {
+        const float v = g[i];
+        m2 = v > m1 ? m1 : (v > m2 ? v : m2);
+        m1 = v > m1 ? v : m1;
       }
     }
     s_gs[wave][lane] = (gsz >= 2) ? (m1 + m2) : m1;
@@ -237,7 +247,15 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
   if (active && lane < G) {
     const float mine = s_gs[wave][lane];
     int rank = 0;
-    for (int g = 0; g < G; ++g) rank += beats(s_gs[wave][g], g, mine, lane) ? 1 : 0;
+    if (G % 4 == 0) {
+      for (int g = 0; g < G; g += 4) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(&s_gs[wave][g]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rank += beats(q[u], g + u, mine, lane) ? 1 : 0;
+      }
+    } else {
+      for (int g = 0; g < G; ++g) rank += beats(s_gs[wave][g], g, mine, lane) ? 1 : 0;
+    }
     keep = rank < TG;
   }
   const unsigned long long kept = __ballot(keep);
