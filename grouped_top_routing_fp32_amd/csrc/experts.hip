@@ -764,8 +764,10 @@ static hipError_t allow_full_lds(const void* fn, std::atomic<uint64_t>& done) {
 }
 
 // Workgroups of 256 threads of `fn` that the device holds at once with `lds` bytes
-// of dynamic LDS each (0 if the runtime cannot tell); computed once per kernel (the
-// kernel's dynamic-LDS limit is raised first, as for its launches).
+// of dynamic LDS each (0 if the runtime cannot tell); computed once per kernel, on
+// the first device that asks, and used for all (the kernels are built for one GPU
+// model; the figure only picks a ring depth, never correctness).  The kernel's
+// dynamic-LDS limit is raised first, as for its launches.
 static int resident_blocks(const void* fn, size_t lds, std::atomic<int>& cached) {
   int n = cached.load(std::memory_order_acquire);
   if (n >= 0) return n;
