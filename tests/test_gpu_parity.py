@@ -335,11 +335,14 @@ def test_forward_skewed(beam_experts):
     assert counts.max() >= 20 * counts.mean()
 
 
-# Beam dims across the batch sizes where the expert path changes form: T <= 128
-# stream kernels (T = 128: several experts with more than one 8-row pass); from
-# T = 160 the grouped GEMMs, first with nearly empty tiles, then partial ones;
+# Beam dims across the batch sizes where the expert path changes form: T <= 1024
+# stream kernels (T = 1: two-slot rings, every workgroup resident at once; T = 128:
+# experts with more than one 8-row tile; 256 .. 1024: 16-, 32- and 64-row tiles); from
+# T = 2048 the grouped GEMMs: tiles of at most two levels (three activation and three
+# weight stages), of three (T = 4096, 6144: two and three), four-level tiles with small
+# merged fifth levels (T = 8192), full tiles followed by short ones (T = 12288), and
 # T = 32768, twice the prefill batch: about 1024 rows, four tiles, per expert.
-@pytest.mark.parametrize("T", [1, 8, 128, 160, 256, 512, 1024, 2048, 4096, 32768])
+@pytest.mark.parametrize("T", [1, 8, 128, 160, 256, 512, 1024, 2048, 4096, 6144, 8192, 12288, 32768])
 def test_forward_beam_sizes(beam_experts, T):
     _announce(f"forward Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
@@ -659,7 +662,7 @@ def test_forward_fp8_rejects_unsupported_intermediate():
     assert ei.value.status == binding.BEAM_MOE_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("T", [1, 64, 256, 512, 1024, 2048, 16384])
+@pytest.mark.parametrize("T", [1, 64, 256, 512, 1024, 2048, 4096, 8192, 16384])
 def test_forward_fp8_beam(beam_experts_fp8, T):
     _announce(f"forward fp8 Beam T={T}")
     wl = synth.with_tokens(synth.WORKLOADS["decode"], T)
