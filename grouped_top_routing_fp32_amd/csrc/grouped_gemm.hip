@@ -36,7 +36,8 @@
 // copies adds a full drain at each loop head.
 // Down: the weight stage is loaded into registers, converted to fp16 and
 // written to LDS by the threads themselves, in the same layout the copies
-// produce; the accumulators are kept in units of 2^s of the stage's 64-column
+// produce (on short tiles the copies bring the bf16 weights and each wave
+// converts its own rows in place); the accumulators are kept in units of 2^s of the stage's 64-column
 // activation block and rescaled (exactly) when s changes from one stage to the
 // next, so the weights are never scaled.
 // FP8 weights (E4M3 codes with one fp32 scale per output row; 「Reflection 放出
@@ -104,10 +105,15 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
   const WT* w1 = static_cast<const WT*>(w1v);
   // weights through registers (FP8 codes, bf16 down weights to convert), or copied by the
   // load unit (bf16 gate/up weights, and down weights already in fp16: WF16)
-  constexpr bool kRegB = FP8 || (!GATEUP && !WF16);
+  // bf16 down on the three-stage path: its weights are copied by the load unit as
+  // bf16 and converted to fp16 in place in LDS, each wave its own 32 rows once they
+  // have landed (the same conversion the register path applies)
+  constexpr bool kCvtB = !GATEUP && !FP8 && !WF16 && NB == 3;
+  constexpr bool kRegB = (FP8 || (!GATEUP && !WF16)) && !kCvtB;
   constexpr int BM = 64 * kLev;           // rows per A stage
   constexpr int kAPer = BM / 8;           // A rows copied per wave
   static_assert((NA == 2 && NB == 2) || (NB == 3 && NA >= 2 && NA <= 3 && !kRegB), "ring shapes");
+  static_assert(!kCvtB || kBK * 2 * 32 == 4 * 64 * 16, "a wave's 32 weight rows are 4 KB: 4 chunks per lane");
   static_assert((NA * BM + NB * kBN) * kBK <= kRingHalfs, "ring");
   uint16_t(*sA)[BM * kBK] = reinterpret_cast<uint16_t(*)[BM * kBK]>(ring);
   uint16_t(*sB)[kSlotHalfs] = reinterpret_cast<uint16_t(*)[kSlotHalfs]>(ring + NA * BM * kBK);
@@ -176,6 +182,14 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
     for (int q = 0; q < 4; ++q) breg[q] = *reinterpret_cast<const BReg*>(bsrc[q] + k);
   };
   // the weights are converted unscaled: down's accumulators carry the activations' 2^s
+  auto convert_b = [&](int slot) {  // this wave's 32 rows of the slot, bf16 -> fp16 in place
+    uint16_t* rows = &sB[slot][(32 * wave) * kBK];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4* c = reinterpret_cast<u32x4*>(rows + (lane + 64 * i) * 8);
+      *c = bf16x8_to_f16x8(*c);
+    }
+  };
   auto store_b = [&](int slot) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -354,6 +368,15 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
     issue_b(0, 0);
     if constexpr (NA == 3) issue_a(1, 1);
     issue_b(1, 1);
+    if constexpr (kCvtB) {
+      // stage 0's weights: issued before stage 1's copies (and, NA = 3, stage 1's activations)
+      if (NA == 3 && copy_a)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLev + 4));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+      asm volatile("" ::: "memory");
+      convert_b(0);
+    }
     auto main_loop3 = [&](auto full) {
       for (int st = 0; st < nk; ++st) {
         const int slot = st % 3;
@@ -379,6 +402,23 @@ __device__ __forceinline__ void gemm_block(uint16_t* ring, float* smax, int32_t*
         }
         math(st % NA, slot, 0, full);
         math(st % NA, slot, 1, full);
+        if constexpr (kCvtB) {
+          // stage st + 1's weights (requested a step earlier) into fp16 for the next step;
+          // requested after them: this step's activation and weight copies
+          if (st + 1 < nk) {
+            const bool a_later = st + NA - 1 < nk && copy_a, b_later = st + 2 < nk;
+            if (a_later && b_later)
+              __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLev + 4));
+            else if (b_later)
+              __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+            else if (a_later)
+              __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLev));
+            else
+              __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            asm volatile("" ::: "memory");
+            convert_b((st + 1) % 3);
+          }
+        }
       }
     };
     if (tl.rows >= BM)
@@ -551,10 +591,11 @@ __global__ __launch_bounds__(gg::kThreads, 1) void grouped_gemm_kernel(
     }
   }
   // Tiles of at most three levels (experts with few rows) are bound by their
-  // weight stream; where the load unit copies both operands they keep the weights
-  // of two stages in flight.  (Kernels that take their weights through registers
-  // are bound by their LDS traffic at these heights, not by the stream.)
-  if constexpr (!FP8 && (GATEUP || WF16)) {
+  // weight stream: where the load unit copies the weights (bf16 gate/up, fp16 down,
+  // and bf16 down, converted in LDS) they keep two stages of them in flight.  (The
+  // FP8 kernels, which decode their weights through registers, are bound by their
+  // LDS traffic at these heights, not by the stream.)
+  if constexpr (!FP8) {
     if (tl.rows <= 128) {
       gemm_block<GATEUP, FP8, 2, WF16, 3, 3>(ring, smax, srow, stab, tl, nblk, act, sorted_slots, w0v, w1v, s0, s1,
                                              out, hscale, oscale, Kdim, Ndim, topk);
