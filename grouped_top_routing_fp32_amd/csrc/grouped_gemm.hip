@@ -37,9 +37,9 @@
 // Down: the weight stage is loaded into registers, converted to fp16 and
 // written to LDS by the threads themselves, in the same layout the copies
 // produce (on short tiles the copies bring the bf16 weights and each wave
-// converts its own rows in place); the accumulators are kept in units of 2^s of the stage's 64-column
-// activation block and rescaled (exactly) when s changes from one stage to the
-// next, so the weights are never scaled.
+// converts its own rows in place); the accumulators are kept in units of 2^s
+// of the stage's 64-column activation block and rescaled (exactly) when s
+// changes from one stage to the next, so the weights are never scaled.
 // FP8 weights (E4M3 codes with one fp32 scale per output row; 「Reflection 放出
 // 501B 的 Beam 权重：四套精度、滑动窗口和一场榜单落差」, the FP8 repository's
 // precision listing): both projections take their weights through registers
